@@ -1,0 +1,303 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle of the routed mixture-of-experts
+ * FFN layer.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
+ * benchmark's CPU-baseline leg use it; the library never does.  It shares no
+ * code, header, table or helper with the HIP path.
+ *
+ * What is computed, and where it comes from.  The pages describe the layer
+ * only by name; the arithmetic below is the standard Qwen-family sparse MoE
+ * block, read as plainly as the pages allow:
+ *   - veloGB10 README, "The model": routed experts per layer, a top-k choice
+ *     per token (512 experts, top-10), plus one always-on shared expert.
+ *   - Qwen3.6-35B-A3B for NInfer, "Artifact": routed experts have separate
+ *     gate/up and down projections; the shared expert has the same form.
+ *   - Qwen3.8 Flash-Next . GB10 UltraFast, first bullet ("verified-
+ *     deterministic floor"): the token-to-expert alignment (the
+ *     moe_align_block_size step) is made independent of thread arrival order,
+ *     and the weighted combine avoids a float-atomicAdd epilogue.  Read here
+ *     as: alignment lists each expert's slots in ascending slot order, and the
+ *     combine sums a token's k expert outputs in slot order.
+ *   - veloGB10 README, "Kernel work": router fold, grouped expert kernels
+ *     that stream weights without rebuilding them, shared expert overlapped
+ *     with the routed step.
+ *
+ * Readings fixed here (the pages are silent on all of them):
+ *   R-route  logits l[t][e] = sum_h x[t][h] * Wr[e][h] + b[e]; the k largest
+ *            logits are chosen, ties to the lower expert index, -0 == +0, NaN
+ *            below every number; slots j = 0..k-1 in that order; gate weights
+ *            are the softmax over all E logits renormalised over the chosen k,
+ *            which equals exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0).
+ *   R-align  slot i = t*k + j; c_e = #slots routed to e; each expert's
+ *            segment is padded to a multiple of BM (empty experts get none);
+ *            segments are laid out in expert order; inside a segment slot ids
+ *            ascend; padding and the tail up to the capacity hold the
+ *            sentinel T*k; block_expert maps each BM block to its expert, -1
+ *            past the padded total.
+ *   R-ffn    SwiGLU expert: h_r = silu(g_r) * u_r with g = x.Wgu[r], u =
+ *            x.Wgu[I + r] (rows [0, I) gate, [I, 2I) up); y_o = h . Wd[o].
+ *            For fp8 weights, W = code * row_scale and the scale multiplies
+ *            the finished row sum.
+ *   R-shared shared expert with the same form; its output is scaled by
+ *            sigmoid(x . w_sg).
+ *   R-round  the HIP path stores h, each expert's output y and the layer
+ *            output as bf16.  With `rounding` set, the oracle rounds at the
+ *            same three points (fp64 -> bf16, round-to-nearest-even, single
+ *            rounding); everything else stays fp64.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* number formats                                                            */
+
+/* bfloat16 bits -> value: the upper 16 bits of an IEEE-754 binary32. */
+double oracle_bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Nearest bfloat16 (8 significant bits, binary32 exponent range), ties to
+ * even, computed in one rounding from the double.  Returns the bit pattern. */
+uint16_t oracle_bf16_round(double v) {
+  if (isnan(v)) return 0x7FC0;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                      /* a in [2^(e-1), 2^e) */
+  int E = e - 1;                     /* exponent of the leading bit */
+  if (E < -126) E = -126;            /* bf16 subnormals: quantum 2^-133 */
+  double quantum = ldexp(1.0, E - 7);
+  double q = nearbyint(a / quantum); /* ties to even in the default mode */
+  double r = q * quantum;            /* exact: q has at most 9 bits */
+  if (r >= ldexp(1.0, 128)) return sign | 0x7F80; /* overflow to infinity */
+  float f = (float)r;                /* exact: r is representable in binary32 */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+double oracle_bf16_rounded(double v) { return oracle_bf16_value(oracle_bf16_round(v)); }
+
+/* OCP 8-bit E4M3FN code -> value: sign s, exponent field E (bias 7), mantissa
+ * m: E == 0 gives (-1)^s * 2^-6 * m/8, E == 15 with m == 7 is NaN, otherwise
+ * (-1)^s * 2^(E-7) * (1 + m/8).  There are no infinities. */
+double oracle_fp8_value(uint8_t q) {
+  int s = (q >> 7) & 1, E = (q >> 3) & 15, m = q & 7;
+  double mag;
+  if (E == 15 && m == 7) return NAN;
+  if (E == 0) mag = ldexp((double)m / 8.0, -6);
+  else mag = ldexp(1.0 + (double)m / 8.0, E - 7);
+  return s ? -mag : mag;
+}
+
+/* weight element n of a bank stored as bf16 (wtype 0) or fp8 codes (wtype 1) */
+static double weight(const void *w, int wtype, size_t n) {
+  if (wtype == 0) return oracle_bf16_value(((const uint16_t *)w)[n]);
+  return oracle_fp8_value(((const uint8_t *)w)[n]);
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* ------------------------------------------------------------------------ */
+/* routing                                                                   */
+
+/* Router logits in fp64: l[t][e] = sum_h x[t][h] * Wr[e][h] + b[e] (b may be
+ * NULL).  veloGB10 README, "Kernel work" (router fold); R-route above. */
+void oracle_router_logits(int T, int H, int E, const uint16_t *x, const float *w_r, const float *b_r,
+                          double *logits) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h) acc += oracle_bf16_value(x[(size_t)t * H + h]) * (double)w_r[(size_t)e * H + h];
+      if (b_r) acc += (double)b_r[e];
+      logits[(size_t)t * E + e] = acc;
+    }
+}
+
+/* The shared expert's gate logit z[t] = sum_h x[t][h] * w_sg[h], fp64. */
+void oracle_shared_gate_logits(int T, int H, const uint16_t *x, const float *w_sg, double *z) {
+  for (int t = 0; t < T; ++t) {
+    double acc = 0.0;
+    for (int h = 0; h < H; ++h) acc += oracle_bf16_value(x[(size_t)t * H + h]) * (double)w_sg[h];
+    z[t] = acc;
+  }
+}
+
+/* Is (a, ea) ranked before (b, eb)?  Larger logit first; equal logits (IEEE
+ * equality, so -0 == +0) by lower expert index; NaN after every number. */
+static int ranks_before(float a, int ea, float b, int eb) {
+  int na = isnan(a), nb = isnan(b);
+  if (na != nb) return nb;
+  if (!na && a != b) return a > b;
+  return ea < eb;
+}
+
+/* Top-k routing from given fp32 logits [T][E] (R-route): ids [T][k] int32 in
+ * rank order and gate weights [T][k] in fp64.  renormalize != 0: softmax over
+ * all experts renormalised over the chosen k; renormalize == 0: the plain
+ * softmax probability of each chosen expert.  veloGB10 README, "The model"
+ * (top-k per token); Qwen3.8 Flash-Next . GB10 UltraFast, "How it works"
+ * (sort-free verify-path top-k is the selection being mirrored). */
+void oracle_route_topk(int T, int E, int k, int renormalize, const float *logits, int32_t *ids, double *w) {
+  char *taken = (char *)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const float *l = logits + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+      }
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+    }
+    double top = (double)l[ids[(size_t)t * k]];
+    double denom = 0.0;
+    if (renormalize) {
+      for (int j = 0; j < k; ++j) denom += exp((double)l[ids[(size_t)t * k + j]] - top);
+    } else {
+      for (int e = 0; e < E; ++e) denom += exp((double)l[e] - top);
+    }
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = exp((double)l[ids[(size_t)t * k + j]] - top) / denom;
+  }
+  free(taken);
+}
+
+/* ------------------------------------------------------------------------ */
+/* alignment                                                                 */
+
+/* Capacity of the padded slot list: every slot, plus at most BM-1 padding for
+ * each expert that can be touched, rounded up to BM. */
+int64_t oracle_align_capacity(int T, int k, int E, int BM) {
+  int64_t n = (int64_t)T * k;
+  int64_t touched = n < E ? n : E;
+  int64_t c = n + touched * (BM - 1);
+  return (c + BM - 1) / BM * BM;
+}
+
+/* Token-to-expert alignment (R-align): histogram, padded exclusive scan and a
+ * stable scatter of slot ids.  Qwen3.8 Flash-Next . GB10 UltraFast, first
+ * bullet and "Configuration reference" (moe_align_block_size with the
+ * arrival-order shim).  Returns 0, or -1 when cap is too small. */
+int oracle_align(int T, int k, int E, int BM, int64_t cap, const int32_t *ids, int32_t *sorted,
+                 int32_t *block_expert, int32_t *counts, int32_t *offsets, int32_t *num_padded) {
+  int64_t n = (int64_t)T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t i = 0; i < n; ++i) counts[ids[i]] += 1;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    int32_t padded = (counts[e] + BM - 1) / BM * BM;
+    offsets[e + 1] = offsets[e] + padded;
+  }
+  *num_padded = offsets[E];
+  if (offsets[E] > cap) return -1;
+  for (int64_t p = 0; p < cap; ++p) sorted[p] = (int32_t)n;
+  for (int e = 0; e < E; ++e) {
+    int32_t r = 0;
+    for (int64_t i = 0; i < n; ++i)
+      if (ids[i] == e) sorted[offsets[e] + r++] = (int32_t)i;
+  }
+  for (int64_t b = 0; b < cap / BM; ++b) block_expert[b] = -1;
+  for (int e = 0; e < E; ++e)
+    for (int32_t p = offsets[e]; p < offsets[e + 1]; p += BM) block_expert[p / BM] = e;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* experts and the layer                                                     */
+
+/* One token through one SwiGLU expert of a bank (R-ffn, R-round).
+ * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down projections).
+ *   x [H] bf16 bits; w_gu [2I][H], w_d [H][I] (this expert's slices);
+ *   s_gu [2I], s_d [H] row scales for fp8 (ignored for bf16);
+ *   y [H] output in fp64 (bf16-rounded values when rounding != 0). */
+static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w_gu, const void *w_d,
+                       const float *s_gu, const float *s_d, int rounding, double *hbuf, double *y) {
+  for (int r = 0; r < I; ++r) {
+    double g = 0.0, u = 0.0;
+    for (int h = 0; h < H; ++h) {
+      double xv = oracle_bf16_value(x[h]);
+      g += xv * weight(w_gu, wtype, (size_t)r * H + h);
+      u += xv * weight(w_gu, wtype, (size_t)(I + r) * H + h);
+    }
+    if (wtype == 1) {
+      g *= (double)s_gu[r];
+      u *= (double)s_gu[I + r];
+    }
+    double a = silu(g) * u;
+    hbuf[r] = rounding ? oracle_bf16_rounded(a) : a;
+  }
+  for (int o = 0; o < H; ++o) {
+    double acc = 0.0;
+    for (int r = 0; r < I; ++r) acc += hbuf[r] * weight(w_d, wtype, (size_t)o * I + r);
+    if (wtype == 1) acc *= (double)s_d[o];
+    y[o] = rounding ? oracle_bf16_rounded(acc) : acc;
+  }
+}
+
+static size_t elem_bytes(int wtype) { return wtype == 0 ? 2 : 1; }
+
+/* The layer for a list of tokens, routed by the given ids and gate weights:
+ *   out[t] = sum_{j<k} w[t][j] * y_{e(t,j)}(x_t) + sigmoid(x_t . w_sg) * y_shared(x_t)
+ * summed in slot order j = 0..k-1, then the shared term (R-shared), rounded to
+ * bf16 when rounding != 0 (R-round).  The shared expert is absent when I_s == 0.
+ * Qwen3.8 Flash-Next . GB10 UltraFast, first bullet (combine without float
+ * atomics: a fixed order); veloGB10 README, "The model" (shared expert).
+ *   x [T][H] bf16; w_gu [E][2I][H]; w_d [E][H][I]; s_gu [E][2I]; s_d [E][H];
+ *   ids [T][k]; w [T][k] fp64; shared: ws_gu [2I_s][H], ws_d [H][I_s],
+ *   ss_gu [2I_s], ss_d [H], w_sg [H] fp32;
+ *   tokens [n_tok] (token indices to compute); out [n_tok][H] fp64. */
+void oracle_moe_layer(int T, int H, int E, int k, int I, int wtype, const uint16_t *x, const void *w_gu,
+                      const void *w_d, const float *s_gu, const float *s_d, const int32_t *ids, const double *w,
+                      int I_s, const void *ws_gu, const void *ws_d, const float *ss_gu, const float *ss_d,
+                      const float *w_sg, int n_tok, const int32_t *tokens, int rounding, double *out) {
+  (void)T;
+  (void)E;
+  int Imax = I > I_s ? I : I_s;
+  double *hbuf = (double *)malloc(sizeof(double) * (size_t)Imax);
+  double *y = (double *)malloc(sizeof(double) * (size_t)H);
+  double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+  size_t eb = elem_bytes(wtype);
+  for (int q = 0; q < n_tok; ++q) {
+    int t = tokens[q];
+    const uint16_t *xt = x + (size_t)t * H;
+    for (int o = 0; o < H; ++o) acc[o] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      const char *gu = (const char *)w_gu + (size_t)e * 2 * I * H * eb;
+      const char *dn = (const char *)w_d + (size_t)e * H * I * eb;
+      const float *sg = wtype == 1 ? s_gu + (size_t)e * 2 * I : NULL;
+      const float *sd = wtype == 1 ? s_d + (size_t)e * H : NULL;
+      expert_ffn(H, I, wtype, xt, gu, dn, sg, sd, rounding, hbuf, y);
+      double wj = w[(size_t)t * k + j];
+      for (int o = 0; o < H; ++o) acc[o] += wj * y[o];
+    }
+    if (I_s > 0) {
+      double z = 0.0;
+      for (int h = 0; h < H; ++h) z += oracle_bf16_value(xt[h]) * (double)w_sg[h];
+      double gamma = sigmoid(z);
+      expert_ffn(H, I_s, wtype, xt, ws_gu, ws_d, ss_gu, ss_d, rounding, hbuf, y);
+      for (int o = 0; o < H; ++o) acc[o] += gamma * y[o];
+    }
+    for (int o = 0; o < H; ++o) out[(size_t)q * H + o] = rounding ? oracle_bf16_rounded(acc[o]) : acc[o];
+  }
+  free(hbuf);
+  free(y);
+  free(acc);
+}
+
+/* One expert applied to one token, exposed for the pins (y [H] fp64). */
+void oracle_expert(int H, int I, int wtype, const uint16_t *x, const void *w_gu, const void *w_d,
+                   const float *s_gu, const float *s_d, int rounding, double *y) {
+  double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
+  expert_ffn(H, I, wtype, x, w_gu, w_d, s_gu, s_d, rounding, hbuf, y);
+  free(hbuf);
+}
