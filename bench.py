@@ -1,0 +1,273 @@
+"""Benchmark of the routed MoE layer on one MI355X.
+
+A step is one moe_layer_forward call (router, top-k, alignment, routed experts, shared
+expert, combine) over one batch of synthetic tokens, on one of L layer replicas that all
+stay resident in HBM; the replicas are cycled so that each step streams its experts from
+HBM rather than from the 256 MB Infinity Cache.  Prints one JSON line.
+
+Default workload: the Qwen3.6-35B-A3B-like decode/verify layer (hidden 2048, 256 experts,
+top-8, intermediate 512, one shared expert of 512 with a sigmoid gate, bf16 weights) on a
+T=8 verify block (a DFlash block-8 verify pass).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak) at T=8 verify block, bf16"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    # name: (recipe, T, description)
+    "qwen36_T8": ("qwen36_a3b", 8, "Qwen3.6-35B-A3B-like MoE layer, T=8 verify block"),
+    "qwen36_T1": ("qwen36_a3b", 1, "Qwen3.6-35B-A3B-like MoE layer, T=1 decode"),
+    "qwen36_T32": ("qwen36_a3b", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32 (two 16-position blocks)"),
+    "qwen36_zipf_T32": ("qwen36_a3b_zipf", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32, Zipf(1.1) expert load"),
+    "flash_fp8_T1": ("flash_next_fp8", 1, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=1 decode"),
+    "flash_fp8_T6": ("flash_next_fp8", 6, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=6 MTP verify block"),
+    "prefill_T4096": ("prefill", 4096, "Qwen3.6-35B-A3B-like MoE layer, 4096-token prefill chunk"),
+}
+
+DECODE_STAGES = ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"]
+PREFILL_STAGES = ["router_split", "router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
+                  "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen36_T8", choices=sorted(WORKLOADS))
+    p.add_argument("--replicas", type=int, default=0, help="layer replicas in HBM (0: 16 decode, 2 prefill)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it still matches the source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_verify_moe_amd as moe
+    from synth import configs
+
+    recipe, T, desc = WORKLOADS[args.workload]
+    cfg = configs.CONFIGS[recipe]
+    prefill = T > 64
+    L_rep = args.replicas or (2 if prefill else 16)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs: replica 0's expert banks, copied to L distinct HBM buffers; each replica has
+    # its own router, bias and tokens (so each step touches its own set of experts)
+    t0 = time.time()
+    host = configs.make_layer(cfg, seed=0, replica=0)
+    base = moe.Layer.from_host(host, device=dev)
+    layers, xs, outs, wss, host_routers, host_x = [], [], [], [], [], []
+    for r in range(L_rep):
+        hr = configs.make_layer(cfg, seed=0, replica=r, with_experts=False)
+        routed = moe.Bank(base.routed.w_gate_up.clone(), base.routed.w_down.clone(),
+                          None if base.routed.s_gate_up is None else base.routed.s_gate_up.clone(),
+                          None if base.routed.s_down is None else base.routed.s_down.clone())
+        shared = None
+        if base.shared is not None:
+            shared = moe.Bank(base.shared.w_gate_up.clone(), base.shared.w_down.clone(),
+                              None if base.shared.s_gate_up is None else base.shared.s_gate_up.clone(),
+                              None if base.shared.s_down is None else base.shared.s_down.clone())
+        rb = None if hr["router_b"] is None else torch.from_numpy(hr["router_b"]).to(dev)
+        sg = None if cfg.I_s == 0 else torch.from_numpy(hr["shared_gate_w"]).to(dev)
+        lay = moe.Layer(torch.from_numpy(hr["router_w"]).to(dev), rb, routed, cfg.k, shared, sg, cfg.renormalize)
+        xb = configs.make_tokens(cfg, T, seed=0, replica=r)
+        layers.append(lay)
+        xs.append(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev))
+        outs.append(torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev))
+        wss.append(torch.empty((moe.moe_layer_workspace_size(T, lay),), dtype=torch.uint8, device=dev))
+        host_routers.append(hr)
+        host_x.append(xb)
+    del base
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    plan = moe.moe_describe_plan(T, layers[0])
+    stages = PREFILL_STAGES if prefill else DECODE_STAGES
+    nst = len(stages)
+
+    # realised routing per replica (touched experts) for the algorithmic byte counts
+    touched = []
+    for r in range(L_rep):
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ids_out=ids, ws=wss[r])
+        torch.cuda.synchronize()
+        touched.append(len(np.unique(ids.cpu().numpy())))
+
+    bw = 2 if cfg.wtype == "bf16" else 1
+    H, I, I_s, E, k = cfg.H, cfg.I, cfg.I_s, cfg.E, cfg.k
+    srow = 4 if cfg.wtype == "fp8" else 0
+
+    def gate_up_bytes(nt):
+        # weights of every touched expert (+ shared) once, tokens read, h written
+        w = nt * (2 * I * H * bw + 2 * I * srow) + (2 * I_s * H * bw + 2 * I_s * srow if I_s else 0)
+        return w + T * H * 2 + T * k * I * 2 + T * I_s * 2
+
+    def layer_bytes(nt):
+        w = nt * (3 * I * H * bw + (2 * I + H) * srow) + ((3 * I_s * H * bw + (2 * I_s + H) * srow) if I_s else 0)
+        router = E * H * 4 + (E * 4 if host_routers[0]["router_b"] is not None else 0) + (H * 4 if I_s else 0)
+        return w + router + 2 * T * H * 2
+
+    flops_layer = 2 * T * k * 3 * H * I + (2 * T * 3 * H * I_s if I_s else 0)
+
+    # ---- warmup
+    for i in range(args.warmup):
+        r = i % L_rep
+        moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events around every stage on the launch stream
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    for evs in events:
+        for ev in evs:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        r = i % L_rep
+        moe.moe_set_stage_events(events[i])
+        moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
+    moe.moe_set_stage_events(None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    stage_ms = np.zeros((K, nst))
+    for i in range(K):
+        for s in range(nst):
+            stage_ms[i, s] = events[i][s].elapsed_time(events[i][s + 1])
+    gpu_ms = np.array([events[i][0].elapsed_time(events[i][nst]) for i in range(K)])
+    nt_steps = np.array([touched[i % L_rep] for i in range(K)])
+
+    ms_per_step = elapsed * 1e3 / K
+    value = T * K / elapsed
+
+    # dominant kernel: the gate/up expert stream (decode) or the gate/up MFMA GEMM (prefill)
+    dom = 2 if not prefill else 4
+    dom_name = stages[dom]
+    dom_ms = stage_ms[:, dom]
+    src = ["speculative_verify_moe_amd/csrc/gemv.hip" if not prefill else "speculative_verify_moe_amd/csrc/gemm.hip",
+           "speculative_verify_moe_amd/csrc/device.h"]
+    src_hash = source_hash(src)
+    if not prefill:
+        alg_bytes = np.array([gate_up_bytes(n) for n in nt_steps], dtype=np.float64)
+        achieved = alg_bytes.sum() / (dom_ms.sum() * 1e-3) / 1e9
+        traffic = load_traffic(dom_name, args.workload, src_hash)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": dom_name, "avg_us": round(float(dom_ms.mean()) * 1e3, 2),
+                    "alg_bytes_per_launch": int(alg_bytes.mean())}
+    else:
+        # gate/up GEMM flops: every routed slot and every token through the shared expert
+        fl = 2 * T * k * 2 * H * I + 2 * T * 2 * H * I_s
+        achieved = fl / (dom_ms.mean() * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": load_traffic(dom_name, args.workload, src_hash), "kernel": dom_name,
+                    "avg_us": round(float(dom_ms.mean()) * 1e3, 2), "alg_flops_per_launch": int(fl)}
+
+    lb = np.array([layer_bytes(n) for n in nt_steps], dtype=np.float64)
+    layer = {"us_per_layer_wall": round(ms_per_step * 1e3, 2),
+             "us_per_layer_gpu": round(float(gpu_ms.mean()) * 1e3, 2),
+             "alg_bytes_per_layer": int(lb.mean()),
+             "hbm_gbs_gpu": round(lb.sum() / (gpu_ms.sum() * 1e-3) / 1e9, 1),
+             "hbm_frac_gpu": round(lb.sum() / (gpu_ms.sum() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "mfma_frac_gpu": round(flops_layer / (gpu_ms.mean() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+             "touched_experts_mean": round(float(nt_steps.mean()), 2),
+             "stage_us": {s: round(float(stage_ms[:, j].mean()) * 1e3, 2) for j, s in enumerate(stages)}}
+
+    # ---- CPU baseline: the fp64 oracle, as it stands, on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        hl = dict(host)
+        if prefill:
+            sample_T = 16
+        else:
+            sample_T = T
+        n_calls = 0
+        t_c = time.perf_counter()
+        while True:
+            r = n_calls % L_rep
+            hr = host_routers[r]
+            hl["router_w"], hl["router_b"] = hr["router_w"], hr["router_b"]
+            if I_s:
+                hl["shared_gate_w"] = hr["shared_gate_w"]
+            xb = host_x[r][:sample_T]
+            lg = oracle.router_logits(xb, hr["router_w"], hr["router_b"]).astype(np.float32)
+            ids, w = oracle.route_topk(lg, k, cfg.renormalize)
+            oracle.moe_layer(xb, hl, ids, w, rounding=True)
+            n_calls += 1
+            if time.perf_counter() - t_c >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - t_c
+        cpu = {"value": round(n_calls * sample_T / cpu_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_calls} oracle layer calls of {sample_T} tokens each (router, top-k, experts, shared, "
+                         f"combine; fp64) on replicas cycled like the GPU steps, {cpu_s:.1f} s single-threaded",
+               "cpu": _cpu_model()}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.wtype if cfg.wtype == "bf16" else "fp8-e4m3 weights, bf16 activations",
+        "data": "synthetic",
+        "config": {"workload": desc, "T": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
+                   "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep, "path": plan.split()[0]},
+        "roofline": roofline, "layer": layer, "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1), "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

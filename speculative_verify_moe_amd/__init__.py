@@ -1,0 +1,10 @@
+"""MI355X (gfx950) routed mixture-of-experts layer for speculative-decoding verify blocks
+and prefill chunks.  The C ABI is ``include/moe.h``; this package is its Python binding.
+
+Importing it requires the built HIP library (``libmoe_mi355x.so``); there is no CPU path.
+"""
+from ._lib import (  # noqa: F401
+    Bank, Layer, MoeError, moe_align, moe_align_capacity, moe_align_workspace_size, moe_describe_plan,
+    moe_experts_forward, moe_experts_workspace_size, moe_last_error, moe_layer_forward, moe_layer_workspace_size,
+    moe_route_topk, moe_set_stage_events, LIB_PATH, EXPORTS,
+)

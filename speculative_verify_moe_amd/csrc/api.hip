@@ -1,0 +1,520 @@
+// api.hip -- the C ABI of include/moe.h: validation, workspace plan, kernel dispatch.
+//
+// Everything here runs on the host.  Validation comes first and touches no HIP
+// API, so a bad argument is reported without any device work; then the device is
+// checked to be gfx950, the workspace is carved into buffers and the kernels of
+// the chosen path are enqueued on the caller's stream.  Nothing is allocated.
+//
+// Bad configurations are refused before any work with the arithmetic that failed,
+// as the veloGB10 README ("Concurrent requests on the EXL3 path") refuses a model
+// that cannot fit; the library reads no environment variable (same README, "Still
+// in force from v0.7.0": every option is an explicit argument).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512];
+thread_local char g_plan[2048];
+thread_local void *g_events[64];
+thread_local int g_nevents = 0;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t capacity(int64_t T, int64_t k, int64_t E, int64_t BM) {
+  const int64_t n = T * k;
+  const int64_t touched = n < E ? n : E;
+  const int64_t c = n + touched * (BM - 1);
+  return (c + BM - 1) / BM * BM;
+}
+
+bool valid_bm(int BM) { return BM == 16 || BM == 32 || BM == 64 || BM == 128; }
+
+std::atomic<int> g_arch[64];
+
+moe_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  int st = g_arch[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X); this library targets gfx950 only", dev);
+  return MOE_OK;
+}
+
+struct Stager {
+  hipStream_t s;
+  int i = 0;
+  explicit Stager(hipStream_t st) : s(st) {}
+  void mark() {
+    if (i < g_nevents && g_events[i] != nullptr) hipEventRecord((hipEvent_t)g_events[i], s);
+    ++i;
+  }
+};
+
+moe_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- bank validation
+moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, int n_expected) {
+  if (b->wtype != MOE_W_BF16 && b->wtype != MOE_W_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "%s.wtype = %d: must be MOE_W_BF16 (0) or MOE_W_FP8_E4M3 (1)", name, b->wtype);
+  if (need_n && b->num_experts != n_expected)
+    return fail(MOE_ERR_INVALID_ARG, "%s.num_experts = %d: expected %d", name, b->num_experts, n_expected);
+  if (b->hidden != H) return fail(MOE_ERR_INVALID_ARG, "%s.hidden = %d: expected H = %d", name, b->hidden, H);
+  if (b->inter < 64 || b->inter % 64 != 0 || b->inter > 8192)
+    return fail(MOE_ERR_INVALID_ARG, "%s.inter = %d: must be a multiple of 64 in [64, 8192]", name, b->inter);
+  if (b->w_gate_up == nullptr || b->w_down == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "%s: w_gate_up and w_down are required", name);
+  if (!aligned16(b->w_gate_up) || !aligned16(b->w_down))
+    return fail(MOE_ERR_MISALIGNED, "%s: weight pointers must be 16-byte aligned", name);
+  if (b->wtype == MOE_W_FP8_E4M3) {
+    if (b->s_gate_up == nullptr || b->s_down == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "%s: fp8 weights need s_gate_up and s_down row scales", name);
+    if (!aligned4(b->s_gate_up) || !aligned4(b->s_down))
+      return fail(MOE_ERR_MISALIGNED, "%s: scale pointers must be 4-byte aligned", name);
+  }
+  return MOE_OK;
+}
+
+moe_status check_hidden(int H) {
+  if (H < 64 || H % 64 != 0 || H > 16384)
+    return fail(MOE_ERR_INVALID_ARG, "hidden = %d: must be a multiple of 64 in [64, 16384]", H);
+  return MOE_OK;
+}
+
+moe_status check_ek(int E, int k) {
+  if (E < 1 || E > kMaxExperts) return fail(MOE_ERR_INVALID_ARG, "num_experts = %d: must be in [1, %d]", E, kMaxExperts);
+  const int kmax = E < kMaxTopK ? E : kMaxTopK;
+  if (k < 1 || k > kmax) return fail(MOE_ERR_INVALID_ARG, "top_k = %d: must be in [1, min(E, %d)] = [1, %d]", k, kMaxTopK, kmax);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- layer plan
+enum Path { PATH_NONE = 0, PATH_DECODE = 1, PATH_PREFILL = 2 };
+
+struct LayerPlan {
+  Path path = PATH_NONE;
+  int BM = 16;
+  int64_t cap = 0;
+  size_t off_logits, off_gate, off_ids, off_w, off_gamma, off_counts, off_offsets, off_np, off_sorted, off_bexp;
+  size_t off_h, off_hs, off_w3, off_hist, off_y, off_ys;
+  size_t total = 0;
+};
+
+bool is_decode(int T, int k) { return T <= kDecodeMaxT && (int64_t)T * k <= kSmallSlots; }
+
+LayerPlan plan_layer(int T, const moe_layer *L) {
+  LayerPlan p;
+  if (T == 0) return p;
+  const int H = L->hidden, E = L->num_experts, k = L->top_k, I = L->routed.inter;
+  const bool shared = L->shared.num_experts > 0;
+  const int I_s = shared ? L->shared.inter : 0;
+  const int64_t n = (int64_t)T * k;
+  p.path = is_decode(T, k) ? PATH_DECODE : PATH_PREFILL;
+  p.BM = p.path == PATH_DECODE ? 16 : 64;
+  p.cap = capacity(T, k, E, p.BM);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o = align_up(o + bytes, 256);
+    return r;
+  };
+  p.off_logits = take((size_t)T * E * 4);
+  p.off_gate = take((size_t)T * 4);
+  p.off_ids = take((size_t)n * 4);
+  p.off_w = take((size_t)n * 4);
+  p.off_gamma = take((size_t)T * 4);
+  p.off_counts = take((size_t)E * 4);
+  p.off_offsets = take((size_t)(E + 1) * 4);
+  p.off_np = take(4);
+  p.off_sorted = take((size_t)p.cap * 4);
+  p.off_bexp = take((size_t)(p.cap / p.BM) * 4);
+  if (p.path == PATH_DECODE) {
+    p.off_h = take((size_t)n * I * 2);
+    p.off_hs = take((size_t)T * I_s * 2);
+    p.off_w3 = p.off_hist = p.off_y = p.off_ys = 0;
+  } else {
+    p.off_w3 = take((size_t)3 * (E + 1) * H * 2);
+    p.off_hist = take(align_hist_ints(n, E) * 4);
+    p.off_h = take((size_t)p.cap * I * 2);
+    p.off_hs = take((size_t)T * I_s * 2);
+    p.off_y = take((size_t)n * H * 2);
+    p.off_ys = take((size_t)T * H * 2);
+  }
+  p.total = o;
+  return p;
+}
+
+moe_status validate_layer(int T, const moe_layer *L) {
+  if (L == nullptr) return fail(MOE_ERR_INVALID_ARG, "layer descriptor is NULL");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d: must be >= 0", T);
+  moe_status st;
+  if ((st = check_hidden(L->hidden)) != MOE_OK) return st;
+  if ((st = check_ek(L->num_experts, L->top_k)) != MOE_OK) return st;
+  if (L->router_w == nullptr) return fail(MOE_ERR_INVALID_ARG, "router_w is required");
+  if (!aligned16(L->router_w)) return fail(MOE_ERR_MISALIGNED, "router_w must be 16-byte aligned");
+  if (L->router_b != nullptr && !aligned4(L->router_b)) return fail(MOE_ERR_MISALIGNED, "router_b must be 4-byte aligned");
+  if ((st = check_bank(&L->routed, "routed", L->hidden, true, L->num_experts)) != MOE_OK) return st;
+  if (L->shared.num_experts != 0) {
+    if ((st = check_bank(&L->shared, "shared", L->hidden, true, 1)) != MOE_OK) return st;
+    if (L->shared.wtype != L->routed.wtype)
+      return fail(MOE_ERR_UNSUPPORTED, "shared.wtype = %d differs from routed.wtype = %d", L->shared.wtype, L->routed.wtype);
+    if (L->shared_gate_w == nullptr) return fail(MOE_ERR_INVALID_ARG, "shared_gate_w is required with a shared expert");
+    if (!aligned16(L->shared_gate_w)) return fail(MOE_ERR_MISALIGNED, "shared_gate_w must be 16-byte aligned");
+  }
+  if (T > 0 && !is_decode(T, L->top_k)) {
+    if (L->routed.wtype != MOE_W_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "T = %d with top_k = %d takes the prefill (MFMA) path, which needs bf16 weights; "
+                  "fp8 weights run only for T <= %d and T*k <= %d", T, L->top_k, kDecodeMaxT, kSmallSlots);
+    if (L->hidden % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", L->hidden);
+  }
+  return MOE_OK;
+}
+
+void fill_gemv(GemvArgs &g, const uint16_t *x, int T, int H, int k, const moe_bank *routed, int E) {
+  memset(&g, 0, sizeof(g));
+  g.x = x;
+  g.T = T;
+  g.H = H;
+  g.k = k;
+  g.wtype = routed->wtype;
+  g.E = E;
+  g.I = routed->inter;
+  g.w_gu = routed->w_gate_up;
+  g.s_gu = routed->s_gate_up;
+  g.w_d = routed->w_down;
+  g.s_d = routed->s_down;
+}
+
+}  // namespace
+
+// ======================================================================== exported
+extern "C" {
+
+size_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t BM) {
+  if (T < 0 || k < 1 || E < 1 || !valid_bm(BM)) return 0;
+  return (size_t)capacity(T, k, E, BM);
+}
+
+size_t moe_align_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const int64_t n = (int64_t)T * k;
+  if (n <= kSmallSlots) return 0;
+  return align_hist_ints(n, E) * 4;
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+moe_status moe_set_stage_events(void *const *events, int32_t n_events) {
+  if (events == nullptr || n_events <= 0) {
+    g_nevents = 0;
+    return MOE_OK;
+  }
+  if (n_events > 64) return fail(MOE_ERR_INVALID_ARG, "n_events = %d: at most 64", n_events);
+  for (int i = 0; i < n_events; ++i) g_events[i] = events[i];
+  g_nevents = n_events;
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                          int32_t *topk_ids, float *topk_w, void *stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d: must be >= 0", T);
+  moe_status st = check_ek(E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w are required");
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w))
+    return fail(MOE_ERR_MISALIGNED, "logits, topk_ids and topk_w must be 4-byte aligned");
+  if ((st = check_device()) != MOE_OK) return st;
+  return launched(launch_topk(logits, T, E, k, renormalize != 0, topk_ids, topk_w, nullptr, nullptr,
+                              (hipStream_t)stream),
+                  "moe_route_topk");
+}
+
+moe_status moe_align(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t BM, int64_t cap,
+                     int32_t *sorted_ids, int32_t *block_expert, int32_t *expert_counts, int32_t *expert_offsets,
+                     int32_t *num_padded, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d: must be >= 0", T);
+  moe_status st = check_ek(E, k);
+  if (st != MOE_OK) return st;
+  if (!valid_bm(BM)) return fail(MOE_ERR_INVALID_ARG, "BM = %d: must be 16, 32, 64 or 128", BM);
+  const int64_t need = capacity(T, k, E, BM);
+  if (cap < need) return fail(MOE_ERR_WORKSPACE, "cap = %lld < moe_align_capacity(T=%d, k=%d, E=%d, BM=%d) = %lld",
+                              (long long)cap, T, k, E, BM, (long long)need);
+  if (cap % BM != 0) return fail(MOE_ERR_INVALID_ARG, "cap = %lld is not a multiple of BM = %d", (long long)cap, BM);
+  if (cap > (int64_t)1 << 30) return fail(MOE_ERR_INVALID_ARG, "cap = %lld exceeds 2^30", (long long)cap);
+  if (topk_ids == nullptr && T > 0) return fail(MOE_ERR_INVALID_ARG, "topk_ids is required");
+  if (sorted_ids == nullptr || block_expert == nullptr || expert_counts == nullptr || expert_offsets == nullptr ||
+      num_padded == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "sorted_ids, block_expert, expert_counts, expert_offsets and num_padded are required");
+  const int64_t n = (int64_t)T * k;
+  const size_t wsz = moe_align_workspace_size(T, k, E);
+  if (ws_bytes < wsz || (wsz > 0 && ws == nullptr))
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < moe_align_workspace_size = %zu", ws_bytes, wsz);
+  if ((st = check_device()) != MOE_OK) return st;
+  AlignOut al{sorted_ids, block_expert, expert_counts, expert_offsets, num_padded};
+  hipError_t e;
+  if (n <= kSmallSlots) e = launch_align_small(topk_ids, (int)n, E, BM, cap, al, (hipStream_t)stream);
+  else e = launch_align_large(topk_ids, (int)n, E, BM, cap, al, (int32_t *)ws, (hipStream_t)stream);
+  return launched(e, "moe_align");
+}
+
+size_t moe_experts_workspace_size(int32_t T, int32_t k, const moe_bank *routed, int32_t BM) {
+  if (routed == nullptr || T <= 0 || k < 1 || routed->num_experts < 1 || !valid_bm(BM)) return 0;
+  const int64_t n = (int64_t)T * k;
+  const size_t I = (size_t)routed->inter, H = (size_t)routed->hidden;
+  if (is_decode(T, k)) return align_up((size_t)n * I * 2, 256);
+  const int64_t cap = capacity(T, k, routed->num_experts, BM);
+  return align_up((size_t)cap * I * 2, 256) + align_up((size_t)n * H * 2, 256);
+}
+
+moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *routed, int32_t k, const float *topk_w,
+                               const int32_t *sorted_ids, const int32_t *block_expert, const int32_t *expert_counts,
+                               const int32_t *expert_offsets, int32_t BM, int64_t cap, uint16_t *out, void *ws,
+                               size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (routed == nullptr) return fail(MOE_ERR_INVALID_ARG, "routed bank is NULL");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d: must be >= 0", T);
+  moe_status st;
+  if ((st = check_hidden(routed->hidden)) != MOE_OK) return st;
+  const int E = routed->num_experts, H = routed->hidden;
+  if ((st = check_ek(E, k)) != MOE_OK) return st;
+  if ((st = check_bank(routed, "routed", H, false, 0)) != MOE_OK) return st;
+  if (!valid_bm(BM)) return fail(MOE_ERR_INVALID_ARG, "BM = %d: must be 16, 32, 64 or 128", BM);
+  if (T == 0) return MOE_OK;
+  const int64_t need = capacity(T, k, E, BM);
+  if (cap < need || cap % BM != 0)
+    return fail(MOE_ERR_WORKSPACE, "cap = %lld must be a multiple of BM = %d and >= %lld", (long long)cap, BM,
+                (long long)need);
+  if (x == nullptr || out == nullptr || topk_w == nullptr || sorted_ids == nullptr || block_expert == nullptr ||
+      expert_counts == nullptr || expert_offsets == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "x, out, topk_w and the alignment arrays are required");
+  if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_MISALIGNED, "x and out must be 16-byte aligned");
+  const bool decode = is_decode(T, k);
+  if (!decode) {
+    if (routed->wtype != MOE_W_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "T = %d, k = %d takes the prefill (MFMA) path, which needs bf16 weights", T, k);
+    if (BM != 64 && BM != 128) return fail(MOE_ERR_UNSUPPORTED, "the prefill path needs BM = 64 or 128 (got %d)", BM);
+    if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", H);
+  }
+  const size_t wsz = moe_experts_workspace_size(T, k, routed, BM);
+  if (ws == nullptr || ws_bytes < wsz)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < moe_experts_workspace_size = %zu", ws_bytes, wsz);
+  if (!aligned16(ws)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (decode) {
+    GemvArgs g;
+    fill_gemv(g, x, T, H, k, routed, E);
+    g.counts = expert_counts;
+    g.offsets = expert_offsets;
+    g.sorted = sorted_ids;
+    g.topk_w = topk_w;
+    g.h = (uint16_t *)ws;
+    g.out = out;
+    if ((st = launched(launch_gemv_gate_up(g, s, nullptr, 0), "gemv_gate_up")) != MOE_OK) return st;
+    return launched(launch_gemv_down(g, s, nullptr, 0), "gemv_down");
+  }
+  GemmArgs a{};
+  a.x = x;
+  a.T = T;
+  a.H = H;
+  a.k = k;
+  a.E = E;
+  a.I = routed->inter;
+  a.BM = BM;
+  a.cap = cap;
+  a.w_gu = (const uint16_t *)routed->w_gate_up;
+  a.w_d = (const uint16_t *)routed->w_down;
+  a.sorted = sorted_ids;
+  a.block_expert = block_expert;
+  a.h = (uint16_t *)ws;
+  a.y = (uint16_t *)((char *)ws + align_up((size_t)cap * a.I * 2, 256));
+  if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
+  if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
+  return launched(launch_combine(a.y, nullptr, topk_w, nullptr, T, H, k, out, s), "combine");
+}
+
+size_t moe_layer_workspace_size(int32_t T, const moe_layer *L) {
+  if (L == nullptr || T <= 0) return 0;
+  if (L->num_experts < 1 || L->num_experts > kMaxExperts || L->top_k < 1) return 0;
+  return plan_layer(T, L).total;
+}
+
+const char *moe_describe_plan(int32_t T, const moe_layer *L) {
+  g_plan[0] = 0;
+  if (validate_layer(T, L) != MOE_OK) {
+    snprintf(g_plan, sizeof(g_plan), "invalid: %s", g_err);
+    return g_plan;
+  }
+  if (T == 0) {
+    snprintf(g_plan, sizeof(g_plan), "T=0: no kernels");
+    return g_plan;
+  }
+  const LayerPlan p = plan_layer(T, L);
+  const int E = L->num_experts, k = L->top_k;
+  if (p.path == PATH_DECODE) {
+    snprintf(g_plan, sizeof(g_plan),
+             "path=decode T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_rows grid=%d; "
+             "1 topk_align_small grid=1x1024; 2 gemv_gate_up; 3 gemv_down_combine",
+             T, E, k, p.BM, (long long)p.cap, p.total, (E + (L->shared.num_experts > 0 ? 1 : 0) + 3) / 4);
+  } else {
+    snprintf(g_plan, sizeof(g_plan),
+             "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_split; 1 router_gemm_mfma; "
+             "2 topk; 3 align (align_hist, align_colscan, align_offsets, align_scatter); 4 gemm_gate_up_mfma; "
+             "5 gemm_down_mfma; 6 combine",
+             T, E, k, p.BM, (long long)p.cap, p.total);
+  }
+  return g_plan;
+}
+
+moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
+                             int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  moe_status st = validate_layer(T, L);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || out == nullptr) return fail(MOE_ERR_INVALID_ARG, "x and out are required");
+  if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_MISALIGNED, "x and out must be 16-byte aligned");
+  if ((logits_out && !aligned4(logits_out)) || (ids_out && !aligned4(ids_out)) || (w_out && !aligned4(w_out)))
+    return fail(MOE_ERR_MISALIGNED, "logits_out, ids_out and w_out must be 4-byte aligned");
+  const LayerPlan p = plan_layer(T, L);
+  if (ws == nullptr || ws_bytes < p.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < moe_layer_workspace_size(T=%d) = %zu", ws_bytes, T, p.total);
+  if (!aligned16(ws)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != MOE_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)ws;
+  const int H = L->hidden, E = L->num_experts, k = L->top_k;
+  const bool shared = L->shared.num_experts > 0;
+  const int64_t n = (int64_t)T * k;
+  float *logits = logits_out ? logits_out : (float *)(base + p.off_logits);
+  float *gate = (float *)(base + p.off_gate);
+  int32_t *ids = ids_out ? ids_out : (int32_t *)(base + p.off_ids);
+  float *w = w_out ? w_out : (float *)(base + p.off_w);
+  float *gamma = (float *)(base + p.off_gamma);
+  AlignOut al{(int32_t *)(base + p.off_sorted), (int32_t *)(base + p.off_bexp), (int32_t *)(base + p.off_counts),
+              (int32_t *)(base + p.off_offsets), (int32_t *)(base + p.off_np)};
+  Stager sg(s);
+
+  if (p.path == PATH_DECODE) {
+    sg.mark();
+    if ((st = launched(launch_router_rows(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
+                                          logits, gate, s), "router_rows")) != MOE_OK)
+      return st;
+    sg.mark();
+    if ((st = launched(launch_topk_align_small(logits, shared ? gate : nullptr, T, E, k, L->renormalize != 0, p.BM,
+                                               p.cap, ids, w, shared ? gamma : nullptr, al, s),
+                       "topk_align_small")) != MOE_OK)
+      return st;
+    GemvArgs g;
+    fill_gemv(g, x, T, H, k, &L->routed, E);
+    g.counts = al.counts;
+    g.offsets = al.offsets;
+    g.sorted = al.sorted;
+    g.topk_w = w;
+    g.has_shared = shared ? 1 : 0;
+    if (shared) {
+      g.I_s = L->shared.inter;
+      g.ws_gu = L->shared.w_gate_up;
+      g.ss_gu = L->shared.s_gate_up;
+      g.ws_d = L->shared.w_down;
+      g.ss_d = L->shared.s_down;
+      g.gamma = gamma;
+    }
+    g.h = (uint16_t *)(base + p.off_h);
+    g.h_s = (uint16_t *)(base + p.off_hs);
+    g.out = out;
+    sg.mark();
+    if ((st = launched(launch_gemv_gate_up(g, s, nullptr, 0), "gemv_gate_up")) != MOE_OK) return st;
+    sg.mark();
+    if ((st = launched(launch_gemv_down(g, s, nullptr, 0), "gemv_down")) != MOE_OK) return st;
+    sg.mark();
+    return MOE_OK;
+  }
+
+  // prefill chunk
+  uint16_t *w3 = (uint16_t *)(base + p.off_w3);
+  sg.mark();
+  if ((st = launched(launch_router_split(L->router_w, shared ? L->shared_gate_w : nullptr, E, H, w3, s),
+                     "router_split")) != MOE_OK)
+    return st;
+  sg.mark();
+  if ((st = launched(launch_router_gemm(x, T, H, w3, E, shared ? 1 : 0, L->router_b, logits, gate, s),
+                     "router_gemm")) != MOE_OK)
+    return st;
+  sg.mark();
+  if ((st = launched(launch_topk(logits, T, E, k, L->renormalize != 0, ids, w, shared ? gate : nullptr,
+                                 shared ? gamma : nullptr, s), "topk")) != MOE_OK)
+    return st;
+  sg.mark();
+  if ((st = launched(launch_align_large(ids, (int)n, E, p.BM, p.cap, al, (int32_t *)(base + p.off_hist), s),
+                     "align")) != MOE_OK)
+    return st;
+  GemmArgs a{};
+  a.x = x;
+  a.T = T;
+  a.H = H;
+  a.k = k;
+  a.E = E;
+  a.I = L->routed.inter;
+  a.BM = p.BM;
+  a.cap = p.cap;
+  a.w_gu = (const uint16_t *)L->routed.w_gate_up;
+  a.w_d = (const uint16_t *)L->routed.w_down;
+  a.sorted = al.sorted;
+  a.block_expert = al.block_expert;
+  a.has_shared = shared ? 1 : 0;
+  a.I_s = shared ? L->shared.inter : 0;
+  a.ws_gu = shared ? (const uint16_t *)L->shared.w_gate_up : nullptr;
+  a.ws_d = shared ? (const uint16_t *)L->shared.w_down : nullptr;
+  a.h = (uint16_t *)(base + p.off_h);
+  a.h_s = (uint16_t *)(base + p.off_hs);
+  a.y = (uint16_t *)(base + p.off_y);
+  a.y_s = (uint16_t *)(base + p.off_ys);
+  sg.mark();
+  if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
+  sg.mark();
+  if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
+  sg.mark();
+  if ((st = launched(launch_combine(a.y, shared ? a.y_s : nullptr, w, shared ? gamma : nullptr, T, H, k, out, s),
+                     "combine")) != MOE_OK)
+    return st;
+  sg.mark();
+  return MOE_OK;
+}
+
+}  // extern "C"

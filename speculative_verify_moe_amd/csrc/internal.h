@@ -1,0 +1,96 @@
+// internal.h -- host-side launchers shared between the translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Decode/verify blocks run the GEMV path when T <= kDecodeMaxT and T*k <= kSmallSlots.
+constexpr int kDecodeMaxT = 64;
+constexpr int kSmallSlots = 1024;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+// Slots per block of the multi-block alignment.
+constexpr int kAlignChunk = 256;
+
+struct AlignOut {
+  int32_t *sorted;
+  int32_t *block_expert;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *num_padded;
+};
+
+// ---------------------------------------------------------------- route.hip
+hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
+                              const float *w_sg, float *logits, float *gate_logit, hipStream_t s);
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *ids, float *w,
+                       const float *gate_logit, float *gamma, hipStream_t s);
+hipError_t launch_topk_align_small(const float *logits, const float *gate_logit, int T, int E, int k, int renorm,
+                                   int BM, int64_t cap, int32_t *ids, float *w, float *gamma, AlignOut al,
+                                   hipStream_t s);
+hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s);
+// hist: align_hist_ints(n, E) int32 of scratch.
+size_t align_hist_ints(int64_t n, int E);
+hipError_t launch_align_large(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, int32_t *hist,
+                              hipStream_t s);
+int align_large_kernels();
+
+// ---------------------------------------------------------------- gemv.hip
+struct GemvArgs {
+  const uint16_t *x;
+  int T, H, k;
+  int wtype;
+  // routed bank
+  int E, I;
+  const void *w_gu;
+  const float *s_gu;
+  const void *w_d;
+  const float *s_d;
+  const int32_t *counts;
+  const int32_t *offsets;
+  const int32_t *sorted;
+  const float *topk_w;
+  // shared expert (has_shared == 0: absent)
+  int has_shared, I_s;
+  const void *ws_gu;
+  const float *ss_gu;
+  const void *ws_d;
+  const float *ss_d;
+  const float *gamma;
+  // intermediates and output
+  uint16_t *h;    // [T*k][I], row = slot
+  uint16_t *h_s;  // [T][I_s]
+  uint16_t *out;  // [T][H]
+};
+hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
+hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
+
+// ---------------------------------------------------------------- gemm.hip
+struct GemmArgs {
+  const uint16_t *x;
+  int T, H, k, E, I, BM;
+  int64_t cap;
+  const uint16_t *w_gu;
+  const uint16_t *w_d;
+  const int32_t *sorted;
+  const int32_t *block_expert;
+  int has_shared, I_s;
+  const uint16_t *ws_gu;
+  const uint16_t *ws_d;
+  uint16_t *h;    // [cap][I], row = sorted position
+  uint16_t *h_s;  // [T][I_s]
+  uint16_t *y;    // [T*k][H], row = slot
+  uint16_t *y_s;  // [T][H]
+};
+hipError_t launch_router_split(const float *w_r, const float *w_sg, int E, int H, uint16_t *w3, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w3, int E, int has_sg,
+                              const float *b_r, float *logits, float *gate_logit, hipStream_t s);
+hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s);
+hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
+                          int H, int k, uint16_t *out, hipStream_t s);
+
+}  // namespace moe

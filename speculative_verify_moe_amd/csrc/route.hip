@@ -1,0 +1,349 @@
+// route.hip -- router logits, top-k routing and token-to-expert alignment for gfx950.
+//
+// Router: veloGB10 README, "Kernel work" ("router fold spread across more of the
+// GPU"): at decode the router is a 2-4 MiB fp32 read on the serial head of the
+// layer, so every wavefront takes one router row for all tokens and the rows spread
+// over all CUs.
+// Top-k: Qwen3.8 Flash-Next . GB10 UltraFast, "How it works" (a sort-free
+// verify-path top-k): one wavefront per token holds the token's E logits in
+// registers as 64-bit (rank code, ~expert) keys; each of the k rounds is a local
+// max plus a 6-step xor-butterfly max, and the winner's key is cleared.  No sort.
+// Alignment: Qwen3.8 Flash-Next . GB10 UltraFast, first bullet (moe_align_block_size
+// with an arrival-order shim): counts come from integer LDS atomics (their final
+// value does not depend on arrival order) and each slot's place inside its expert's
+// segment is its rank among earlier slots of the same expert, so the output is the
+// stable order by slot index whatever the thread timing.
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+// ============================================================ router (decode)
+// One wavefront per router row n (n < E: expert rows, n == E: the shared gate
+// row), all T tokens, TG tokens per pass.  Lane l owns float4 groups g = l + 64c.
+template <int TG>
+__global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__restrict__ x, int T, int H,
+                                                          const float *__restrict__ w_r,
+                                                          const float *__restrict__ b_r, int E,
+                                                          const float *__restrict__ w_sg,
+                                                          float *__restrict__ logits,
+                                                          float *__restrict__ gate_logit) {
+  const int lane = lane_id();
+  const int n = blockIdx.x * 4 + wave_id();
+  const int NR = E + (w_sg != nullptr ? 1 : 0);
+  if (n >= NR) return;
+  const float *row = n < E ? w_r + (size_t)n * H : w_sg;
+  const float bias = (n < E && b_r != nullptr) ? b_r[n] : 0.0f;
+  const int G4 = H / 4;
+  for (int t0 = 0; t0 < T; t0 += TG) {
+    float acc[TG];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) acc[i] = 0.0f;
+    for (int g = lane; g < G4; g += kWave) {
+      const float4 w = *reinterpret_cast<const float4 *>(row + 4 * g);
+#pragma unroll
+      for (int i = 0; i < TG; ++i) {
+        const int t = t0 + i;
+        if (t < T) {
+          const uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)t * H + 4 * g);
+          acc[i] = fmaf(w.x, bf16_lo(xv.x), acc[i]);
+          acc[i] = fmaf(w.y, bf16_hi(xv.x), acc[i]);
+          acc[i] = fmaf(w.z, bf16_lo(xv.y), acc[i]);
+          acc[i] = fmaf(w.w, bf16_hi(xv.y), acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+      const float v = wave_sum(acc[i]);
+      const int t = t0 + i;
+      if (lane == 0 && t < T) {
+        if (n < E) logits[(size_t)t * E + n] = v + bias;
+        else gate_logit[t] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
+                              const float *w_sg, float *logits, float *gate_logit, hipStream_t s) {
+  const int NR = E + (w_sg != nullptr ? 1 : 0);
+  dim3 grid((NR + 3) / 4), block(256);
+  if (T <= 1) hipLaunchKernelGGL(router_rows_kernel<1>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (T <= 4) hipLaunchKernelGGL(router_rows_kernel<4>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else hipLaunchKernelGGL(router_rows_kernel<8>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  return hipGetLastError();
+}
+
+// ============================================================ top-k (one wavefront per token)
+// Writes ids[0..k), w[0..k) of one token and, when lds_ids is given, the ids into LDS.
+template <int EPL>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, int k, int renorm,
+                                          int32_t *__restrict__ ids_out, float *__restrict__ w_out,
+                                          int32_t *lds_ids) {
+  const int lane = lane_id();
+  uint64_t key[EPL];
+  float val[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      val[i] = l[e];
+      key[i] = rank_key(val[i], e);
+    } else {
+      val[i] = 0.0f;
+      key[i] = 0;
+    }
+  }
+  int my_e = 0;
+  float my_v = 0.0f, top = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) b = key[i] > b ? key[i] : b;
+    b = wave_max_u64(b);
+    const float v = rank_value((uint32_t)(b >> 32));
+    if (j == 0) top = v;
+    if (lane == j) {
+      my_e = (int)(~(uint32_t)b);
+      my_v = v;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] == b) key[i] = 0;
+  }
+  const float ex = lane < k ? expf(my_v - top) : 0.0f;
+  float denom;
+  if (renorm) {
+    denom = wave_sum(ex);
+  } else {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i < E) part += expf(val[i] - top);
+    denom = wave_sum(part);
+  }
+  if (lane < k) {
+    ids_out[lane] = my_e;
+    w_out[lane] = ex / denom;
+    if (lds_ids != nullptr) lds_ids[lane] = my_e;
+  }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                   int renorm, int32_t *__restrict__ ids, float *__restrict__ w,
+                                                   const float *__restrict__ gate_logit,
+                                                   float *__restrict__ gamma) {
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  topk_wave<EPL>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+  if (gamma != nullptr && lane_id() == 0) gamma[t] = 1.0f / (1.0f + expf(-gate_logit[t]));
+}
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *ids, float *w,
+                       const float *gate_logit, float *gamma, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(256);
+  const int epl = (E + kWave - 1) / kWave;
+  if (epl <= 1) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 2) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  return hipGetLastError();
+}
+
+// ============================================================ alignment, one block (n <= 1024, E <= 1024)
+// s_ids: the n slot ids in LDS.  1024 threads.  Writes every output array.
+__device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, int BM, int cap,
+                                            int32_t *s_cnt, int32_t *s_off, int *s_tmp, AlignOut al) {
+  constexpr int NT = 1024;
+  const int tid = threadIdx.x;
+  if (tid < E) s_cnt[tid] = 0;
+  __syncthreads();
+  if (tid < n) atomicAdd(&s_cnt[s_ids[tid]], 1);
+  __syncthreads();
+  const int padded = tid < E ? (s_cnt[tid] + BM - 1) / BM * BM : 0;
+  int total;
+  const int excl = block_excl_scan<NT>(padded, s_tmp, &total);
+  if (tid < E) s_off[tid] = excl;
+  if (tid == 0) s_off[E] = total;
+  __syncthreads();
+  // stable scatter: a slot's place is its rank among the earlier slots of its expert
+  if (tid < n) {
+    const int e = s_ids[tid];
+    int r = 0;
+    for (int i = 0; i < tid; ++i) r += (s_ids[i] == e) ? 1 : 0;
+    al.sorted[s_off[e] + r] = tid;
+  }
+  // padding and tail: every position that no slot takes holds the sentinel n
+  for (int p = tid; p < cap; p += NT) {
+    bool pad = true;
+    if (p < total) {
+      const int e = segment_of(s_off, E, p);
+      pad = (p - s_off[e]) >= s_cnt[e];
+    }
+    if (pad) al.sorted[p] = n;
+  }
+  for (int b = tid; b < cap / BM; b += NT) {
+    const int p = b * BM;
+    al.block_expert[b] = p < total ? segment_of(s_off, E, p) : -1;
+  }
+  if (tid < E) {
+    al.counts[tid] = s_cnt[tid];
+    al.offsets[tid] = s_off[tid];
+  }
+  if (tid == 0) {
+    al.offsets[E] = total;
+    al.num_padded[0] = total;
+  }
+}
+
+__global__ __launch_bounds__(1024) void align_small_kernel(const int32_t *__restrict__ ids, int n, int E, int BM,
+                                                           int cap, AlignOut al) {
+  __shared__ int32_t s_ids[kSmallSlots];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int s_tmp[1024 / kWave + 1];
+  if (threadIdx.x < n) s_ids[threadIdx.x] = ids[threadIdx.x];
+  __syncthreads();
+  align_block(s_ids, n, E, BM, cap, s_cnt, s_off, s_tmp, al);
+}
+
+hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s) {
+  hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, BM, (int)cap, al);
+  return hipGetLastError();
+}
+
+// Decode head: top-k of all T tokens (16 wavefronts) then the alignment, one block.
+template <int EPL>
+__global__ __launch_bounds__(1024) void topk_align_small_kernel(const float *__restrict__ logits,
+                                                                const float *__restrict__ gate_logit, int T, int E,
+                                                                int k, int renorm, int BM, int cap,
+                                                                int32_t *__restrict__ ids, float *__restrict__ w,
+                                                                float *__restrict__ gamma, AlignOut al) {
+  __shared__ int32_t s_ids[kSmallSlots];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int s_tmp[1024 / kWave + 1];
+  for (int t = wave_id(); t < T; t += 1024 / kWave)
+    topk_wave<EPL>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, w + (size_t)t * k,
+                   s_ids + t * k);
+  if (gamma != nullptr && threadIdx.x < T) gamma[threadIdx.x] = 1.0f / (1.0f + expf(-gate_logit[threadIdx.x]));
+  __syncthreads();
+  align_block(s_ids, T * k, E, BM, cap, s_cnt, s_off, s_tmp, al);
+}
+
+hipError_t launch_topk_align_small(const float *logits, const float *gate_logit, int T, int E, int k, int renorm,
+                                   int BM, int64_t cap, int32_t *ids, float *w, float *gamma, AlignOut al,
+                                   hipStream_t s) {
+  const int epl = (E + kWave - 1) / kWave;
+  dim3 grid(1), block(1024);
+  const int c = (int)cap;
+  if (epl <= 1) hipLaunchKernelGGL(topk_align_small_kernel<1>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  else if (epl <= 2) hipLaunchKernelGGL(topk_align_small_kernel<2>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  else if (epl <= 4) hipLaunchKernelGGL(topk_align_small_kernel<4>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  else if (epl <= 8) hipLaunchKernelGGL(topk_align_small_kernel<8>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  else hipLaunchKernelGGL(topk_align_small_kernel<16>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  return hipGetLastError();
+}
+
+// ============================================================ alignment, many blocks (any n)
+// 1. per-chunk histograms  hist[c][e]  (chunks of kAlignChunk slots)
+// 2. per-expert exclusive scan over chunks (in place) and the counts
+// 3. padded scan over experts: offsets, num_padded, block_expert
+// 4. scatter: position = offsets[e] + hist[c][e] + rank inside the chunk; sentinel fill
+size_t align_hist_ints(int64_t n, int E) {
+  const int64_t chunks = (n + kAlignChunk - 1) / kAlignChunk;
+  return (size_t)(chunks * E);
+}
+int align_large_kernels() { return 4; }
+
+__global__ __launch_bounds__(kAlignChunk) void align_hist_kernel(const int32_t *__restrict__ ids, int n, int E,
+                                                                 int32_t *__restrict__ hist) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kAlignChunk) s_cnt[e] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * kAlignChunk + threadIdx.x;
+  if (i < n) atomicAdd(&s_cnt[ids[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kAlignChunk) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// One block per expert: exclusive scan of hist[.][e] over the chunks.
+__global__ __launch_bounds__(256) void align_colscan_kernel(int32_t *__restrict__ hist, int chunks, int E,
+                                                            int32_t *__restrict__ counts) {
+  __shared__ int s_tmp[256 / kWave + 1];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < chunks; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int v = c < chunks ? hist[(size_t)c * E + e] : 0;
+    int total;
+    const int ex = block_excl_scan<256>(v, s_tmp, &total);
+    if (c < chunks) hist[(size_t)c * E + e] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+__global__ __launch_bounds__(1024) void align_offsets_kernel(const int32_t *__restrict__ counts, int E, int BM,
+                                                             int cap, AlignOut al) {
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int s_tmp[1024 / kWave + 1];
+  const int tid = threadIdx.x;
+  const int padded = tid < E ? (counts[tid] + BM - 1) / BM * BM : 0;
+  int total;
+  const int excl = block_excl_scan<1024>(padded, s_tmp, &total);
+  if (tid < E) {
+    s_off[tid] = excl;
+    al.offsets[tid] = excl;
+  }
+  if (tid == 0) {
+    s_off[E] = total;
+    al.offsets[E] = total;
+    al.num_padded[0] = total;
+  }
+  __syncthreads();
+  for (int b = tid; b < cap / BM; b += 1024) {
+    const int p = b * BM;
+    al.block_expert[b] = p < total ? segment_of(s_off, E, p) : -1;
+  }
+}
+
+__global__ __launch_bounds__(kAlignChunk) void align_scatter_kernel(const int32_t *__restrict__ ids, int n, int E,
+                                                                    int cap, const int32_t *__restrict__ hist,
+                                                                    AlignOut al) {
+  __shared__ int32_t s_ids[kAlignChunk];
+  const int base = blockIdx.x * kAlignChunk;
+  const int i = base + threadIdx.x;
+  s_ids[threadIdx.x] = i < n ? ids[i] : -1;
+  __syncthreads();
+  if (i < n) {
+    const int e = s_ids[threadIdx.x];
+    int r = 0;
+    for (int q = 0; q < (int)threadIdx.x; ++q) r += (s_ids[q] == e) ? 1 : 0;
+    al.sorted[al.offsets[e] + hist[(size_t)blockIdx.x * E + e] + r] = i;
+  }
+  const int total = al.num_padded[0];
+  for (int p = i; p < cap; p += gridDim.x * kAlignChunk) {
+    bool pad = true;
+    if (p < total) {
+      const int e = segment_of(al.offsets, E, p);
+      pad = (p - al.offsets[e]) >= al.counts[e];
+    }
+    if (pad) al.sorted[p] = n;
+  }
+}
+
+hipError_t launch_align_large(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, int32_t *hist,
+                              hipStream_t s) {
+  const int chunks = (n + kAlignChunk - 1) / kAlignChunk;
+  hipLaunchKernelGGL(align_hist_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, hist);
+  hipLaunchKernelGGL(align_colscan_kernel, dim3(E), dim3(256), 0, s, hist, chunks, E, al.counts);
+  hipLaunchKernelGGL(align_offsets_kernel, dim3(1), dim3(1024), 0, s, al.counts, E, BM, (int)cap, al);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, (int)cap, hist, al);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+"""Helpers shared by the GPU tests: layer construction (cached), device<->host views, and the
+comparison of one layer call against the CPU oracle."""
+import functools
+
+import numpy as np
+import torch
+
+import oracle
+from synth import configs
+
+TOL = {"bf16": 1e-3, "fp8": 5e-3}
+
+
+def bf16_bits(t):
+    """bf16 CUDA tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_values(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_dev_bf16(bits, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+@functools.lru_cache(maxsize=4)
+def _experts(H, E, I, I_s, wtype, seed, replica):
+    cfg = configs.LayerConfig("cache", H=H, E=E, k=1, I=I, I_s=I_s, wtype=wtype, bias="none", BM=16)
+    return configs.make_layer(cfg, seed=seed, replica=replica)
+
+
+def host_layer(cfg, seed=0, replica=0):
+    """Host layer dict; expert banks of equal shape and seed are generated once and shared."""
+    L = configs.make_layer(cfg, seed=seed, replica=replica, with_experts=False)
+    ex = _experts(cfg.H, cfg.E, cfg.I, cfg.I_s, cfg.wtype, seed, replica)
+    for key in ("w_gate_up", "w_down", "s_gate_up", "s_down", "shared_w_gate_up", "shared_w_down",
+                "shared_s_gate_up", "shared_s_down"):
+        if key in ex:
+            L[key] = ex[key]
+    return L
+
+
+_dev_cache = {}
+
+
+def device_layer(L):
+    from speculative_verify_moe_amd import Layer
+    key = (L["name"], L["H"], L["E"], L["k"], L["I"], L["I_s"], L["wtype"], id(L["w_gate_up"]))
+    if key not in _dev_cache:
+        if len(_dev_cache) >= 3:
+            _dev_cache.clear()
+            torch.cuda.empty_cache()
+        # the entry keeps L alive, so the id() in the key cannot be reused while cached
+        _dev_cache[key] = (L, Layer.from_host(L))
+    return _dev_cache[key][1]
+
+
+def run_layer(L, x_bits):
+    """One moe_layer_forward call; returns host copies of out bits, logits, ids, w."""
+    from speculative_verify_moe_amd import moe_layer_forward
+    D = device_layer(L)
+    x = to_dev_bf16(x_bits)
+    T = x_bits.shape[0]
+    logits = torch.empty((T, L["E"]), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, L["k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, L["k"]), dtype=torch.float32, device="cuda")
+    out = moe_layer_forward(x, D, logits_out=logits, ids_out=ids, w_out=w)
+    torch.cuda.synchronize()
+    return bf16_bits(out), logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check_layer(L, x_bits, tokens=None, report=None):
+    """Compare one layer call with the oracle.  Routing: bit-exact ids from the device logits,
+    weights within 1e-6; logits within 1e-5 (1 + |L|) of fp64; output relL2 / max-abs bars."""
+    out_bits, lg, ids, w = run_layer(L, x_bits)
+    T = x_bits.shape[0]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = np.asarray(tokens, dtype=np.int32)
+    # logits against fp64 on the sampled tokens
+    L64 = oracle.router_logits(x_bits[tokens], L["router_w"], L["router_b"])
+    err = np.abs(lg[tokens].astype(np.float64) - L64)
+    assert np.all(err <= 1e-5 * (1.0 + np.abs(L64))), f"logit error {err.max()}"
+    # routing from the device logits: ids exact for every token, weights within 1e-6
+    ids_ref, w_ref = oracle.route_topk(lg, L["k"], L.get("renormalize", True))
+    assert np.array_equal(ids, ids_ref), "top-k ids differ from the oracle"
+    assert np.max(np.abs(w.astype(np.float64) - w_ref)) <= 1e-6
+    # layer output on the sampled tokens, routed as the device routed
+    ref = oracle.moe_layer(x_bits, L, ids_ref, w_ref, tokens=tokens, rounding=True)
+    got = bf16_values(out_bits[tokens])
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mx = np.max(np.abs(got - ref))
+    tol = TOL[L["wtype"]]
+    if report is not None:
+        report.update(rel_l2=rel, max_abs=mx, max_ref=np.max(np.abs(ref)))
+    assert rel <= tol, f"relL2 {rel:.3e} > {tol}"
+    assert mx <= 1e-2 * np.max(np.abs(ref)), f"max-abs {mx:.3e} > 1e-2 * {np.max(np.abs(ref)):.3e}"
+    return out_bits

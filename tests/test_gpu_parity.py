@@ -1,0 +1,254 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI (GPU only).
+
+Bars: routing ids and every alignment array bit-exact; router weights within 1e-6;
+logits within 1e-5 (1 + |L|) of fp64; layer output relL2 <= 1e-3 (bf16 weights) or
+<= 5e-3 (fp8 weights) and max-abs <= 1e-2 max|ref|; bitwise identical output run to run.
+The oracle routes from the logits the device produced, so a legitimate fp32 near-tie
+cannot flip an expert between the two sides; the logits are checked separately.
+"""
+import hashlib
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import speculative_verify_moe_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- top-k routing
+
+ROUTE_CASES = [
+    # name, T, E, k, kind, renorm
+    ("tiny", 4, 16, 2, "normal", True),
+    ("qwen36_T8", 8, 256, 8, "normal", True),
+    ("flash_T6", 6, 512, 10, "normal", True),
+    ("prefill_T4096", 4096, 256, 8, "normal", True),
+    ("ties", 100, 64, 8, "ties", True),
+    ("E1024_k32", 33, 1024, 32, "normal", True),
+    ("E1", 5, 1, 1, "normal", True),
+    ("E100_ragged_lanes", 37, 100, 7, "normal", True),
+    ("no_renorm", 19, 256, 8, "normal", False),
+    ("spread", 7, 300, 5, "wide", True),
+]
+
+
+def _logits(kind, T, E, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "ties":
+        return rng.choice(np.array([-1.0, -0.0, 0.0, 1.0], np.float32), size=(T, E))
+    if kind == "wide":
+        return (rng.standard_normal((T, E)) * 30).astype(np.float32)
+    return rng.standard_normal((T, E)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: c[0])
+def test_route_topk_bit_exact(case):
+    from speculative_verify_moe_amd import moe_route_topk
+    name, T, E, k, kind, renorm = case
+    _say(f"[route] {name} T={T} E={E} k={k}")
+    lg = _logits(kind, T, E, zlib.crc32(name.encode()) % 1000)
+    ids, w = moe_route_topk(torch.from_numpy(lg).cuda(), k, renormalize=renorm)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route_topk(lg, k, renorm)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)) <= 1e-6
+
+
+# ---------------------------------------------------------------- alignment
+
+ALIGN_CASES = [
+    # name, T, k, E, BM, extra capacity blocks
+    ("tiny", 4, 2, 16, 16, 0),
+    ("qwen36_T8", 8, 8, 256, 16, 0),
+    ("qwen36_T32", 32, 8, 256, 16, 3),
+    ("flash_T6", 6, 10, 512, 16, 0),
+    ("one_block_max", 64, 16, 1024, 32, 0),
+    ("bm128", 50, 8, 64, 128, 1),
+    ("prefill_T4096", 4096, 8, 256, 64, 0),
+    ("prefill_flash", 4096, 10, 512, 64, 2),
+    ("large_ragged", 1337, 3, 200, 16, 1),
+    ("E1", 300, 1, 1, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES, ids=lambda c: c[0])
+def test_align_bit_exact(case):
+    from speculative_verify_moe_amd import moe_align, moe_align_capacity
+    name, T, k, E, BM, extra = case
+    _say(f"[align] {name} T={T} k={k} E={E} BM={BM}")
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    cap = moe_align_capacity(T, k, E, BM) + extra * BM
+    got = moe_align(torch.from_numpy(ids).cuda(), E, BM, cap=cap)
+    torch.cuda.synchronize()
+    ref = oracle.align(ids, E, BM, cap)
+    assert np.array_equal(got["sorted_ids"].cpu().numpy(), ref["sorted_ids"])
+    assert np.array_equal(got["block_expert"].cpu().numpy(), ref["block_expert"])
+    assert np.array_equal(got["expert_counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), ref["offsets"])
+    assert int(got["num_padded"].cpu().numpy()[0]) == ref["num_padded"]
+
+
+def test_align_of_device_routing_at_prefill_size():
+    """Route then align on the device at T=4096; both stages bit-exact."""
+    from speculative_verify_moe_amd import moe_align, moe_route_topk
+    lg = _logits("normal", 4096, 256, 5)
+    ids, _ = moe_route_topk(torch.from_numpy(lg).cuda(), 8)
+    al = moe_align(ids, 256, 64)
+    torch.cuda.synchronize()
+    ids_ref, _ = oracle.route_topk(lg, 8)
+    ref = oracle.align(ids_ref, 256, 64, al["cap"])
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(al["sorted_ids"].cpu().numpy(), ref["sorted_ids"])
+
+
+# ---------------------------------------------------------------- whole layer
+
+LAYER_CASES = [
+    # name, recipe, T, sampled tokens (None: all)
+    ("tiny_T4", "tiny", 4, None),
+    ("tiny_T1", "tiny", 1, None),
+    ("tiny_T9", "tiny", 9, None),
+    ("tiny_T64", "tiny", 64, None),
+    ("tiny_T65_prefill", "tiny", 65, None),
+    ("tiny_T100_prefill", "tiny", 100, None),
+    ("tiny_T600_prefill", "tiny", 600, None),
+    ("qwen36_T1", "qwen36_a3b", 1, None),
+    ("qwen36_T8", "qwen36_a3b", 8, None),
+    ("qwen36_T5", "qwen36_a3b", 5, None),
+    ("qwen36_T32", "qwen36_a3b", 32, None),
+    ("qwen36_zipf_T32", "qwen36_a3b_zipf", 32, None),
+    ("qwen36_T64", "qwen36_a3b", 64, [0, 13, 31, 63]),
+    ("flash_fp8_T1", "flash_next_fp8", 1, None),
+    ("flash_fp8_T6", "flash_next_fp8", 6, None),
+    ("prefill_T4096", "prefill", 4096, [0, 1, 63, 64, 777, 2048, 3001, 4031, 4095]),
+    ("prefill_T200", "prefill", 200, [0, 64, 127, 128, 199]),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: c[0])
+def test_layer_parity(case):
+    name, recipe, T, tokens = case
+    _say(f"[layer] {name} recipe={recipe} T={T}")
+    cfg = configs.CONFIGS[recipe]
+    L = G.host_layer(cfg)
+    x = configs.make_tokens(cfg, T)
+    rep = {}
+    G.check_layer(L, x, tokens=tokens, report=rep)
+    _say(f"[layer] {name} relL2={rep['rel_l2']:.3e} max_abs={rep['max_abs']:.3e}")
+
+
+def test_layer_tiny_variants():
+    """Ragged and degenerate shapes at the tiny size: k = E, k = 1, one expert, shared expert of
+    a different width, no renormalisation, H not a multiple of 512."""
+    variants = [dict(k=16), dict(k=1), dict(E=1, k=1), dict(I_s=64, bias="normal"), dict(I_s=192),
+                dict(renormalize=False, I_s=128), dict(H=192, I=64), dict(H=128, I=256, I_s=64)]
+    for v in variants:
+        for T in (3, 70):
+            cfg = configs.with_shape(configs.CONFIGS["tiny"], **v)
+            if T > 64 and (cfg.H % 128 != 0):
+                continue
+            _say(f"[layer-variant] {v} T={T}")
+            L = configs.make_layer(cfg, seed=11)
+            x = configs.make_tokens(cfg, T, seed=11)
+            G.check_layer(L, x)
+
+
+def test_zero_tokens_is_a_no_op():
+    from speculative_verify_moe_amd import moe_layer_forward
+    cfg = configs.CONFIGS["tiny"]
+    D = G.device_layer(G.host_layer(cfg))
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    out = moe_layer_forward(x, D)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.H)
+
+
+def test_zero_input_gives_zero_output():
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], I_s=64)
+    L = configs.make_layer(cfg, seed=2)
+    x = np.zeros((5, cfg.H), np.uint16)
+    out, _, _, _ = G.run_layer(L, x)
+    assert np.all((out & 0x7FFF) == 0)
+
+
+# ---------------------------------------------------------------- determinism, batch invariance
+
+def _digest(bits):
+    return hashlib.sha256(bits.tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("recipe,T,runs", [("qwen36_a3b", 8, 20), ("flash_next_fp8", 6, 10), ("prefill", 4096, 5)])
+def test_bitwise_deterministic(recipe, T, runs):
+    from speculative_verify_moe_amd import moe_layer_forward
+    _say(f"[determinism] {recipe} T={T} runs={runs}")
+    cfg = configs.CONFIGS[recipe]
+    D = G.device_layer(G.host_layer(cfg))
+    x = G.to_dev_bf16(configs.make_tokens(cfg, T))
+    digests = set()
+    for _ in range(runs):
+        out = moe_layer_forward(x, D)
+        torch.cuda.synchronize()
+        digests.add(_digest(G.bf16_bits(out)))
+    assert len(digests) == 1
+
+
+def test_verify_block_rows_equal_single_token_calls():
+    """Row t of a T=8 verify-block call is bitwise the T=1 call on token t (decode path)."""
+    from speculative_verify_moe_amd import moe_layer_forward
+    cfg = configs.CONFIGS["qwen36_a3b"]
+    D = G.device_layer(G.host_layer(cfg))
+    xb = configs.make_tokens(cfg, 8)
+    x = G.to_dev_bf16(xb)
+    block = G.bf16_bits(moe_layer_forward(x, D))
+    for t in range(8):
+        one = G.bf16_bits(moe_layer_forward(x[t:t + 1].contiguous(), D))
+        assert np.array_equal(one[0], block[t]), f"row {t}"
+
+
+# ---------------------------------------------------------------- experts entry point
+
+@pytest.mark.parametrize("recipe,T,BM", [("tiny", 4, 16), ("qwen36_a3b", 8, 16), ("tiny", 300, 64),
+                                         ("prefill", 4096, 64), ("tiny", 130, 128)])
+def test_experts_forward_parity(recipe, T, BM):
+    from speculative_verify_moe_amd import moe_align, moe_experts_forward, moe_route_topk
+    _say(f"[experts] {recipe} T={T} BM={BM}")
+    cfg = configs.CONFIGS[recipe]
+    L = G.host_layer(cfg)
+    xb = configs.make_tokens(cfg, T)
+    lg = oracle.router_logits(xb, L["router_w"], L["router_b"]).astype(np.float32)
+    ids, w = moe_route_topk(torch.from_numpy(lg).cuda(), cfg.k)
+    al = moe_align(ids, cfg.E, BM)
+    D = G.device_layer(L)
+    routed = D.routed
+    out = moe_experts_forward(G.to_dev_bf16(xb), routed, cfg.k, w, al, BM)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route_topk(lg, cfg.k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    tokens = np.arange(T) if T <= 300 else np.array([0, 5, 1000, 2047, 4095])
+    Lr = dict(L, I_s=0)
+    ref = oracle.moe_layer(xb, Lr, ids_ref, w_ref, tokens=tokens, rounding=True)
+    got = G.bf16_values(G.bf16_bits(out)[tokens])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-3
+    assert np.max(np.abs(got - ref)) <= 1e-2 * np.max(np.abs(ref))
