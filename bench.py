@@ -36,6 +36,7 @@ WORKLOADS = {
     "prefill_T4096": ("prefill", 4096, "Qwen3.6-35B-A3B-like MoE layer, 4096-token prefill chunk"),
 }
 
+FUSED_STAGES = ["moe_decode_fused"]
 DECODE_STAGES = ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"]
 PREFILL_STAGES = ["router_split", "router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
                   "combine"]
@@ -50,6 +51,7 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="layer replicas in HBM (0: 16 decode, 2 prefill)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--four-kernel", action="store_true", help="run decode blocks as four kernels, not the fused one")
     return p.parse_args()
 
 
@@ -90,6 +92,8 @@ def main():
     L_rep = args.replicas or (2 if prefill else 16)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.four_kernel:
+        moe.moe_set_option(moe.MOE_OPT_DECODE_FUSED, 0)
 
     # ---- inputs: replica 0's expert banks, copied to L distinct HBM buffers; each replica has
     # its own router, bias and tokens (so each step touches its own set of experts)
@@ -114,14 +118,15 @@ def main():
         layers.append(lay)
         xs.append(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev))
         outs.append(torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev))
-        wss.append(torch.empty((moe.moe_layer_workspace_size(T, lay),), dtype=torch.uint8, device=dev))
+        wss.append(torch.zeros((moe.moe_layer_workspace_size(T, lay),), dtype=torch.uint8, device=dev))
         host_routers.append(hr)
         host_x.append(xb)
     del base
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     plan = moe.moe_describe_plan(T, layers[0])
-    stages = PREFILL_STAGES if prefill else DECODE_STAGES
+    fused = "decode-fused" in plan
+    stages = PREFILL_STAGES if prefill else (FUSED_STAGES if fused else DECODE_STAGES)
     nst = len(stages)
 
     # realised routing per replica (touched experts) for the algorithmic byte counts
@@ -181,15 +186,22 @@ def main():
     ms_per_step = elapsed * 1e3 / K
     value = T * K / elapsed
 
-    # dominant kernel: the gate/up expert stream (decode) or the gate/up MFMA GEMM (prefill)
-    dom = 2 if not prefill else 4
+    # dominant kernel: the fused layer kernel, the gate/up expert stream (four-kernel decode) or
+    # the gate/up MFMA GEMM (prefill)
+    dom = 0 if fused else (4 if prefill else 2)
     dom_name = stages[dom]
     dom_ms = stage_ms[:, dom]
-    src = ["speculative_verify_moe_amd/csrc/gemv.hip" if not prefill else "speculative_verify_moe_amd/csrc/gemm.hip",
-           "speculative_verify_moe_amd/csrc/device.h"]
+    csrc = "speculative_verify_moe_amd/csrc/"
+    if fused:
+        src = [csrc + "fused.hip", csrc + "topk.h", csrc + "device.h"]
+    elif prefill:
+        src = [csrc + "gemm.hip", csrc + "device.h"]
+    else:
+        src = [csrc + "gemv.hip", csrc + "device.h"]
     src_hash = source_hash(src)
     if not prefill:
-        alg_bytes = np.array([gate_up_bytes(n) for n in nt_steps], dtype=np.float64)
+        per = layer_bytes if fused else gate_up_bytes
+        alg_bytes = np.array([per(n) for n in nt_steps], dtype=np.float64)
         achieved = alg_bytes.sum() / (dom_ms.sum() * 1e-3) / 1e9
         traffic = load_traffic(dom_name, args.workload, src_hash)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -251,7 +263,8 @@ def main():
         "vs_baseline": None, "dtype": cfg.wtype if cfg.wtype == "bf16" else "fp8-e4m3 weights, bf16 activations",
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
-                   "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep, "path": plan.split()[0]},
+                   "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep,
+                   "path": plan.split()[0].split("=")[1]},
         "roofline": roofline, "layer": layer, "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1), "device": torch.cuda.get_device_name(0),
     }

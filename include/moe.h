@@ -74,7 +74,7 @@ typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1 } moe_wtype;
 typedef struct {
   int32_t wtype;           /* moe_wtype */
   int32_t num_experts;     /* n; a shared bank with n == 0 means "no shared expert" */
-  int32_t hidden;          /* H, multiple of 64 */
+  int32_t hidden;          /* H, multiple of 64, at most 8192 */
   int32_t inter;           /* I, multiple of 64 */
   const void *w_gate_up;   /* [n][2I][H]: rows [0,I) gate, rows [I,2I) up */
   const void *w_down;      /* [n][H][I] */
@@ -145,7 +145,10 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
                                const int32_t *expert_counts, const int32_t *expert_offsets, int32_t BM,
                                int64_t cap, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes moe_layer_forward needs for T tokens. */
+/* Workspace bytes moe_layer_forward needs for T tokens.  The workspace is scratch for
+ * one call at a time; a decode/verify block on the fused kernel also keeps its grid
+ * barrier words there (each call writes a fresh 31-bit token, so no reset is needed;
+ * zeroing a new workspace once rules out a stale word that happens to equal a token). */
 size_t moe_layer_workspace_size(int32_t T, const moe_layer *L);
 
 /* The whole layer: router, top-k, alignment, routed experts, shared expert and
@@ -165,12 +168,22 @@ const char *moe_last_error(void);
  * buffer, valid until the next call on the thread). */
 const char *moe_describe_plan(int32_t T, const moe_layer *L);
 
+/* Options of the calling thread (no environment variable is read).
+ *   MOE_OPT_DECODE_FUSED: 1 (default) runs decode/verify blocks that fit the fused
+ *   kernel (H <= 2048, I and I_s <= 512, tokens and intermediates within LDS) as one
+ *   kernel -- router, top-k, alignment, experts and combine with two grid-wide barriers
+ *   (one block per CU, all resident); 0 runs the same steps as four kernels (router,
+ *   top-k + alignment, gate/up, down + combine).  Both give bitwise the same routing and
+ *   output.  Other shapes always take the four-kernel path. */
+enum { MOE_OPT_DECODE_FUSED = 1 };
+moe_status moe_set_option(int32_t key, int32_t value);
+
 /* Measurement hook.  events: n_events hipEvent_t handles (host array), or NULL to
  * turn the hook off.  While set on a thread, each moe_layer_forward call on that
  * thread records events[i] on its stream just before its stage i and
  * events[n_stages] after the last stage (only as many as n_events allows).  A stage
  * is one kernel or a fixed group of kernels; moe_describe_plan names the stages in
- * launch order (decode: 4 stages, prefill: 7). */
+ * launch order (fused decode: 1 stage, four-kernel decode: 4, prefill: 7). */
 moe_status moe_set_stage_events(void *const *events, int32_t n_events);
 
 #ifdef __cplusplus

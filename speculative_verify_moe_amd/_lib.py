@@ -49,6 +49,7 @@ EXPORTS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_describe_plan": (ctypes.c_char_p, [_I32, ctypes.POINTER(_Layer)]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(_P), _I32]),
+    "moe_set_option": (ctypes.c_int, [_I32, _I32]),
 }
 for _name, (_res, _args) in EXPORTS.items():
     _f = getattr(_lib, _name)
@@ -180,6 +181,13 @@ def moe_describe_plan(T, layer):
     return _lib.moe_describe_plan(T, ctypes.byref(layer.struct)).decode()
 
 
+MOE_OPT_DECODE_FUSED = 1
+
+
+def moe_set_option(key, value):
+    _check(_lib.moe_set_option(key, value))
+
+
 def moe_set_stage_events(events):
     """events: list of torch.cuda.Event(enable_timing=True) (recorded on the layer's stream), or None."""
     if not events:
@@ -261,7 +269,7 @@ def moe_layer_forward(x, layer, out=None, logits_out=None, ids_out=None, w_out=N
         if t is not None:
             _dev(t, dt, name)
     if ws is None:
-        ws = _workspace(moe_layer_workspace_size(T, layer), x.device)
+        ws = torch.zeros((max(moe_layer_workspace_size(T, layer), 1),), dtype=torch.uint8, device=x.device)
     _check(_lib.moe_layer_forward(_ptr(x), T, ctypes.byref(layer.struct), _ptr(out), _ptr(logits_out), _ptr(ids_out),
                                   _ptr(w_out), _ptr(ws), ws.numel(), _stream()))
     return out

@@ -6,7 +6,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "route.hip", "gemv.hip", "gemm.hip", "fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # packed fp32 vector ops stay off: plain scalar fp32 code only

@@ -25,6 +25,7 @@ thread_local char g_err[512];
 thread_local char g_plan[2048];
 thread_local void *g_events[64];
 thread_local int g_nevents = 0;
+thread_local int g_opt_fused = 1;
 
 moe_status fail(moe_status st, const char *fmt, ...) {
   va_list ap;
@@ -105,8 +106,8 @@ moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, i
 }
 
 moe_status check_hidden(int H) {
-  if (H < 64 || H % 64 != 0 || H > 16384)
-    return fail(MOE_ERR_INVALID_ARG, "hidden = %d: must be a multiple of 64 in [64, 16384]", H);
+  if (H < 64 || H % 64 != 0 || H > 8192)
+    return fail(MOE_ERR_INVALID_ARG, "hidden = %d: must be a multiple of 64 in [64, 8192]", H);
   return MOE_OK;
 }
 
@@ -125,7 +126,7 @@ struct LayerPlan {
   int BM = 16;
   int64_t cap = 0;
   size_t off_logits, off_gate, off_ids, off_w, off_gamma, off_counts, off_offsets, off_np, off_sorted, off_bexp;
-  size_t off_h, off_hs, off_w3, off_hist, off_y, off_ys;
+  size_t off_h, off_hs, off_w3, off_hist, off_y, off_ys, off_tl, off_bar;
   size_t total = 0;
 };
 
@@ -160,6 +161,8 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
   if (p.path == PATH_DECODE) {
     p.off_h = take((size_t)n * I * 2);
     p.off_hs = take((size_t)T * I_s * 2);
+    p.off_tl = take(touched_ints(E, n) * 4);
+    p.off_bar = take((size_t)kBarrierWords * 4);
     p.off_w3 = p.off_hist = p.off_y = p.off_ys = 0;
   } else {
     p.off_w3 = take((size_t)3 * (E + 1) * H * 2);
@@ -168,6 +171,7 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     p.off_hs = take((size_t)T * I_s * 2);
     p.off_y = take((size_t)n * H * 2);
     p.off_ys = take((size_t)T * H * 2);
+    p.off_tl = p.off_bar = 0;
   }
   p.total = o;
   return p;
@@ -234,6 +238,15 @@ size_t moe_align_workspace_size(int32_t T, int32_t k, int32_t E) {
 
 const char *moe_last_error(void) { return g_err; }
 
+moe_status moe_set_option(int32_t key, int32_t value) {
+  if (key == MOE_OPT_DECODE_FUSED) {
+    if (value != 0 && value != 1) return fail(MOE_ERR_INVALID_ARG, "MOE_OPT_DECODE_FUSED takes 0 or 1 (got %d)", value);
+    g_opt_fused = value;
+    return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID_ARG, "unknown option key %d", key);
+}
+
 moe_status moe_set_stage_events(void *const *events, int32_t n_events) {
   if (events == nullptr || n_events <= 0) {
     g_nevents = 0;
@@ -295,7 +308,7 @@ size_t moe_experts_workspace_size(int32_t T, int32_t k, const moe_bank *routed, 
   if (routed == nullptr || T <= 0 || k < 1 || routed->num_experts < 1 || !valid_bm(BM)) return 0;
   const int64_t n = (int64_t)T * k;
   const size_t I = (size_t)routed->inter, H = (size_t)routed->hidden;
-  if (is_decode(T, k)) return align_up((size_t)n * I * 2, 256);
+  if (is_decode(T, k)) return align_up((size_t)n * I * 2, 256) + align_up(touched_ints(routed->num_experts, n) * 4, 256);
   const int64_t cap = capacity(T, k, routed->num_experts, BM);
   return align_up((size_t)cap * I * 2, 256) + align_up((size_t)n * H * 2, 256);
 }
@@ -336,11 +349,17 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   if ((st = check_device()) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (decode) {
+    const int64_t n = (int64_t)T * k;
+    const Touched tl = touched_at((int32_t *)((char *)ws + align_up((size_t)n * routed->inter * 2, 256)), E);
+    if ((st = launched(launch_compact_touched(expert_counts, expert_offsets, sorted_ids, E, tl, s),
+                       "compact_touched")) != MOE_OK)
+      return st;
     GemvArgs g;
     fill_gemv(g, x, T, H, k, routed, E);
-    g.counts = expert_counts;
-    g.offsets = expert_offsets;
-    g.sorted = sorted_ids;
+    g.tl_n = tl.n;
+    g.tl_e = tl.e;
+    g.tl_start = tl.start;
+    g.tl_slots = tl.slots;
     g.topk_w = topk_w;
     g.h = (uint16_t *)ws;
     g.out = out;
@@ -385,6 +404,15 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
   }
   const LayerPlan p = plan_layer(T, L);
   const int E = L->num_experts, k = L->top_k;
+  const bool shared = L->shared.num_experts > 0;
+  if (p.path == PATH_DECODE && g_opt_fused != 0 &&
+      fused_decode_fits(T, L->hidden, E, k, L->routed.inter, shared ? L->shared.inter : 0, L->routed.wtype)) {
+    snprintf(g_plan, sizeof(g_plan),
+             "path=decode-fused T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 moe_decode_fused "
+             "(router, top-k, alignment, gate/up, down, combine; one kernel, two grid barriers)",
+             T, E, k, p.BM, (long long)p.cap, p.total);
+    return g_plan;
+  }
   if (p.path == PATH_DECODE) {
     snprintf(g_plan, sizeof(g_plan),
              "path=decode T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_rows grid=%d; "
@@ -430,21 +458,68 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
               (int32_t *)(base + p.off_offsets), (int32_t *)(base + p.off_np)};
   Stager sg(s);
 
+  const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 &&
+                     fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0, L->routed.wtype);
+  if (fused) {
+    FusedArgs f{};
+    f.x = x;
+    f.T = T;
+    f.H = H;
+    f.E = E;
+    f.k = k;
+    f.I = L->routed.inter;
+    f.I_s = shared ? L->shared.inter : 0;
+    f.renorm = L->renormalize != 0;
+    f.has_shared = shared ? 1 : 0;
+    f.BM = p.BM;
+    f.cap = (int)p.cap;
+    f.wtype = L->routed.wtype;
+    f.w_r = L->router_w;
+    f.b_r = L->router_b;
+    f.w_sg = shared ? L->shared_gate_w : nullptr;
+    f.w_gu = L->routed.w_gate_up;
+    f.s_gu = L->routed.s_gate_up;
+    f.w_d = L->routed.w_down;
+    f.s_d = L->routed.s_down;
+    if (shared) {
+      f.ws_gu = L->shared.w_gate_up;
+      f.ss_gu = L->shared.s_gate_up;
+      f.ws_d = L->shared.w_down;
+      f.ss_d = L->shared.s_down;
+    }
+    f.logits = logits;
+    f.gate_logit = gate;
+    f.ids = ids;
+    f.topw = w;
+    f.gamma = gamma;
+    f.al = al;
+    f.h = (uint16_t *)(base + p.off_h);
+    f.h_s = (uint16_t *)(base + p.off_hs);
+    f.out = out;
+    f.bar = (unsigned *)(base + p.off_bar);
+    sg.mark();
+    if ((st = launched(launch_fused_decode(f, s, nullptr, 0), "moe_decode_fused")) != MOE_OK) return st;
+    sg.mark();
+    return MOE_OK;
+  }
+
   if (p.path == PATH_DECODE) {
     sg.mark();
     if ((st = launched(launch_router_rows(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
                                           logits, gate, s), "router_rows")) != MOE_OK)
       return st;
     sg.mark();
+    const Touched tl = touched_at((int32_t *)(base + p.off_tl), E);
     if ((st = launched(launch_topk_align_small(logits, shared ? gate : nullptr, T, E, k, L->renormalize != 0, p.BM,
-                                               p.cap, ids, w, shared ? gamma : nullptr, al, s),
+                                               p.cap, ids, w, shared ? gamma : nullptr, al, tl, s),
                        "topk_align_small")) != MOE_OK)
       return st;
     GemvArgs g;
     fill_gemv(g, x, T, H, k, &L->routed, E);
-    g.counts = al.counts;
-    g.offsets = al.offsets;
-    g.sorted = al.sorted;
+    g.tl_n = tl.n;
+    g.tl_e = tl.e;
+    g.tl_start = tl.start;
+    g.tl_slots = tl.slots;
     g.topk_w = w;
     g.has_shared = shared ? 1 : 0;
     if (shared) {

@@ -1,8 +1,8 @@
 // device.h -- small device helpers shared by the gfx950 kernels of the MoE layer.
 //
-// Wave64 everywhere: a wavefront is 64 lanes, reductions are xor butterflies whose
-// result is bitwise identical in every lane (each step adds the same two operands
-// in every lane pair), so every reduction here has one fixed order.
+// Wave64 everywhere: a wavefront is 64 lanes in four 16-lane DPP rows.  Reductions use
+// DPP permutations inside a row and readlane across rows; every step has one fixed
+// pairing, so every reduction here has one fixed order (bitwise reproducible).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,18 +56,100 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// DPP lane permutations (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1],
+// row_half_mirror (lane i <-> 7-i in each 8-lane half row), row_mirror (i <-> 15-i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Sum over each 16-lane row: every lane of the row ends with the same value (each step
+// adds a lane and its mirror partner, the same two operands on both sides).
+// (The DPP source is read with bound_ctrl set, the form the compiler folds into a single
+// DPP-modified add; every lane of a full wavefront is a valid source for these patterns,
+// so the zero fill is never taken and the sums are those of a plain move plus add.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_src(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_add_src<kDppXor1>(v);
+  v += dpp_add_src<kDppXor2>(v);
+  v += dpp_add_src<kDppHalfMirror>(v);
+  v += dpp_add_src<kDppMirror>(v);
   return v;
 }
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Sum over the wavefront, returned uniform: row sums, then (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
 
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t lane_value_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Maximum over the wavefront, returned uniform.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
+  v = max_u64(v, dpp_u64<kDppXor1>(v));
+  v = max_u64(v, dpp_u64<kDppXor2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  return max_u64(max_u64(lane_value_u64(v, 0), lane_value_u64(v, 16)),
+                 max_u64(lane_value_u64(v, 32), lane_value_u64(v, 48)));
+}
+
+// DPP row broadcasts (GFX9): lane 15 of each row into the next row, lane 31 into rows 2
+// and 3.  Rows outside the row mask keep `old`.
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppRowShr1 = 0x111;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_upd_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+// Maximum / minimum over the wavefront, returned uniform: row reductions, then the row
+// broadcasts carry the running value into lane 63.  `old` is the operation's identity, so
+// each step compiles to a single DPP-modified max / min.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_upd_u32<kDppXor1, 0xF>(0u, v));
+  v = max(v, dpp_upd_u32<kDppXor2, 0xF>(0u, v));
+  v = max(v, dpp_upd_u32<kDppHalfMirror, 0xF>(0u, v));
+  v = max(v, dpp_upd_u32<kDppMirror, 0xF>(0u, v));
+  v = max(v, dpp_upd_u32<kDppRowBcast15, 0xA>(0u, v));
+  v = max(v, dpp_upd_u32<kDppRowBcast31, 0xC>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_upd_u32<kDppXor1, 0xF>(~0u, v));
+  v = min(v, dpp_upd_u32<kDppXor2, 0xF>(~0u, v));
+  v = min(v, dpp_upd_u32<kDppHalfMirror, 0xF>(~0u, v));
+  v = min(v, dpp_upd_u32<kDppMirror, 0xF>(~0u, v));
+  v = min(v, dpp_upd_u32<kDppRowBcast15, 0xA>(~0u, v));
+  v = min(v, dpp_upd_u32<kDppRowBcast31, 0xC>(~0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Inclusive prefix sum over the wavefront's lanes (Hillis-Steele within each 16-lane row
+// with row shifts, then the row broadcasts); lanes shifted in from outside a row add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_upd_u32<kDppRowShr1, 0xF>(0u, v);
+  v += dpp_upd_u32<kDppRowShr1 + 1, 0xF>(0u, v);
+  v += dpp_upd_u32<kDppRowShr1 + 3, 0xF>(0u, v);
+  v += dpp_upd_u32<kDppRowShr1 + 7, 0xF>(0u, v);
+  v += dpp_upd_u32<kDppRowBcast15, 0xA>(0u, v);
+  v += dpp_upd_u32<kDppRowBcast31, 0xC>(0u, v);
   return v;
 }
 

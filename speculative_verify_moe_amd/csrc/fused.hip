@@ -1,0 +1,684 @@
+// fused.hip -- the whole decode/verify-block MoE layer in one kernel (gfx950).
+//
+// veloGB10 README, "Kernel work": the router fold spread across the GPU, several small
+// kernels (the expert routing among them) folded into their neighbours, grouped expert
+// kernels that never rebuild weights, shared-expert work overlapped with the MoE step.
+// Qwen3.8 Flash-Next . GB10 UltraFast, first bullet: a deterministic floor -- alignment
+// in slot order and a combine without float atomics.
+//
+// One block per CU (8 wavefronts); the grid never exceeds what the device holds resident
+// at once, so every block runs concurrently and the grid-wide barriers complete.  Four
+// phases separated by two barriers:
+//   0  tokens staged in LDS; wavefronts 0..6 of block b own router rows (row n on block
+//      n % NB, wavefront n / NB); wavefront 7 meanwhile loads the shared expert's gate/up
+//      rows it will need first in phase A.                               -- grid sync
+//   1  every block routes all T tokens itself from the logits (top-k per wavefront,
+//      histogram, scans, stable slot lists in LDS): no launch, no second sync.  Block 0
+//      also writes the routing and the padded alignment to global memory.
+//   A  gate/up stream: block b owns gate/up row pair b (2b, 2b+1 and I+2b, I+2b+1) of
+//      every touched expert and of the shared expert; h goes to global memory.
+//                                                                        -- grid sync
+//      Each wavefront then issues its first phase-B weight rows while h is staged.
+//   B  down stream: h staged in LDS, block b owns output rows 8b..8b+7 of every touched
+//      expert and the shared one, y kept in LDS, combine in slot order in fp32.
+// Lane mapping as in gemv.hip: four 16-lane DPP rows per wavefront, one weight row each,
+// 16-byte column groups per lane, one 4-step DPP sum per dot product set.
+//
+// Grid barrier: each block stores this call's token into its own flag word, one
+// wavefront of block 0 polls all flags with one coalesced load per round and then
+// stores the token into a release word that every block polls; spins are bounded, so a
+// misuse can give wrong results but never a hang.  Wavefront 0 does the polling and never
+// has weight prefetches in flight at a barrier: vector loads return in issue order, so a
+// poll queued behind 16 KiB of prefetch would see the flags microseconds late.  Data that crosses a barrier (logits,
+// gate logits, h) is written and read with agent-scope atomic accesses (sc1: coherent
+// across the XCDs' L2s), so the barrier needs no cache write-back or invalidate --
+// every wavefront waits for its own stores to complete before its block arrives.
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+
+#include "device.h"
+#include "internal.h"
+#include "topk.h"
+
+namespace moe {
+
+namespace {
+constexpr int kNW = 8;
+constexpr int kNT = kNW * kWave;
+constexpr int kOct = 8;  // output rows per block in phase B
+// Widths (elements) the lanes' column groups span: H <= kXW, I and I_s <= kHW.  The LDS
+// rows of the tokens and of h end in two zero uint4; a lane's column index beyond the row
+// is clamped onto them (its weights are zero too), so the dot-product loops have no
+// bounds tests and no branch.
+constexpr int kXW = 2048;
+constexpr int kHW = 512;
+}  // namespace
+
+__host__ __device__ __forceinline__ size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+constexpr unsigned kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ unsigned ld_agent(const unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wavefront's stores have completed (vmcnt counts loads and stores in
+// issue order, so this also waits for earlier loads); the clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// flags[kMaxBlocks]: per-block arrival words, then the release word and a timeout count.
+// Every wavefront that wrote data the other blocks will read calls wait_stores() first.
+__device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
+  const unsigned nb = gridDim.x;
+  unsigned *rel = flags + kMaxBlocks;
+  __syncthreads();
+  if (threadIdx.x == 0) st_agent(&flags[blockIdx.x], token);
+  if (blockIdx.x == 0 && threadIdx.x < kWave) {
+    unsigned spins = 0;
+    while (true) {
+      // every flag of a round loaded at once (no short-circuit chain of loads)
+      constexpr int kPer = kMaxBlocks / kWave;
+      unsigned v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const unsigned i = threadIdx.x + kWave * j;
+        if (kWave * j < nb) v[j] = ld_agent(&flags[i < nb ? i : nb - 1]);
+      }
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (kWave * j < nb) ok &= v[j] == token;
+      if (__all(ok)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        if (threadIdx.x == 0) atomicAdd(rel + 1, 1u);
+        break;
+      }
+    }
+    if (threadIdx.x == 0) st_agent(rel, token);
+  }
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (ld_agent(rel) != token) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        atomicAdd(rel + 1, 1u);
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  __syncthreads();
+}
+
+template <int ESZ, int CGU, int CGD, int CR>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void moe_decode_fused_kernel(FusedArgs a) {
+  static_assert(16 * CGU * (16 / ESZ) == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
+  static_assert(16 * CGD * (16 / ESZ) == kHW, "lanes must span an h row");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int VPG = 16 / ESZ;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
+  const int NB = gridDim.x;
+  const int T = a.T, H = a.H, E = a.E, k = a.k;
+  const int n_slots = T * k;
+  const int G8 = H / 8;
+  const int xg = G8 + 2;                                                // uint4 per LDS token row
+  const int hg = ((a.has_shared && a.I_s > a.I) ? a.I_s : a.I) / 8 + 2;  // uint4 per LDS h row
+
+  // ---------------- LDS: routing region, then the data region (x, later h and y)
+  int *s_ids = reinterpret_cast<int *>(smem);         // [T*k]
+  float *s_topw = reinterpret_cast<float *>(s_ids + n_slots);
+  int *s_slots = reinterpret_cast<int *>(s_topw + n_slots);      // [T*k] grouped by expert
+  int *s_stok = s_slots + n_slots;                                // [T*k] their tokens
+  float *s_gamma = reinterpret_cast<float *>(s_stok + n_slots);   // [64]
+  int *s_cnt = reinterpret_cast<int *>(s_gamma + kDecodeMaxT);    // [E]
+  int *s_cs = s_cnt + E;                                          // [E+1]
+  int *s_fl = s_cs + E + 1;                                       // [E+1]
+  int *s_e = s_fl + E + 1;                                        // [E]
+  int *s_start = s_e + E;                                         // [E+1]
+  int *s_off = s_start + E + 1;                                   // [E+1] padded offsets
+  unsigned *s_mlo = reinterpret_cast<unsigned *>(s_off + E + 1);  // [E] tokens 0..31 per expert
+  unsigned *s_mhi = s_mlo + E;                                    // [E] tokens 32..63
+  __shared__ int s_nt;
+  __shared__ uint32_t s_wsum[2 * kNW];
+  char *data = smem + a.lds_route;
+
+  // ---------------- phase 0: router rows, shared-expert prefetch, tokens to LDS
+  const int NR = E + (a.w_sg != nullptr ? 1 : 0);
+  constexpr int kPrefetchWave = kNW - 1;
+  const int my_row = wave < kPrefetchWave ? wave * NB + blockIdx.x : -1;  // rows beyond NB*(kNW-1): more passes
+  float4 wr[CR];
+  auto load_router_row = [&](int n) {
+    const float4 *row = reinterpret_cast<const float4 *>(n < E ? a.w_r + (size_t)n * H : a.w_sg);
+#pragma unroll
+    for (int c = 0; c < CR; ++c) {
+      const int g = lane + kWave * c;
+      if (g < H / 4) {
+        const uint4 u = ld_stream(reinterpret_cast<const uint4 *>(row + g));
+        wr[c] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+      } else {
+        wr[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  if (my_row >= 0 && my_row < NR) load_router_row(my_row);
+
+  // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
+  const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
+  uint4 wa[CGU], wb[CGU];
+  auto gu_row = [&](bool shared, int e, int p) -> const uint4 * {
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_gu : (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
+    const int Iw = shared ? a.I_s : a.I;
+    const int row = rg < 2 ? 2 * p + rg : Iw + 2 * p + (rg - 2);
+    return reinterpret_cast<const uint4 *>(bank + (size_t)row * H * ESZ);
+  };
+  auto gu_load = [&](uint4(&w)[CGU], bool shared, int e, int p) {
+    const uint4 *ptr = gu_row(shared, e, p);
+    const int G = H / VPG;
+#pragma unroll
+    for (int c = 0; c < CGU; ++c) {
+      const int g = l16 + 16 * c;
+      w[c] = g < G ? ld_stream(ptr + g) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  const bool first_pair_shared = a.has_shared && 2 * (int)blockIdx.x < a.I_s;
+
+  // tokens to LDS by wavefronts 0..6 (the prefetch wavefront's loads stay in flight), in
+  // rows of xg uint4 ending in the zero pad; unguarded (clamped) loads, so they overlap
+  uint4 *sx = reinterpret_cast<uint4 *>(data);
+  if (wave < kPrefetchWave) {
+    constexpr int kStep = kPrefetchWave * kWave, kB = 8;
+    const uint4 *gx = reinterpret_cast<const uint4 *>(a.x);
+    const int n16 = T * xg, last = T * G8 - 1;
+    for (int base = tid; base < n16; base += kB * kStep) {
+      uint4 v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = base + j * kStep, t = i / xg, g = i - t * xg;
+        v[j] = gx[min(t * G8 + g, last)];
+        if (g >= G8) v[j] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (base + j * kStep < n16) sx[base + j * kStep] = v[j];
+    }
+  }
+  const uint4 *xs = sx;
+  for (int e = tid; e < E; e += kNT) {
+    s_mlo[e] = 0u;
+    s_mhi[e] = 0u;
+  }
+  __syncthreads();
+  if (wave == kPrefetchWave && (int)blockIdx.x < NPair && first_pair_shared) gu_load(wa, true, 0, blockIdx.x);
+
+  auto router_rows = [&](int n) {
+    const float bias = (n < E && a.b_r != nullptr) ? a.b_r[n] : 0.0f;
+    const uint2 *x2 = reinterpret_cast<const uint2 *>(xs);
+    for (int t0 = 0; t0 < T; t0 += 4) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CR; ++c) {
+        const int g = min(lane + kWave * c, H / 4);  // H / 4: the zero pad (zero weights too)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 xv = x2[min(t0 + j, T - 1) * (2 * xg) + g];  // rows past T: not stored
+          float s = acc[j];
+          s = fmaf(wr[c].x, bf16_lo(xv.x), s);
+          s = fmaf(wr[c].y, bf16_hi(xv.x), s);
+          s = fmaf(wr[c].z, bf16_lo(xv.y), s);
+          s = fmaf(wr[c].w, bf16_hi(xv.y), s);
+          acc[j] = s;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (t0 + j < T) {
+          const float v = wave_sum(acc[j]);
+          if (lane == 0) {
+            float *dst = n < E ? a.logits + (size_t)(t0 + j) * E + n : a.gate_logit + t0 + j;
+            __hip_atomic_store(dst, n < E ? v + bias : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+  };
+  if (my_row >= 0 && my_row < NR) router_rows(my_row);
+  // rows beyond the first pass (E + 1 > 7 * NB): strided passes
+  for (int n = my_row + (kNW - 1) * NB; my_row >= 0 && n < NR; n += (kNW - 1) * NB) {
+    load_router_row(n);
+    router_rows(n);
+  }
+  if (wave != kPrefetchWave) wait_stores();  // the router rows' logit stores
+  grid_barrier(a.bar, 2 * a.epoch + 1);
+
+  // ---------------- phase 1: routing in every block
+  {
+    const int epl = (E + kWave - 1) / kWave;
+    // per expert, the set of tokens that chose it (T <= 64: two 32-bit words, cleared in
+    // phase 0); the k experts of one token are distinct, so a slot's rank inside its
+    // expert's group (slot order) is the number of earlier tokens in that set
+    for (int t = wave; t < T; t += kNW) {
+      const float *lg = a.logits + (size_t)t * E;
+      if (epl <= 1) topk_wave<1, true>(lg, E, k, a.renorm, s_ids + t * k, s_topw + t * k, nullptr);
+      else if (epl <= 2) topk_wave<2, true>(lg, E, k, a.renorm, s_ids + t * k, s_topw + t * k, nullptr);
+      else if (epl <= 4) topk_wave<4, true>(lg, E, k, a.renorm, s_ids + t * k, s_topw + t * k, nullptr);
+      else if (epl <= 8) topk_wave<8, true>(lg, E, k, a.renorm, s_ids + t * k, s_topw + t * k, nullptr);
+      else topk_wave<16, true>(lg, E, k, a.renorm, s_ids + t * k, s_topw + t * k, nullptr);
+      if (lane < k) {
+        const int e = s_ids[t * k + lane];
+        atomicOr(t < 32 ? &s_mlo[e] : &s_mhi[e], 1u << (t & 31));
+      }
+    }
+    if (a.has_shared && tid < T) {
+      const float z = __hip_atomic_load(a.gate_logit + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_gamma[tid] = 1.0f / (1.0f + expf(-z));
+    }
+    __syncthreads();
+    // block scan over the experts (thread tid owns experts per*tid .. per*tid+per-1) of two
+    // packed words: touched flag | slot count << 16, and the padded slot count
+    const int BM = a.BM;
+    {
+      const int per = (E + kNT - 1) / kNT;  // 1 or 2
+      const int e0 = tid * per;
+      auto word_a = [](int c) -> uint32_t { return (c > 0 ? 1u : 0u) | ((uint32_t)c << 16); };
+      auto word_b = [&](int c) -> uint32_t { return (uint32_t)((c + BM - 1) / BM * BM); };
+      uint32_t va = 0, vb = 0;
+      for (int u = 0; u < per; ++u) {
+        const int e = e0 + u;
+        if (e < E) {
+          const int c = __popc(s_mlo[e]) + __popc(s_mhi[e]);
+          s_cnt[e] = c;
+          va += word_a(c);
+          vb += word_b(c);
+        }
+      }
+      const uint32_t ia = wave_incl_scan_u32(va), ib = wave_incl_scan_u32(vb);
+      if (lane == kWave - 1) {
+        s_wsum[2 * wave] = ia;
+        s_wsum[2 * wave + 1] = ib;
+      }
+      __syncthreads();
+      uint32_t ra = ia - va, rb = ib - vb;
+      for (int w = 0; w < wave; ++w) {
+        ra += s_wsum[2 * w];
+        rb += s_wsum[2 * w + 1];
+      }
+      for (int u = 0; u < per; ++u) {
+        const int e = e0 + u;
+        if (e < E) {
+          s_fl[e] = (int)(ra & 0xFFFFu);
+          s_cs[e] = (int)(ra >> 16);
+          s_off[e] = (int)rb;
+          ra += word_a(s_cnt[e]);
+          rb += word_b(s_cnt[e]);
+        }
+      }
+      if (tid == kNT - 1) {
+        s_fl[E] = (int)(ra & 0xFFFFu);
+        s_cs[E] = (int)(ra >> 16);
+        s_off[E] = (int)rb;
+      }
+    }
+    __syncthreads();
+    const int nt = s_fl[E];
+    for (int e = tid; e < E; e += kNT) {
+      if (s_cnt[e] > 0) {
+        s_e[s_fl[e]] = e;
+        s_start[s_fl[e]] = s_cs[e];
+      }
+    }
+    if (tid == 0) {
+      s_start[nt] = n_slots;
+      s_nt = nt;
+    }
+    for (int i = tid; i < n_slots; i += kNT) {
+      const int t = i / k, e = s_ids[i];
+      const unsigned lo = s_mlo[e], hi = s_mhi[e];
+      const int r = t < 32 ? __popc(lo & ((1u << t) - 1u)) : __popc(lo) + __popc(hi & ((1u << (t - 32)) - 1u));
+      s_slots[s_cs[e] + r] = i;
+      s_stok[s_cs[e] + r] = t;
+    }
+    __syncthreads();
+    // the routing and the padded alignment for the caller, spread over the blocks: any
+    // position p of the padded list follows from the padded scan and the slot lists
+    {
+      const int NBk = gridDim.x, b = blockIdx.x;
+      for (int i = b * kNT + tid; i < n_slots; i += NBk * kNT) {
+        a.ids[i] = s_ids[i];
+        a.topw[i] = s_topw[i];
+      }
+      if (a.has_shared && b == NBk - 1 && tid < T) a.gamma[tid] = s_gamma[tid];
+      const int total = s_off[E];
+      for (int e = b * kNT + tid; e <= E; e += NBk * kNT) {
+        if (e < E) a.al.counts[e] = s_cnt[e];
+        a.al.offsets[e] = s_off[e];
+      }
+      if (b == 0 && tid == 0) a.al.num_padded[0] = total;
+      for (int p = b * kNT + tid; p < a.cap; p += NBk * kNT) {
+        int v = n_slots;
+        if (p < total) {
+          const int e = segment_of(s_off, E, p);
+          const int r = p - s_off[e];
+          if (r < s_cnt[e]) v = s_slots[s_cs[e] + r];
+        }
+        a.al.sorted[p] = v;
+      }
+      for (int bb = b * kNT + tid; bb < a.cap / BM; bb += NBk * kNT) {
+        const int p = bb * BM;
+        a.al.block_expert[bb] = p < total ? segment_of(s_off, E, p) : -1;
+      }
+    }
+  }
+  const int nr = s_nt;
+
+  // ---------------- phase A: gate/up for row pairs p = b, b + NB, ...
+  for (int p = blockIdx.x; p < NPair; p += NB) {
+    const bool sh = a.has_shared && 2 * p < a.I_s;
+    const bool rt = 2 * p < a.I;
+    const int n_r = rt ? nr : 0;
+    const int NE = n_r + (sh ? 1 : 0);
+    // entry q: q == 0 is the shared expert when sh, then routed experts in ascending order
+    auto ent_shared = [&](int q) { return sh && q == 0; };
+    auto ent_index = [&](int q) { return q - (sh ? 1 : 0); };
+    auto compute = [&](const uint4(&w)[CGU], int q) {
+      const bool shared = ent_shared(q);
+      const int ri = ent_index(q);
+      const int e = shared ? 0 : s_e[ri];
+      const int q0 = shared ? 0 : s_start[ri];
+      const int q1 = shared ? T : s_start[ri + 1];
+      float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
+      if (ESZ == 1) {
+        const float *sc = shared ? a.ss_gu : a.s_gu + (size_t)e * 2 * a.I;
+        const int Iw = shared ? a.I_s : a.I;
+        sg0 = sc[2 * p];
+        sg1 = sc[2 * p + 1];
+        su0 = sc[Iw + 2 * p];
+        su1 = sc[Iw + 2 * p + 1];
+      }
+      for (int qq = q0; qq < q1; ++qq) {
+        const int slot = shared ? qq : s_slots[qq];
+        const int t = shared ? qq : s_stok[qq];
+        const uint4 *xr = xs + (size_t)t * xg;
+        float acc = 0.0f;
+        // the token's LDS reads are issued in groups of 4 ahead of their use (one
+        // accumulation chain, same order as the lane loop)
+        uint4 xv[CGU * (3 - ESZ)];
+#pragma unroll
+        for (int c = 0; c < CGU; ++c) {
+          if (c % 4 == 0) {
+#pragma unroll
+            for (int u = c; u < c + 4 && u < CGU; ++u) {
+              const int gu = min(l16 + 16 * u, H / VPG);  // H / VPG: the zero pad
+              if (ESZ == 2) {
+                xv[u] = xr[gu];
+              } else {
+                xv[2 * u] = xr[2 * gu];
+                xv[2 * u + 1] = xr[2 * gu + 1];
+              }
+            }
+          }
+          if (ESZ == 2) {
+            acc = dot8_bf16(w[c], xv[c], acc);
+          } else {
+            const uint4 x0 = xv[2 * c], x1 = xv[2 * c + 1];
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].x), x0.x, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].x), x0.y, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].y), x0.z, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].y), x0.w, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].z), x1.x, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].z), x1.y, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].w), x1.z, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].w), x1.w, acc);
+          }
+        }
+        acc = row16_sum(acc);
+        const float g0 = lane_value(acc, 0) * sg0, g1 = lane_value(acc, 16) * sg1;
+        const float u0 = lane_value(acc, 32) * su0, u1 = lane_value(acc, 48) * su1;
+        if (lane == 0) {
+          uint16_t *dst = shared ? a.h_s + (size_t)t * a.I_s + 2 * p : a.h + (size_t)slot * a.I + 2 * p;
+          __hip_atomic_store(reinterpret_cast<uint32_t *>(dst),
+                             pack_bf16x2(g0 / (1.0f + expf(-g0)) * u0, g1 / (1.0f + expf(-g1)) * u1),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    };
+    auto load = [&](uint4(&w)[CGU], int q) {
+      const bool shared = ent_shared(q);
+      gu_load(w, shared, shared ? 0 : s_e[ent_index(q)], p);
+    };
+    int q = (wave + 1) % kNW;  // the prefetch wavefront takes entry 0 (the shared expert)
+    const bool preloaded = (p == (int)blockIdx.x) && wave == kPrefetchWave && first_pair_shared;
+    if (q < NE && !preloaded) load(wa, q);
+    while (q < NE) {
+      const int q2 = q + kNW;
+      if (q2 < NE) load(wb, q2);
+      compute(wa, q);
+      if (q2 >= NE) break;
+      const int q3 = q2 + kNW;
+      if (q3 < NE) load(wa, q3);
+      compute(wb, q2);
+      q = q3;
+    }
+  }
+
+  // ---------------- phase B: the second grid barrier, then the first rows' loads
+  const int NOct = H / kOct;
+  const int NEB = nr + (a.has_shared ? 1 : 0);
+  uint4 da[2][CGD], db[2][CGD];
+  auto dn_load = [&](uint4(&w)[2][CGD], int q, int o) {
+    const bool shared = a.has_shared && q == 0;
+    const int ri = q - (a.has_shared ? 1 : 0);
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + (size_t)s_e[ri] * H * a.I * ESZ;
+    const int K = shared ? a.I_s : a.I;
+    const int G = K / VPG;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 *ptr = reinterpret_cast<const uint4 *>(bank + (size_t)(kOct * o + 4 * s + rg) * K * ESZ);
+#pragma unroll
+      for (int c = 0; c < CGD; ++c) {
+        const int g = l16 + 16 * c;
+        w[s][c] = g < G ? ld_stream(ptr + g) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  wait_stores();  // this wavefront's h stores
+  grid_barrier(a.bar, 2 * a.epoch + 2);
+  // first phase-B rows in flight while h is staged
+  if ((int)blockIdx.x < NOct && wave < NEB) dn_load(da, wave, blockIdx.x);
+
+  // ---------------- phase B: down + combine for octets o = b, b + NB, ...
+  float *s_y = reinterpret_cast<float *>(data);               // [T*k][8]
+  float *s_ys = s_y + (size_t)n_slots * kOct;                  // [T][8]
+  // h crosses the barrier: 16-byte loads with the sc1 cache policy (coherent across the
+  // XCDs' L2s) into LDS rows of hg uint4 ending in the zero pad: rows 0..T*k-1 are the
+  // slots, then (with a shared expert) one row per token
+  uint4 *hl = reinterpret_cast<uint4 *>(data + al16((size_t)(n_slots + T) * kOct * 4));
+  {
+    typedef int i4_t __attribute__((ext_vector_type(4)));
+    constexpr int kSc1 = 16;  // cache-policy bit sc1
+    const int gr = a.I / 8, gs = a.I_s / 8;
+    const int nrows = n_slots + (a.has_shared ? T : 0);
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, n_slots * gr * 16, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(a.has_shared ? a.h_s : a.h, 0, (a.has_shared ? T * gs : 0) * 16, 0x00020000);
+    constexpr int kBatch = 8;
+    const int n16 = nrows * hg;
+    for (int base = tid; base < n16; base += kBatch * kNT) {
+      i4_t v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * kNT, r = i / hg, g = i - r * hg;
+        const bool sh = r >= n_slots;
+        const bool ok = i < n16 && g < (sh ? gs : gr);
+        const int off = ok ? (sh ? (r - n_slots) * gs + g : r * gr + g) * 16 : 0;
+        if (sh) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1);
+        else v[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, kSc1);
+        if (!ok) v[j] = i4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * kNT;
+        if (i < n16) hl[i] = make_uint4(v[j].x, v[j].y, v[j].z, v[j].w);
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = blockIdx.x; o < NOct; o += NB) {
+    auto compute = [&](const uint4(&w)[2][CGD], int q) {
+      const bool shared = a.has_shared && q == 0;
+      const int ri = q - (a.has_shared ? 1 : 0);
+      const int e = shared ? 0 : s_e[ri];
+      const int q0 = shared ? 0 : s_start[ri];
+      const int q1 = shared ? T : s_start[ri + 1];
+      const int Kv = (shared ? a.I_s : a.I) / VPG;
+      float sc0 = 1.f, sc1 = 1.f;
+      if (ESZ == 1) {
+        const float *sc = shared ? a.ss_d : a.s_d + (size_t)e * H;
+        sc0 = sc[kOct * o + rg];
+        sc1 = sc[kOct * o + 4 + rg];
+      }
+      for (int qq = q0; qq < q1; ++qq) {
+        const int slot = shared ? qq : s_slots[qq];
+        const uint4 *hr = hl + (size_t)(shared ? n_slots + qq : slot) * hg;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < CGD; ++c) {
+          const int g = min(l16 + 16 * c, Kv);  // Kv: the zero pad (zero weights too)
+          if (ESZ == 2) {
+            const uint4 hv = hr[g];
+            acc0 = dot8_bf16(w[0][c], hv, acc0);
+            acc1 = dot8_bf16(w[1][c], hv, acc1);
+          } else {
+            const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              float acc = s == 0 ? acc0 : acc1;
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].x), h0.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].x), h0.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].y), h0.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].y), h0.w, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].z), h1.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].z), h1.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].w), h1.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].w), h1.w, acc);
+              if (s == 0) acc0 = acc;
+              else acc1 = acc;
+            }
+          }
+        }
+        acc0 = row16_sum(acc0);
+        acc1 = row16_sum(acc1);
+        if (l16 == 0) {
+          float *dst = shared ? s_ys + (size_t)qq * kOct : s_y + (size_t)slot * kOct;
+          dst[rg] = round_bf16(acc0 * sc0);
+          dst[4 + rg] = round_bf16(acc1 * sc1);
+        }
+      }
+    };
+    int q = wave;
+    if (q < NEB && o != (int)blockIdx.x) dn_load(da, q, o);
+    while (q < NEB) {
+      const int q2 = q + kNW;
+      if (q2 < NEB) dn_load(db, q2, o);
+      compute(da, q);
+      if (q2 >= NEB) break;
+      const int q3 = q2 + kNW;
+      if (q3 < NEB) dn_load(da, q3, o);
+      compute(db, q2);
+      q = q3;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < T * kOct; idx += kNT) {
+      const int t = idx / kOct, rr = idx % kOct;
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) acc = fmaf(s_topw[t * k + j], s_y[(size_t)(t * k + j) * kOct + rr], acc);
+      if (a.has_shared) acc = fmaf(s_gamma[t], s_ys[t * kOct + rr], acc);
+      a.out[(size_t)t * H + kOct * o + rr] = to_bf16(acc);
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================ host side
+namespace {
+constexpr size_t kFusedLdsMax = 156 * 1024;
+
+size_t route_bytes(int T, int k, int E) {
+  const size_t n = (size_t)T * k;
+  return al16((4 * n + kDecodeMaxT + 8 * (size_t)E + 4) * 4);
+}
+}  // namespace
+
+size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared, int *xlds, int *hlds) {
+  const size_t rb = route_bytes(T, k, E);
+  const size_t n = (size_t)T * k;
+  const size_t xb = (size_t)T * (H / 8 + 2) * 16;
+  const size_t yb = al16((n + T) * kOct * 4);
+  const size_t hb = (n + (has_shared ? (size_t)T : 0)) * ((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16;
+  *xlds = rb + xb <= kFusedLdsMax;
+  *hlds = rb + yb + hb <= kFusedLdsMax;
+  return rb + std::max(xb, yb + hb);
+}
+
+// The fused kernel's register tiles hold H <= 2048 and I, I_s <= 512; the tokens and h
+// must fit in LDS (T rows of H + 16 elements, and T * k (+ T) rows of max(I, I_s) + 16).
+bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype) {
+  (void)wtype;
+  if (T < 1 || T > kDecodeMaxT || T * k > kSmallSlots || E > kMaxExperts) return false;
+  if (H > kXW || I > kHW || I_s > kHW) return false;
+  int xlds, hlds;
+  fused_lds_bytes(T, H, E, k, I, I_s, I_s > 0, &xlds, &hlds);
+  return xlds && hlds;
+}
+
+namespace {
+std::atomic<unsigned> g_epoch{1};
+}
+
+template <int ESZ, int CGU, int CGD, int CR>
+static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *nb_out) {
+  auto kern = moe_decode_fused_kernel<ESZ, CGU, CGD, CR>;
+  static size_t allowed = 64 * 1024;
+  if (lds > allowed) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), kNT, lds);
+  if (e != hipSuccess) return e;
+  // one block per CU; the whole grid must be resident at once for the barriers
+  const int nb = std::min(cus, kMaxBlocks);
+  if (per_cu < 1 || (long)per_cu * cus < nb) return hipErrorInvalidConfiguration;
+  *nb_out = nb;
+  a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3FFFFFFFu;  // tokens 2e+1, 2e+2: never 0
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(kNT), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {
+  int xlds = 0, hlds = 0;
+  const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared, &xlds, &hlds);
+  if (!xlds || !hlds) return hipErrorInvalidValue;
+  a.xlds = 1;
+  a.lds_route = route_bytes(a.T, a.k, a.E);
+  int nb = 0;
+  hipError_t e;
+  if (a.wtype == 0) e = launch_fused_t<2, 16, 4, 8>(a, lds, s, &nb);
+  else e = launch_fused_t<1, 8, 2, 8>(a, lds, s, &nb);
+  if (desc) snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu", a.wtype == 0 ? "bf16" : "fp8", nb, kNT, lds);
+  return e;
+}
+
+}  // namespace moe

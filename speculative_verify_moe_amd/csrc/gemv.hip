@@ -4,23 +4,28 @@
 // weights; the shared expert overlapped with the MoE step.  Qwen3.8 Flash-Next .
 // GB10 UltraFast, first bullet: a combine without a float-atomicAdd epilogue.
 //
-// At these token counts every touched expert sees 1..T tokens, so the work is a
-// weight stream: ~4 MiB (bf16) of gate/up rows and ~2 MiB of down rows per touched
-// expert, each read exactly once from HBM, with a handful of dot products per weight
-// row.  Both kernels are "row owners": a block owns a fixed slice of output rows and
-// walks every touched expert (plus the shared expert) for that slice, so every block
-// streams the same number of bytes whatever the routing, and the grid does not depend
-// on the routing.  Inside a block, wavefront w takes entries w, w+NW, ... of the
-// touched list; the next entry's weight rows are loaded while the current one is
-// reduced.  A lane owns 16-byte column groups g = lane + 64*c of a row, so each
-// wavefront-wide load is a contiguous 1 KiB of one weight row.
+// At these token counts every touched expert sees 1..T tokens, so the work is a weight
+// stream: ~4 MiB (bf16) of gate/up rows and ~2 MiB of down rows per touched expert,
+// each read exactly once from HBM, with a few dot products per row.  Both kernels are
+// "row owners": a block owns a fixed slice of output rows and walks every touched
+// expert (plus the shared expert) for that slice, so every block streams the same bytes
+// whatever the routing and the grid does not depend on the routing.
 //
-//   gate/up: block b owns gate rows [b*RT, b*RT+RT) and the matching up rows
-//            (I + the same); h[slot][r] = bf16(silu(g) * u).
-//   down:    block b owns output rows [b*RO, b*RO+RO); y = bf16(h . W_d[row]) for
-//            every slot of every touched expert into LDS, then the block combines
-//            out[t][row] = bf16(sum_j w[t][j] * y[t*k+j][row] + gamma_t * y_s[t][row])
-//            in slot order.  No float atomics; each output is written once.
+// Lane mapping: a wavefront is four 16-lane rows; DPP row r of the wavefront holds one
+// weight row, each lane 16-byte column groups g = lane%16 + 16c, so one load
+// instruction fetches 256 contiguous bytes from each of four weight rows and the four
+// dot products finish with one 4-step DPP sum inside the rows.  Wavefront w of a block
+// takes entries w, w+NW, ... of the touched list; the next entry's rows are in flight
+// (non-temporal loads) while the current entry is reduced.  Tokens (gate/up) and the
+// intermediate h (down) are staged in LDS once per block, so the loop reads only LDS
+// and registers besides the weight stream.
+//
+//   gate/up: block b owns gate rows 2b, 2b+1 and the matching up rows I+2b, I+2b+1
+//            (DPP rows 0..3); h[slot][r] = bf16(silu(g) * u).
+//   down:    block b owns output rows 8b..8b+7 (DPP rows 0..3 hold 8b+r and 8b+4+r);
+//            y = bf16(h . W_d[row]) for every slot of every touched expert goes to LDS,
+//            then the block combines out[t][row] = bf16(sum_j w[t][j] * y[t*k+j][row]
+//            + gamma_t * y_s[t][row]) in slot order.  No float atomics.
 #include <cstdio>
 
 #include "device.h"
@@ -28,439 +33,377 @@
 
 namespace moe {
 
-// Touched experts (counts > 0) in ascending order, computed by wavefront 0.
-__device__ __forceinline__ void touched_list(const int32_t *__restrict__ counts, int E, int32_t *s_e, int *s_n) {
-  if (wave_id() != 0) return;
-  const int lane = lane_id();
-  int n = 0;
-  for (int base = 0; base < E; base += kWave) {
-    const int e = base + lane;
-    const int c = e < E ? counts[e] : 0;
-    const uint64_t m = __ballot(c > 0);
-    if (c > 0) s_e[n + __popcll(m & ((1ull << lane) - 1ull))] = e;
-    n += __popcll(m);
-  }
-  if (lane == 0) *s_n = n;
-}
+namespace {
+constexpr int kGuNW = 8;      // wavefronts per gate/up block
+constexpr int kDnNW = 8;      // wavefronts per down block
+constexpr int kDnRows = 8;    // output rows per down block
+constexpr size_t kLdsMax = 150 * 1024;
+}  // namespace
 
-struct Entry {
-  const uint8_t *w;   // this expert's weight bank (bytes)
-  const float *scale; // fp8 row scales of the bank, or nullptr
-  int rows_half;      // I of the bank (gate/up) or its contraction length (down)
-  int off, cnt;       // slot list [off, off + cnt) of sorted (routed) / tokens 0..cnt-1 (shared)
-  bool routed;
+__device__ __forceinline__ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// LDS image of the touched list: e[nr], start[nr+1], slots[T*k]
+struct ListLds {
+  const int32_t *e;
+  const int32_t *start;
+  const int32_t *slots;
 };
 
-__device__ __forceinline__ Entry gate_up_entry(const GemvArgs &a, const int32_t *s_e, int nr, int ent, int esz) {
-  Entry en;
-  if (ent < nr) {
-    const int e = s_e[ent];
-    en.w = (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * a.H * esz;
-    en.scale = a.s_gu != nullptr ? a.s_gu + (size_t)e * 2 * a.I : nullptr;
-    en.rows_half = a.I;
-    en.off = a.offsets[e];
-    en.cnt = a.counts[e];
-    en.routed = true;
+__device__ __forceinline__ ListLds stage_list(const GemvArgs &a, int nr, int32_t *base, int nthreads) {
+  int32_t *e = base, *start = base + nr, *slots = base + 2 * nr + 1;
+  const int n_slots = a.T * a.k;
+  for (int i = threadIdx.x; i < nr; i += nthreads) e[i] = a.tl_e[i];
+  for (int i = threadIdx.x; i <= nr; i += nthreads) start[i] = a.tl_start[i];
+  for (int i = threadIdx.x; i < n_slots; i += nthreads) slots[i] = a.tl_slots[i];
+  return ListLds{e, start, slots};
+}
+
+__device__ __forceinline__ void copy_to_lds(uint4 *dst, const uint4 *src, int n, int nthreads) {
+  for (int i = threadIdx.x; i < n; i += nthreads) dst[i] = src[i];
+}
+
+// ============================================================ gate/up
+// ESZ: bytes per weight (2 bf16, 1 fp8 codes).  CG: 16-byte groups per lane per row.
+template <int ESZ, int CG, bool XLDS>
+__global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NT = kGuNW * kWave;
+  constexpr int VPG = 16 / ESZ;  // weights per 16-byte group
+  const int lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
+  const int r0 = blockIdx.x * 2;
+  const bool do_routed = r0 < a.I;
+  const bool do_shared = a.has_shared != 0 && r0 < a.I_s;
+  const int nr = do_routed ? a.tl_n[0] : 0;
+  const int NE = nr + (do_shared ? 1 : 0);
+  const int H = a.H;
+  const int G = H / VPG;       // groups per weight row
+  const int G8 = H / 8;        // 16-byte groups per token row
+
+  // weight row of this lane for entry `ent` (expert id known)
+  auto row_of = [&](int ent, int e) -> const uint4 * {
+    const uint8_t *bank;
+    int Iw;
+    if (ent < nr) {
+      bank = (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
+      Iw = a.I;
+    } else {
+      bank = (const uint8_t *)a.ws_gu;
+      Iw = a.I_s;
+    }
+    const int row = rg < 2 ? r0 + rg : Iw + r0 + (rg - 2);
+    return reinterpret_cast<const uint4 *>(bank + (size_t)row * H * ESZ);
+  };
+  uint4 wa[CG], wb[CG];
+  auto load = [&](uint4(&w)[CG], int ent, int e) {
+    const uint4 *p = row_of(ent, e);
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int g = l16 + 16 * c;
+      w[c] = g < G ? ld_stream(p + g) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // first entry's rows go out before the staging below
+  int ent = wave;
+  if (ent < NE) load(wa, ent, ent < nr ? a.tl_e[ent] : 0);
+
+  int32_t *lbase = reinterpret_cast<int32_t *>(smem);
+  const ListLds lst = stage_list(a, nr, lbase, NT);
+  const uint4 *xs;
+  if (XLDS) {
+    uint4 *s_x = reinterpret_cast<uint4 *>(smem + align16((size_t)(2 * nr + 1 + a.T * a.k) * 4));
+    copy_to_lds(s_x, reinterpret_cast<const uint4 *>(a.x), a.T * G8, NT);
+    xs = s_x;
   } else {
-    en.w = (const uint8_t *)a.ws_gu;
-    en.scale = a.ss_gu;
-    en.rows_half = a.I_s;
-    en.off = 0;
-    en.cnt = a.T;
-    en.routed = false;
-  }
-  return en;
-}
-
-// ============================================================ gate/up, bf16 weights
-// RT gate rows per block, NW wavefronts, CH = ceil(H / 512) column groups per lane.
-template <int RT, int NW, int CH, bool XLDS>
-__global__ __launch_bounds__(NW * kWave) void gemv_gate_up_bf16_kernel(GemvArgs a) {
-  extern __shared__ uint4 s_x[];  // x [T][H/8] when XLDS
-  __shared__ int32_t s_e[kMaxExperts];
-  __shared__ int s_n;
-  const int lane = lane_id(), wave = wave_id();
-  const int r0 = blockIdx.x * RT;
-  const bool do_routed = r0 < a.I;
-  const bool do_shared = a.has_shared != 0 && r0 < a.I_s;
-  const int G8 = a.H / 8;
-  if (do_routed) touched_list(a.counts, a.E, s_e, &s_n);
-  else if (threadIdx.x == 0) s_n = 0;
-  if (XLDS) {
-    const uint4 *xs = reinterpret_cast<const uint4 *>(a.x);
-    for (int i = threadIdx.x; i < a.T * G8; i += NW * kWave) s_x[i] = xs[i];
+    xs = reinterpret_cast<const uint4 *>(a.x);
   }
   __syncthreads();
-  const int nr = s_n;
-  const int NE = nr + (do_shared ? 1 : 0);
 
-  uint4 wa[2 * RT][CH], wb[2 * RT][CH];
-  auto load = [&](uint4(&w)[2 * RT][CH], int ent) {
-    const Entry en = gate_up_entry(a, s_e, nr, ent, 2);
-    const uint16_t *base = reinterpret_cast<const uint16_t *>(en.w);
-#pragma unroll
-    for (int rr = 0; rr < RT; ++rr) {
-      const uint4 *g_row = reinterpret_cast<const uint4 *>(base + (size_t)(r0 + rr) * a.H);
-      const uint4 *u_row = reinterpret_cast<const uint4 *>(base + (size_t)(en.rows_half + r0 + rr) * a.H);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int g = lane + kWave * c;
-        if (g < G8) {
-          w[rr][c] = ld_stream(g_row + g);
-          w[RT + rr][c] = ld_stream(u_row + g);
-        } else {
-          w[rr][c] = make_uint4(0, 0, 0, 0);
-          w[RT + rr][c] = make_uint4(0, 0, 0, 0);
-        }
-      }
+  auto compute = [&](const uint4(&w)[CG], int ent) {
+    const bool routed = ent < nr;
+    const int e = routed ? lst.e[ent] : 0;
+    const int q0 = routed ? lst.start[ent] : 0;
+    const int q1 = routed ? lst.start[ent + 1] : a.T;
+    float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
+    if (ESZ == 1) {
+      const float *sc = routed ? a.s_gu + (size_t)e * 2 * a.I : a.ss_gu;
+      const int Iw = routed ? a.I : a.I_s;
+      sg0 = sc[r0];
+      sg1 = sc[r0 + 1];
+      su0 = sc[Iw + r0];
+      su1 = sc[Iw + r0 + 1];
     }
-  };
-  auto compute = [&](const uint4(&w)[2 * RT][CH], int ent) {
-    const Entry en = gate_up_entry(a, s_e, nr, ent, 2);
-    for (int q = 0; q < en.cnt; ++q) {
-      const int slot = en.routed ? a.sorted[en.off + q] : q;
-      const int t = en.routed ? slot / a.k : q;
-      float acc[2 * RT];
+    for (int q = q0; q < q1; ++q) {
+      const int slot = routed ? lst.slots[q] : q;
+      const int t = routed ? slot / a.k : q;
+      const uint4 *xr = xs + (size_t)t * G8;
+      float acc = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 2 * RT; ++r) acc[r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int g = lane + kWave * c;
-        if (g < G8) {
-          const uint4 xv = XLDS ? s_x[t * G8 + g] : reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H)[g];
-#pragma unroll
-          for (int r = 0; r < 2 * RT; ++r) acc[r] = dot8_bf16(w[r][c], xv, acc[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 2 * RT; ++r) acc[r] = wave_sum(acc[r]);
-      if (lane == 0) {
-        uint16_t *dst = en.routed ? a.h + (size_t)slot * a.I + r0 : a.h_s + (size_t)t * a.I_s + r0;
-#pragma unroll
-        for (int rr = 0; rr < RT; ++rr) {
-          const float gg = acc[rr], uu = acc[RT + rr];
-          dst[rr] = to_bf16(gg / (1.0f + expf(-gg)) * uu);
-        }
-      }
-    }
-  };
-
-  int ent = wave;
-  if (ent < NE) load(wa, ent);
-  while (ent < NE) {
-    const int e2 = ent + NW;
-    if (e2 < NE) load(wb, e2);
-    compute(wa, ent);
-    if (e2 >= NE) break;
-    const int e3 = e2 + NW;
-    if (e3 < NE) load(wa, e3);
-    compute(wb, e2);
-    ent = e3;
-  }
-}
-
-// ============================================================ gate/up, fp8 weights
-// Lane column group g covers 16 codes (16 columns); CH = ceil(H / 1024).
-template <int RT, int NW, int CH, bool XLDS>
-__global__ __launch_bounds__(NW * kWave) void gemv_gate_up_fp8_kernel(GemvArgs a) {
-  extern __shared__ uint4 s_x[];
-  __shared__ int32_t s_e[kMaxExperts];
-  __shared__ int s_n;
-  const int lane = lane_id(), wave = wave_id();
-  const int r0 = blockIdx.x * RT;
-  const bool do_routed = r0 < a.I;
-  const bool do_shared = a.has_shared != 0 && r0 < a.I_s;
-  const int G16 = a.H / 16;
-  const int G8 = a.H / 8;
-  if (do_routed) touched_list(a.counts, a.E, s_e, &s_n);
-  else if (threadIdx.x == 0) s_n = 0;
-  if (XLDS) {
-    const uint4 *xs = reinterpret_cast<const uint4 *>(a.x);
-    for (int i = threadIdx.x; i < a.T * G8; i += NW * kWave) s_x[i] = xs[i];
-  }
-  __syncthreads();
-  const int nr = s_n;
-  const int NE = nr + (do_shared ? 1 : 0);
-
-  uint4 wa[2 * RT][CH], wb[2 * RT][CH];
-  auto load = [&](uint4(&w)[2 * RT][CH], int ent) {
-    const Entry en = gate_up_entry(a, s_e, nr, ent, 1);
-#pragma unroll
-    for (int rr = 0; rr < RT; ++rr) {
-      const uint4 *g_row = reinterpret_cast<const uint4 *>(en.w + (size_t)(r0 + rr) * a.H);
-      const uint4 *u_row = reinterpret_cast<const uint4 *>(en.w + (size_t)(en.rows_half + r0 + rr) * a.H);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int g = lane + kWave * c;
-        if (g < G16) {
-          w[rr][c] = ld_stream(g_row + g);
-          w[RT + rr][c] = ld_stream(u_row + g);
-        } else {
-          w[rr][c] = make_uint4(0, 0, 0, 0);
-          w[RT + rr][c] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-  auto compute = [&](const uint4(&w)[2 * RT][CH], int ent) {
-    const Entry en = gate_up_entry(a, s_e, nr, ent, 1);
-    // codes -> bf16 pairs once per entry
-    uint32_t wv[2 * RT][CH][8];
-#pragma unroll
-    for (int r = 0; r < 2 * RT; ++r)
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        wv[r][c][0] = fp8x2_to_bf16x2<false>(w[r][c].x);
-        wv[r][c][1] = fp8x2_to_bf16x2<true>(w[r][c].x);
-        wv[r][c][2] = fp8x2_to_bf16x2<false>(w[r][c].y);
-        wv[r][c][3] = fp8x2_to_bf16x2<true>(w[r][c].y);
-        wv[r][c][4] = fp8x2_to_bf16x2<false>(w[r][c].z);
-        wv[r][c][5] = fp8x2_to_bf16x2<true>(w[r][c].z);
-        wv[r][c][6] = fp8x2_to_bf16x2<false>(w[r][c].w);
-        wv[r][c][7] = fp8x2_to_bf16x2<true>(w[r][c].w);
-      }
-    float sg[RT], su[RT];
-#pragma unroll
-    for (int rr = 0; rr < RT; ++rr) {
-      sg[rr] = en.scale[r0 + rr];
-      su[rr] = en.scale[en.rows_half + r0 + rr];
-    }
-    for (int q = 0; q < en.cnt; ++q) {
-      const int slot = en.routed ? a.sorted[en.off + q] : q;
-      const int t = en.routed ? slot / a.k : q;
-      float acc[2 * RT];
-#pragma unroll
-      for (int r = 0; r < 2 * RT; ++r) acc[r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int g = lane + kWave * c;
-        if (g < G16) {
-          uint4 x0, x1;
-          if (XLDS) {
-            x0 = s_x[t * G8 + 2 * g];
-            x1 = s_x[t * G8 + 2 * g + 1];
+      for (int c = 0; c < CG; ++c) {
+        const int g = l16 + 16 * c;
+        if (g < G) {
+          if (ESZ == 2) {
+            acc = dot8_bf16(w[c], xr[g], acc);
           } else {
-            const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H);
-            x0 = xr[2 * g];
-            x1 = xr[2 * g + 1];
-          }
-#pragma unroll
-          for (int r = 0; r < 2 * RT; ++r) {
-            float s = acc[r];
-            s = dot2_bf16(wv[r][c][0], x0.x, s);
-            s = dot2_bf16(wv[r][c][1], x0.y, s);
-            s = dot2_bf16(wv[r][c][2], x0.z, s);
-            s = dot2_bf16(wv[r][c][3], x0.w, s);
-            s = dot2_bf16(wv[r][c][4], x1.x, s);
-            s = dot2_bf16(wv[r][c][5], x1.y, s);
-            s = dot2_bf16(wv[r][c][6], x1.z, s);
-            s = dot2_bf16(wv[r][c][7], x1.w, s);
-            acc[r] = s;
+            const uint4 x0 = xr[2 * g], x1 = xr[2 * g + 1];
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].x), x0.x, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].x), x0.y, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].y), x0.z, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].y), x0.w, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].z), x1.x, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].z), x1.y, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].w), x1.z, acc);
+            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].w), x1.w, acc);
           }
         }
       }
-#pragma unroll
-      for (int r = 0; r < 2 * RT; ++r) acc[r] = wave_sum(acc[r]);
+      acc = row16_sum(acc);
+      const float g0 = lane_value(acc, 0) * sg0, g1 = lane_value(acc, 16) * sg1;
+      const float u0 = lane_value(acc, 32) * su0, u1 = lane_value(acc, 48) * su1;
       if (lane == 0) {
-        uint16_t *dst = en.routed ? a.h + (size_t)slot * a.I + r0 : a.h_s + (size_t)t * a.I_s + r0;
-#pragma unroll
-        for (int rr = 0; rr < RT; ++rr) {
-          const float gg = acc[rr] * sg[rr], uu = acc[RT + rr] * su[rr];
-          dst[rr] = to_bf16(gg / (1.0f + expf(-gg)) * uu);
-        }
+        uint16_t *dst = routed ? a.h + (size_t)slot * a.I + r0 : a.h_s + (size_t)t * a.I_s + r0;
+        *reinterpret_cast<uint32_t *>(dst) =
+            pack_bf16x2(g0 / (1.0f + expf(-g0)) * u0, g1 / (1.0f + expf(-g1)) * u1);
       }
     }
   };
 
-  int ent = wave;
-  if (ent < NE) load(wa, ent);
   while (ent < NE) {
-    const int e2 = ent + NW;
-    if (e2 < NE) load(wb, e2);
+    const int e2 = ent + kGuNW;
+    if (e2 < NE) load(wb, e2, e2 < nr ? lst.e[e2] : 0);
     compute(wa, ent);
     if (e2 >= NE) break;
-    const int e3 = e2 + NW;
-    if (e3 < NE) load(wa, e3);
+    const int e3 = e2 + kGuNW;
+    if (e3 < NE) load(wa, e3, e3 < nr ? lst.e[e3] : 0);
     compute(wb, e2);
     ent = e3;
   }
 }
 
 // ============================================================ down + combine
-// RO output rows per block; a lane's column group covers 8 bf16 of h (bf16 weights)
-// or 16 of them (fp8 weights, ESZ = 1).  CI = groups per lane.
-template <int RO, int NW, int CI, int ESZ>
-__global__ __launch_bounds__(NW * kWave) void gemv_down_kernel(GemvArgs a) {
-  extern __shared__ float s_y[];  // [T*k][RO] then [T][RO] for the shared expert
-  __shared__ int32_t s_e[kMaxExperts];
-  __shared__ int s_n;
-  const int lane = lane_id(), wave = wave_id();
-  const int o0 = blockIdx.x * RO;
-  float *s_ys = s_y + (size_t)a.T * a.k * RO;
-  touched_list(a.counts, a.E, s_e, &s_n);
-  __syncthreads();
-  const int nr = s_n;
+// CG: 16-byte groups per lane per weight row; each lane holds two rows (o0 + rg and
+// o0 + 4 + rg).
+template <int ESZ, int CG, bool HLDS>
+__global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NT = kDnNW * kWave;
+  constexpr int VPG = 16 / ESZ;
+  const int lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
+  const int o0 = blockIdx.x * kDnRows;
+  const int nr = a.tl_n[0];
   const int NE = nr + (a.has_shared ? 1 : 0);
-  constexpr int VPG = ESZ == 2 ? 8 : 16;  // weights per 16-byte group
+  const int n_slots = a.T * a.k;
 
-  auto entry = [&](int ent) {
-    Entry en;
-    if (ent < nr) {
-      const int e = s_e[ent];
-      en.w = (const uint8_t *)a.w_d + (size_t)e * a.H * a.I * ESZ;
-      en.scale = a.s_d != nullptr ? a.s_d + (size_t)e * a.H : nullptr;
-      en.rows_half = a.I;
-      en.off = a.offsets[e];
-      en.cnt = a.counts[e];
-      en.routed = true;
-    } else {
-      en.w = (const uint8_t *)a.ws_d;
-      en.scale = a.ss_d;
-      en.rows_half = a.I_s;
-      en.off = 0;
-      en.cnt = a.T;
-      en.routed = false;
-    }
-    return en;
+  auto rows_of = [&](int ent, int e) -> const uint8_t * {
+    if (ent < nr) return (const uint8_t *)a.w_d + (size_t)e * a.H * a.I * ESZ;
+    return (const uint8_t *)a.ws_d;
   };
-  uint4 wa[RO][CI], wb[RO][CI];
-  auto load = [&](uint4(&w)[RO][CI], int ent) {
-    const Entry en = entry(ent);
-    const int G = en.rows_half / VPG;
+  uint4 wa[2][CG], wb[2][CG];
+  auto load = [&](uint4(&w)[2][CG], int ent, int e) {
+    const uint8_t *bank = rows_of(ent, e);
+    const int K = ent < nr ? a.I : a.I_s;
+    const int G = K / VPG;
 #pragma unroll
-    for (int rr = 0; rr < RO; ++rr) {
-      const uint4 *row = reinterpret_cast<const uint4 *>(en.w + (size_t)(o0 + rr) * en.rows_half * ESZ);
+    for (int s = 0; s < 2; ++s) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(bank + (size_t)(o0 + 4 * s + rg) * K * ESZ);
 #pragma unroll
-      for (int c = 0; c < CI; ++c) {
-        const int g = lane + kWave * c;
-        w[rr][c] = g < G ? ld_stream(row + g) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto compute = [&](const uint4(&w)[RO][CI], int ent) {
-    const Entry en = entry(ent);
-    const int G = en.rows_half / VPG;
-    float sc[RO];
-#pragma unroll
-    for (int rr = 0; rr < RO; ++rr) sc[rr] = en.scale != nullptr ? en.scale[o0 + rr] : 1.0f;
-    for (int q = 0; q < en.cnt; ++q) {
-      const int slot = en.routed ? a.sorted[en.off + q] : q;
-      const uint16_t *hrow = en.routed ? a.h + (size_t)slot * a.I : a.h_s + (size_t)q * a.I_s;
-      float acc[RO];
-#pragma unroll
-      for (int rr = 0; rr < RO; ++rr) acc[rr] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < CI; ++c) {
-        const int g = lane + kWave * c;
-        if (g < G) {
-          if (ESZ == 2) {
-            const uint4 hv = reinterpret_cast<const uint4 *>(hrow)[g];
-#pragma unroll
-            for (int rr = 0; rr < RO; ++rr) acc[rr] = dot8_bf16(w[rr][c], hv, acc[rr]);
-          } else {
-            const uint4 h0 = reinterpret_cast<const uint4 *>(hrow)[2 * g];
-            const uint4 h1 = reinterpret_cast<const uint4 *>(hrow)[2 * g + 1];
-#pragma unroll
-            for (int rr = 0; rr < RO; ++rr) {
-              float s = acc[rr];
-              s = dot2_bf16(fp8x2_to_bf16x2<false>(w[rr][c].x), h0.x, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<true>(w[rr][c].x), h0.y, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<false>(w[rr][c].y), h0.z, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<true>(w[rr][c].y), h0.w, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<false>(w[rr][c].z), h1.x, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<true>(w[rr][c].z), h1.y, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<false>(w[rr][c].w), h1.z, s);
-              s = dot2_bf16(fp8x2_to_bf16x2<true>(w[rr][c].w), h1.w, s);
-              acc[rr] = s;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < RO; ++rr) acc[rr] = wave_sum(acc[rr]);
-      if (lane == 0) {
-        float *dst = en.routed ? s_y + (size_t)slot * RO : s_ys + (size_t)q * RO;
-#pragma unroll
-        for (int rr = 0; rr < RO; ++rr) dst[rr] = round_bf16(acc[rr] * sc[rr]);
+      for (int c = 0; c < CG; ++c) {
+        const int g = l16 + 16 * c;
+        w[s][c] = g < G ? ld_stream(p + g) : make_uint4(0, 0, 0, 0);
       }
     }
   };
 
   int ent = wave;
-  if (ent < NE) load(wa, ent);
+  if (ent < NE) load(wa, ent, ent < nr ? a.tl_e[ent] : 0);
+
+  // LDS: list, y [T*k][8] fp32, y_s [T][8] fp32, then h [T*k][I] and h_s [T][I_s] bf16
+  int32_t *lbase = reinterpret_cast<int32_t *>(smem);
+  const ListLds lst = stage_list(a, nr, lbase, NT);
+  float *s_y = reinterpret_cast<float *>(smem + align16((size_t)(2 * nr + 1 + n_slots) * 4));
+  float *s_ys = s_y + (size_t)n_slots * kDnRows;
+  const uint4 *hs, *hss;
+  if (HLDS) {
+    uint4 *h_l = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(s_ys) +
+                                           align16((size_t)(a.has_shared ? a.T : 0) * kDnRows * 4));
+    copy_to_lds(h_l, reinterpret_cast<const uint4 *>(a.h), n_slots * a.I / 8, NT);
+    uint4 *hs_l = h_l + (size_t)n_slots * a.I / 8;
+    if (a.has_shared) copy_to_lds(hs_l, reinterpret_cast<const uint4 *>(a.h_s), a.T * a.I_s / 8, NT);
+    hs = h_l;
+    hss = hs_l;
+  } else {
+    hs = reinterpret_cast<const uint4 *>(a.h);
+    hss = reinterpret_cast<const uint4 *>(a.h_s);
+  }
+  __syncthreads();
+
+  auto compute = [&](const uint4(&w)[2][CG], int ent) {
+    const bool routed = ent < nr;
+    const int e = routed ? lst.e[ent] : 0;
+    const int K = routed ? a.I : a.I_s;
+    const int G = K / VPG;
+    const int q0 = routed ? lst.start[ent] : 0;
+    const int q1 = routed ? lst.start[ent + 1] : a.T;
+    float sc0 = 1.f, sc1 = 1.f;
+    if (ESZ == 1) {
+      const float *sc = routed ? a.s_d + (size_t)e * a.H : a.ss_d;
+      sc0 = sc[o0 + rg];
+      sc1 = sc[o0 + 4 + rg];
+    }
+    for (int q = q0; q < q1; ++q) {
+      const int slot = routed ? lst.slots[q] : q;
+      const uint4 *hr = routed ? hs + (size_t)slot * (a.I / 8) : hss + (size_t)q * (a.I_s / 8);
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        const int g = l16 + 16 * c;
+        if (g < G) {
+          if (ESZ == 2) {
+            const uint4 hv = hr[g];
+            acc0 = dot8_bf16(w[0][c], hv, acc0);
+            acc1 = dot8_bf16(w[1][c], hv, acc1);
+          } else {
+            const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              float acc = s == 0 ? acc0 : acc1;
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].x), h0.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].x), h0.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].y), h0.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].y), h0.w, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].z), h1.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].z), h1.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].w), h1.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].w), h1.w, acc);
+              if (s == 0) acc0 = acc;
+              else acc1 = acc;
+            }
+          }
+        }
+      }
+      acc0 = row16_sum(acc0);
+      acc1 = row16_sum(acc1);
+      if (l16 == 0) {
+        float *dst = routed ? s_y + (size_t)slot * kDnRows : s_ys + (size_t)q * kDnRows;
+        dst[rg] = round_bf16(acc0 * sc0);
+        dst[4 + rg] = round_bf16(acc1 * sc1);
+      }
+    }
+  };
+
   while (ent < NE) {
-    const int e2 = ent + NW;
-    if (e2 < NE) load(wb, e2);
+    const int e2 = ent + kDnNW;
+    if (e2 < NE) load(wb, e2, e2 < nr ? lst.e[e2] : 0);
     compute(wa, ent);
     if (e2 >= NE) break;
-    const int e3 = e2 + NW;
-    if (e3 < NE) load(wa, e3);
+    const int e3 = e2 + kDnNW;
+    if (e3 < NE) load(wa, e3, e3 < nr ? lst.e[e3] : 0);
     compute(wb, e2);
     ent = e3;
   }
   __syncthreads();
   // combine in slot order, fp32, one write per output element
-  for (int idx = threadIdx.x; idx < a.T * RO; idx += NW * kWave) {
-    const int t = idx / RO, rr = idx % RO;
+  for (int idx = threadIdx.x; idx < a.T * kDnRows; idx += NT) {
+    const int t = idx / kDnRows, rr = idx % kDnRows;
     float acc = 0.0f;
-    for (int j = 0; j < a.k; ++j) acc = fmaf(a.topk_w[t * a.k + j], s_y[(size_t)(t * a.k + j) * RO + rr], acc);
-    if (a.has_shared) acc = fmaf(a.gamma[t], s_ys[t * RO + rr], acc);
+    for (int j = 0; j < a.k; ++j)
+      acc = fmaf(a.topk_w[t * a.k + j], s_y[(size_t)(t * a.k + j) * kDnRows + rr], acc);
+    if (a.has_shared) acc = fmaf(a.gamma[t], s_ys[t * kDnRows + rr], acc);
     a.out[(size_t)t * a.H + o0 + rr] = to_bf16(acc);
   }
 }
 
 // ============================================================ launchers
-namespace {
-constexpr int kGuRT = 2, kGuNW = 4;
-constexpr int kDnRO = 8, kDnNW = 4;
-constexpr size_t kLdsBudget = 60 * 1024;
-}  // namespace
+static size_t list_bytes(const GemvArgs &a) { return (((size_t)(2 * a.E + 1 + a.T * a.k) * 4) + 15) & ~(size_t)15; }
 
-template <int CH, bool XLDS>
-static void launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, size_t lds) {
-  if (a.wtype == 0)
-    hipLaunchKernelGGL((gemv_gate_up_bf16_kernel<kGuRT, kGuNW, CH, XLDS>), grid, dim3(kGuNW * kWave), lds, s, a);
-  else
-    hipLaunchKernelGGL((gemv_gate_up_fp8_kernel<kGuRT, kGuNW, CH, XLDS>), grid, dim3(kGuNW * kWave), lds, s, a);
+// Dynamic LDS above 64 KiB has to be allowed per kernel (gfx950 has 160 KiB per CU);
+// the largest size asked for so far is remembered per kernel instantiation.
+template <typename K>
+static hipError_t set_lds(K kernel, size_t bytes) {
+  static size_t allowed = 64 * 1024;
+  if (bytes <= allowed) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) allowed = bytes;
+  return e;
+}
+
+template <int ESZ, int CG>
+static hipError_t launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, bool xlds, size_t lds) {
+  if (xlds) {
+    auto k = gemv_gate_up_kernel<ESZ, CG, true>;
+    hipError_t e = set_lds(k, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(kGuNW * kWave), lds, s, a);
+  } else {
+    auto k = gemv_gate_up_kernel<ESZ, CG, false>;
+    hipLaunchKernelGGL(k, grid, dim3(kGuNW * kWave), lds, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len) {
-  const int rows = a.I > (a.has_shared ? a.I_s : 0) ? a.I : a.I_s;
-  dim3 grid((rows + kGuRT - 1) / kGuRT);
+  const int rows = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
+  dim3 grid(rows / 2);
+  const size_t lb = list_bytes(a);
   const size_t xbytes = (size_t)a.T * a.H * 2;
-  const bool xlds = xbytes + kMaxExperts * 4 + 64 <= kLdsBudget;
-  const int per_group = a.wtype == 0 ? 512 : 1024;  // columns per lane group sweep
-  const int ch = (a.H + per_group - 1) / per_group;
-  const size_t lds = xlds ? xbytes : 0;
-  if (desc) snprintf(desc, desc_len, "gemv_gate_up_%s<RT=%d,NW=%d,CH=%d,XLDS=%d> grid=%u block=%d", a.wtype == 0 ? "bf16" : "fp8", kGuRT, kGuNW, ch, (int)xlds, grid.x, kGuNW * kWave);
-  if (ch <= 1) { if (xlds) launch_gu<1, true>(a, s, grid, lds); else launch_gu<1, false>(a, s, grid, lds); }
-  else if (ch <= 2) { if (xlds) launch_gu<2, true>(a, s, grid, lds); else launch_gu<2, false>(a, s, grid, lds); }
-  else if (ch <= 4) { if (xlds) launch_gu<4, true>(a, s, grid, lds); else launch_gu<4, false>(a, s, grid, lds); }
-  else if (ch <= 8) { if (xlds) launch_gu<8, true>(a, s, grid, lds); else launch_gu<8, false>(a, s, grid, lds); }
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const bool xlds = lb + xbytes <= kLdsMax;
+  const size_t lds = lb + (xlds ? xbytes : 0);
+  const int esz = a.wtype == 0 ? 2 : 1;
+  const int groups = a.H * esz / 16;          // 16-byte groups per weight row
+  const int cg = (groups + 15) / 16;
+  if (desc) snprintf(desc, desc_len, "gemv_gate_up<esz=%d,CG=%d,XLDS=%d> grid=%u block=%d lds=%zu", esz, cg, (int)xlds, grid.x, kGuNW * kWave, lds);
+  if (esz == 2) {
+    if (cg <= 4) return launch_gu<2, 4>(a, s, grid, xlds, lds);
+    if (cg <= 8) return launch_gu<2, 8>(a, s, grid, xlds, lds);
+    if (cg <= 16) return launch_gu<2, 16>(a, s, grid, xlds, lds);
+    if (cg <= 32) return launch_gu<2, 32>(a, s, grid, xlds, lds);
+  } else {
+    if (cg <= 4) return launch_gu<1, 4>(a, s, grid, xlds, lds);
+    if (cg <= 8) return launch_gu<1, 8>(a, s, grid, xlds, lds);
+    if (cg <= 16) return launch_gu<1, 16>(a, s, grid, xlds, lds);
+  }
+  return hipErrorInvalidValue;
 }
 
-template <int CI>
-static void launch_dn(const GemvArgs &a, hipStream_t s, dim3 grid, size_t lds) {
-  if (a.wtype == 0)
-    hipLaunchKernelGGL((gemv_down_kernel<kDnRO, kDnNW, CI, 2>), grid, dim3(kDnNW * kWave), lds, s, a);
-  else
-    hipLaunchKernelGGL((gemv_down_kernel<kDnRO, kDnNW, CI, 1>), grid, dim3(kDnNW * kWave), lds, s, a);
+template <int ESZ, int CG>
+static hipError_t launch_dn(const GemvArgs &a, hipStream_t s, dim3 grid, bool hlds, size_t lds) {
+  if (hlds) {
+    auto k = gemv_down_kernel<ESZ, CG, true>;
+    hipError_t e = set_lds(k, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(kDnNW * kWave), lds, s, a);
+  } else {
+    auto k = gemv_down_kernel<ESZ, CG, false>;
+    hipError_t e = set_lds(k, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, grid, dim3(kDnNW * kWave), lds, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len) {
-  dim3 grid(a.H / kDnRO);
-  const size_t lds = ((size_t)a.T * a.k + (a.has_shared ? a.T : 0)) * kDnRO * sizeof(float);
-  const int kmax = a.I > (a.has_shared ? a.I_s : 0) ? a.I : a.I_s;
-  const int per_group = a.wtype == 0 ? 512 : 1024;
-  const int ci = (kmax + per_group - 1) / per_group;
-  if (desc) snprintf(desc, desc_len, "gemv_down_combine_%s<RO=%d,NW=%d,CI=%d> grid=%u block=%d", a.wtype == 0 ? "bf16" : "fp8", kDnRO, kDnNW, ci, grid.x, kDnNW * kWave);
-  if (ci <= 1) launch_dn<1>(a, s, grid, lds);
-  else if (ci <= 2) launch_dn<2>(a, s, grid, lds);
-  else if (ci <= 4) launch_dn<4>(a, s, grid, lds);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  dim3 grid(a.H / kDnRows);
+  const size_t n_slots = (size_t)a.T * a.k;
+  const size_t base = list_bytes(a) + (((n_slots * kDnRows * 4) + 15) & ~(size_t)15) +
+                      ((((size_t)(a.has_shared ? a.T : 0) * kDnRows * 4) + 15) & ~(size_t)15);
+  const size_t hbytes = n_slots * a.I * 2 + (a.has_shared ? (size_t)a.T * a.I_s * 2 : 0);
+  const bool hlds = base + hbytes <= kLdsMax;
+  const size_t lds = base + (hlds ? hbytes : 0);
+  const int esz = a.wtype == 0 ? 2 : 1;
+  const int kmax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
+  const int groups = kmax * esz / 16;
+  const int cg = (groups + 15) / 16;
+  if (desc) snprintf(desc, desc_len, "gemv_down_combine<esz=%d,CG=%d,HLDS=%d> grid=%u block=%d lds=%zu", esz, cg, (int)hlds, grid.x, kDnNW * kWave, lds);
+  if (esz == 2) {
+    if (cg <= 2) return launch_dn<2, 2>(a, s, grid, hlds, lds);
+    if (cg <= 4) return launch_dn<2, 4>(a, s, grid, hlds, lds);
+    if (cg <= 8) return launch_dn<2, 8>(a, s, grid, hlds, lds);
+  } else {
+    if (cg <= 2) return launch_dn<1, 2>(a, s, grid, hlds, lds);
+    if (cg <= 4) return launch_dn<1, 4>(a, s, grid, hlds, lds);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -14,6 +14,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 // Slots per block of the multi-block alignment.
 constexpr int kAlignChunk = 256;
+// Blocks of the fused decode kernel at most (one per CU) and its barrier words.
+constexpr int kMaxBlocks = 1024;
+constexpr int kBarrierWords = kMaxBlocks + 64;
 
 struct AlignOut {
   int32_t *sorted;
@@ -23,6 +26,21 @@ struct AlignOut {
   int32_t *num_padded;
 };
 
+// Compact list of the touched experts for the decode kernels (all pointers may be null
+// when not wanted): n[0] experts with at least one slot, their ids ascending in e[],
+// their slots grouped by expert (ascending inside a group) in slots[start[i] ..
+// start[i+1]).  Capacity: e[E], start[E+1], slots[T*k].
+struct Touched {
+  int32_t *n;
+  int32_t *e;
+  int32_t *start;
+  int32_t *slots;
+};
+inline size_t touched_ints(int E, int64_t n_slots) { return (size_t)(1 + E + E + 1 + n_slots); }
+inline Touched touched_at(int32_t *base, int E) {
+  return Touched{base, base + 1, base + 1 + E, base + 2 + 2 * E};
+}
+
 // ---------------------------------------------------------------- route.hip
 hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
                               const float *w_sg, float *logits, float *gate_logit, hipStream_t s);
@@ -30,7 +48,9 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
                        const float *gate_logit, float *gamma, hipStream_t s);
 hipError_t launch_topk_align_small(const float *logits, const float *gate_logit, int T, int E, int k, int renorm,
                                    int BM, int64_t cap, int32_t *ids, float *w, float *gamma, AlignOut al,
-                                   hipStream_t s);
+                                   Touched tl, hipStream_t s);
+hipError_t launch_compact_touched(const int32_t *counts, const int32_t *offsets, const int32_t *sorted, int E,
+                                  Touched tl, hipStream_t s);
 hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s);
 // hist: align_hist_ints(n, E) int32 of scratch.
 size_t align_hist_ints(int64_t n, int E);
@@ -49,9 +69,10 @@ struct GemvArgs {
   const float *s_gu;
   const void *w_d;
   const float *s_d;
-  const int32_t *counts;
-  const int32_t *offsets;
-  const int32_t *sorted;
+  const int32_t *tl_n;
+  const int32_t *tl_e;
+  const int32_t *tl_start;
+  const int32_t *tl_slots;
   const float *topk_w;
   // shared expert (has_shared == 0: absent)
   int has_shared, I_s;
@@ -67,6 +88,38 @@ struct GemvArgs {
 };
 hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
 hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
+
+// ---------------------------------------------------------------- fused.hip
+struct FusedArgs {
+  const uint16_t *x;
+  int T, H, E, k, I, I_s, renorm, has_shared, BM, cap, wtype;
+  const float *w_r;
+  const float *b_r;
+  const float *w_sg;
+  const void *w_gu;
+  const float *s_gu;
+  const void *w_d;
+  const float *s_d;
+  const void *ws_gu;
+  const float *ss_gu;
+  const void *ws_d;
+  const float *ss_d;
+  float *logits;      // [T][E]
+  float *gate_logit;  // [T]
+  int32_t *ids;       // [T][k]   (block 0 writes)
+  float *topw;        // [T][k]   (block 0 writes)
+  float *gamma;       // [T]      (block 0 writes)
+  AlignOut al;        // padded alignment (block 0 writes)
+  uint16_t *h;        // [T*k][I]
+  uint16_t *h_s;      // [T][I_s]
+  uint16_t *out;      // [T][H]
+  unsigned *bar;      // barrier words: kMaxBlocks arrival flags, release word, timeout count
+  int xlds;           // set by the launcher
+  unsigned epoch;     // set by the launcher: per-call barrier token base
+  size_t lds_route;   // set by the launcher
+};
+bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype);
+hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len);
 
 // ---------------------------------------------------------------- gemm.hip
 struct GemmArgs {

@@ -15,51 +15,85 @@
 // stable order by slot index whatever the thread timing.
 #include "device.h"
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 
 // ============================================================ router (decode)
-// One wavefront per router row n (n < E: expert rows, n == E: the shared gate
-// row), all T tokens, TG tokens per pass.  Lane l owns float4 groups g = l + 64c.
-template <int TG>
+// One wavefront per router row n (n < E: expert rows, n == E: the shared gate row),
+// all T tokens.  The wavefront's fp32 row is loaded into registers first (lane l owns
+// float4 groups g = l + 64c), the block stages the tokens into LDS while those loads
+// are in flight, then each token is one register dot product and one DPP reduction.
+constexpr int kRouterLds = 64 * 1024;
+
+template <int C>
 __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__restrict__ x, int T, int H,
                                                           const float *__restrict__ w_r,
                                                           const float *__restrict__ b_r, int E,
                                                           const float *__restrict__ w_sg,
                                                           float *__restrict__ logits,
                                                           float *__restrict__ gate_logit) {
+  extern __shared__ uint4 s_x[];
   const int lane = lane_id();
   const int n = blockIdx.x * 4 + wave_id();
   const int NR = E + (w_sg != nullptr ? 1 : 0);
-  if (n >= NR) return;
-  const float *row = n < E ? w_r + (size_t)n * H : w_sg;
-  const float bias = (n < E && b_r != nullptr) ? b_r[n] : 0.0f;
+  const bool active = n < NR;
   const int G4 = H / 4;
-  for (int t0 = 0; t0 < T; t0 += TG) {
-    float acc[TG];
+  float4 w[C];
+  if (active) {
+    const float4 *row = reinterpret_cast<const float4 *>(n < E ? w_r + (size_t)n * H : w_sg);
 #pragma unroll
-    for (int i = 0; i < TG; ++i) acc[i] = 0.0f;
-    for (int g = lane; g < G4; g += kWave) {
-      const float4 w = *reinterpret_cast<const float4 *>(row + 4 * g);
-#pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        const int t = t0 + i;
-        if (t < T) {
-          const uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)t * H + 4 * g);
-          acc[i] = fmaf(w.x, bf16_lo(xv.x), acc[i]);
-          acc[i] = fmaf(w.y, bf16_hi(xv.x), acc[i]);
-          acc[i] = fmaf(w.z, bf16_lo(xv.y), acc[i]);
-          acc[i] = fmaf(w.w, bf16_hi(xv.y), acc[i]);
-        }
+    for (int c = 0; c < C; ++c) {
+      const int g = lane + kWave * c;
+      if (g < G4) {
+        const uint4 u = ld_stream(reinterpret_cast<const uint4 *>(row + g));
+        w[c] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+      } else {
+        w[c] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+  }
+  const float bias = (active && n < E && b_r != nullptr) ? b_r[n] : 0.0f;
+  const int TP = kRouterLds / (H * 2);
+  const int G8 = H / 8;
+  const uint2 *sx2 = reinterpret_cast<const uint2 *>(s_x);
+  for (int t0 = 0; t0 < T; t0 += TP) {
+    const int nt = T - t0 < TP ? T - t0 : TP;
+    __syncthreads();
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t0 * H);
+    for (int i = threadIdx.x; i < nt * G8; i += 256) s_x[i] = src[i];
+    __syncthreads();
+    if (!active) continue;
+    for (int i = 0; i < nt; i += 4) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      const float v = wave_sum(acc[i]);
-      const int t = t0 + i;
-      if (lane == 0 && t < T) {
-        if (n < E) logits[(size_t)t * E + n] = v + bias;
-        else gate_logit[t] = v;
+      for (int c = 0; c < C; ++c) {
+        const int g = lane + kWave * c;
+        if (g < G4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (i + j < nt) {
+              const uint2 xv = sx2[(size_t)(i + j) * G4 + g];
+              float a = acc[j];
+              a = fmaf(w[c].x, bf16_lo(xv.x), a);
+              a = fmaf(w[c].y, bf16_hi(xv.x), a);
+              a = fmaf(w[c].z, bf16_lo(xv.y), a);
+              a = fmaf(w[c].w, bf16_hi(xv.y), a);
+              acc[j] = a;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i + j < nt) {
+          const float v = wave_sum(acc[j]);
+          const int t = t0 + i + j;
+          if (lane == 0) {
+            if (n < E) logits[(size_t)t * E + n] = v + bias;
+            else gate_logit[t] = v;
+          }
+        }
       }
     }
   }
@@ -69,67 +103,18 @@ hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r,
                               const float *w_sg, float *logits, float *gate_logit, hipStream_t s) {
   const int NR = E + (w_sg != nullptr ? 1 : 0);
   dim3 grid((NR + 3) / 4), block(256);
-  if (T <= 1) hipLaunchKernelGGL(router_rows_kernel<1>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else if (T <= 4) hipLaunchKernelGGL(router_rows_kernel<4>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else hipLaunchKernelGGL(router_rows_kernel<8>, grid, block, 0, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  const int TP = kRouterLds / (H * 2);
+  const size_t lds = (size_t)(T < TP ? T : TP) * H * 2;
+  const int C = (H / 4 + kWave - 1) / kWave;
+  if (C <= 2) hipLaunchKernelGGL(router_rows_kernel<2>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 4) hipLaunchKernelGGL(router_rows_kernel<4>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 8) hipLaunchKernelGGL(router_rows_kernel<8>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 16) hipLaunchKernelGGL(router_rows_kernel<16>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else hipLaunchKernelGGL(router_rows_kernel<32>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
   return hipGetLastError();
 }
 
-// ============================================================ top-k (one wavefront per token)
-// Writes ids[0..k), w[0..k) of one token and, when lds_ids is given, the ids into LDS.
-template <int EPL>
-__device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, int k, int renorm,
-                                          int32_t *__restrict__ ids_out, float *__restrict__ w_out,
-                                          int32_t *lds_ids) {
-  const int lane = lane_id();
-  uint64_t key[EPL];
-  float val[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) {
-      val[i] = l[e];
-      key[i] = rank_key(val[i], e);
-    } else {
-      val[i] = 0.0f;
-      key[i] = 0;
-    }
-  }
-  int my_e = 0;
-  float my_v = 0.0f, top = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t b = key[0];
-#pragma unroll
-    for (int i = 1; i < EPL; ++i) b = key[i] > b ? key[i] : b;
-    b = wave_max_u64(b);
-    const float v = rank_value((uint32_t)(b >> 32));
-    if (j == 0) top = v;
-    if (lane == j) {
-      my_e = (int)(~(uint32_t)b);
-      my_v = v;
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (key[i] == b) key[i] = 0;
-  }
-  const float ex = lane < k ? expf(my_v - top) : 0.0f;
-  float denom;
-  if (renorm) {
-    denom = wave_sum(ex);
-  } else {
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) part += expf(val[i] - top);
-    denom = wave_sum(part);
-  }
-  if (lane < k) {
-    ids_out[lane] = my_e;
-    w_out[lane] = ex / denom;
-    if (lds_ids != nullptr) lds_ids[lane] = my_e;
-  }
-}
-
+// ============================================================ top-k (one wavefront per token): topk.h
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                    int renorm, int32_t *__restrict__ ids, float *__restrict__ w,
@@ -154,44 +139,69 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
 }
 
 // ============================================================ alignment, one block (n <= 1024, E <= 1024)
-// s_ids: the n slot ids in LDS.  1024 threads.  Writes every output array.
-__device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, int BM, int cap,
-                                            int32_t *s_cnt, int32_t *s_off, int *s_tmp, AlignOut al) {
+// s_ids: the n slot ids in LDS.  1024 threads.  Writes every output array and, when
+// tl.n is not null, the compact touched-expert list of the decode kernels.
+struct AlignLds {
+  int32_t cnt[kMaxExperts];
+  int32_t off[kMaxExperts + 1];
+  int32_t cstart[kMaxExperts];
+  int tmp[1024 / kWave + 1];
+};
+
+__device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, int BM, int cap, AlignLds &L,
+                                            AlignOut al, Touched tl) {
   constexpr int NT = 1024;
   const int tid = threadIdx.x;
-  if (tid < E) s_cnt[tid] = 0;
+  if (tid < E) L.cnt[tid] = 0;
   __syncthreads();
-  if (tid < n) atomicAdd(&s_cnt[s_ids[tid]], 1);
+  if (tid < n) atomicAdd(&L.cnt[s_ids[tid]], 1);
   __syncthreads();
-  const int padded = tid < E ? (s_cnt[tid] + BM - 1) / BM * BM : 0;
+  const int c = tid < E ? L.cnt[tid] : 0;
+  const int padded = (c + BM - 1) / BM * BM;
   int total;
-  const int excl = block_excl_scan<NT>(padded, s_tmp, &total);
-  if (tid < E) s_off[tid] = excl;
-  if (tid == 0) s_off[E] = total;
+  const int excl = block_excl_scan<NT>(padded, L.tmp, &total);
+  if (tid < E) L.off[tid] = excl;
+  if (tid == 0) L.off[E] = total;
+  const bool want_tl = tl.n != nullptr;
+  if (want_tl) {
+    int n_touched, n_slots;
+    const int idx = block_excl_scan<NT>(c > 0 ? 1 : 0, L.tmp, &n_touched);
+    const int cs = block_excl_scan<NT>(c, L.tmp, &n_slots);
+    if (tid < E) L.cstart[tid] = cs;
+    if (c > 0) {
+      tl.e[idx] = tid;
+      tl.start[idx] = cs;
+    }
+    if (tid == 0) {
+      tl.n[0] = n_touched;
+      tl.start[n_touched] = n_slots;
+    }
+  }
   __syncthreads();
   // stable scatter: a slot's place is its rank among the earlier slots of its expert
   if (tid < n) {
     const int e = s_ids[tid];
     int r = 0;
     for (int i = 0; i < tid; ++i) r += (s_ids[i] == e) ? 1 : 0;
-    al.sorted[s_off[e] + r] = tid;
+    al.sorted[L.off[e] + r] = tid;
+    if (want_tl) tl.slots[L.cstart[e] + r] = tid;
   }
   // padding and tail: every position that no slot takes holds the sentinel n
   for (int p = tid; p < cap; p += NT) {
     bool pad = true;
     if (p < total) {
-      const int e = segment_of(s_off, E, p);
-      pad = (p - s_off[e]) >= s_cnt[e];
+      const int e = segment_of(L.off, E, p);
+      pad = (p - L.off[e]) >= L.cnt[e];
     }
     if (pad) al.sorted[p] = n;
   }
   for (int b = tid; b < cap / BM; b += NT) {
     const int p = b * BM;
-    al.block_expert[b] = p < total ? segment_of(s_off, E, p) : -1;
+    al.block_expert[b] = p < total ? segment_of(L.off, E, p) : -1;
   }
   if (tid < E) {
-    al.counts[tid] = s_cnt[tid];
-    al.offsets[tid] = s_off[tid];
+    al.counts[tid] = L.cnt[tid];
+    al.offsets[tid] = L.off[tid];
   }
   if (tid == 0) {
     al.offsets[E] = total;
@@ -202,12 +212,10 @@ __device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, 
 __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t *__restrict__ ids, int n, int E, int BM,
                                                            int cap, AlignOut al) {
   __shared__ int32_t s_ids[kSmallSlots];
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int s_tmp[1024 / kWave + 1];
+  __shared__ AlignLds L;
   if (threadIdx.x < n) s_ids[threadIdx.x] = ids[threadIdx.x];
   __syncthreads();
-  align_block(s_ids, n, E, BM, cap, s_cnt, s_off, s_tmp, al);
+  align_block(s_ids, n, E, BM, cap, L, al, Touched{nullptr, nullptr, nullptr, nullptr});
 }
 
 hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s) {
@@ -221,30 +229,57 @@ __global__ __launch_bounds__(1024) void topk_align_small_kernel(const float *__r
                                                                 const float *__restrict__ gate_logit, int T, int E,
                                                                 int k, int renorm, int BM, int cap,
                                                                 int32_t *__restrict__ ids, float *__restrict__ w,
-                                                                float *__restrict__ gamma, AlignOut al) {
+                                                                float *__restrict__ gamma, AlignOut al, Touched tl) {
   __shared__ int32_t s_ids[kSmallSlots];
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int s_tmp[1024 / kWave + 1];
+  __shared__ AlignLds L;
   for (int t = wave_id(); t < T; t += 1024 / kWave)
     topk_wave<EPL>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, w + (size_t)t * k,
                    s_ids + t * k);
   if (gamma != nullptr && threadIdx.x < T) gamma[threadIdx.x] = 1.0f / (1.0f + expf(-gate_logit[threadIdx.x]));
   __syncthreads();
-  align_block(s_ids, T * k, E, BM, cap, s_cnt, s_off, s_tmp, al);
+  align_block(s_ids, T * k, E, BM, cap, L, al, tl);
 }
 
 hipError_t launch_topk_align_small(const float *logits, const float *gate_logit, int T, int E, int k, int renorm,
                                    int BM, int64_t cap, int32_t *ids, float *w, float *gamma, AlignOut al,
-                                   hipStream_t s) {
+                                   Touched tl, hipStream_t s) {
   const int epl = (E + kWave - 1) / kWave;
   dim3 grid(1), block(1024);
   const int c = (int)cap;
-  if (epl <= 1) hipLaunchKernelGGL(topk_align_small_kernel<1>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
-  else if (epl <= 2) hipLaunchKernelGGL(topk_align_small_kernel<2>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
-  else if (epl <= 4) hipLaunchKernelGGL(topk_align_small_kernel<4>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
-  else if (epl <= 8) hipLaunchKernelGGL(topk_align_small_kernel<8>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
-  else hipLaunchKernelGGL(topk_align_small_kernel<16>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al);
+  if (epl <= 1) hipLaunchKernelGGL(topk_align_small_kernel<1>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 2) hipLaunchKernelGGL(topk_align_small_kernel<2>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 4) hipLaunchKernelGGL(topk_align_small_kernel<4>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 8) hipLaunchKernelGGL(topk_align_small_kernel<8>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else hipLaunchKernelGGL(topk_align_small_kernel<16>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  return hipGetLastError();
+}
+
+// Compact touched-expert list from an existing alignment (counts, offsets, sorted ids).
+__global__ __launch_bounds__(1024) void compact_touched_kernel(const int32_t *__restrict__ counts,
+                                                               const int32_t *__restrict__ offsets,
+                                                               const int32_t *__restrict__ sorted, int E,
+                                                               Touched tl) {
+  __shared__ int s_tmp[1024 / kWave + 1];
+  const int tid = threadIdx.x;
+  const int c = tid < E ? counts[tid] : 0;
+  int n_touched, n_slots;
+  const int idx = block_excl_scan<1024>(c > 0 ? 1 : 0, s_tmp, &n_touched);
+  const int cs = block_excl_scan<1024>(c, s_tmp, &n_slots);
+  if (c > 0) {
+    tl.e[idx] = tid;
+    tl.start[idx] = cs;
+    const int off = offsets[tid];
+    for (int r = 0; r < c; ++r) tl.slots[cs + r] = sorted[off + r];
+  }
+  if (tid == 0) {
+    tl.n[0] = n_touched;
+    tl.start[n_touched] = n_slots;
+  }
+}
+
+hipError_t launch_compact_touched(const int32_t *counts, const int32_t *offsets, const int32_t *sorted, int E,
+                                  Touched tl, hipStream_t s) {
+  hipLaunchKernelGGL(compact_touched_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, sorted, E, tl);
   return hipGetLastError();
 }
 

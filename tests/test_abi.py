@@ -125,7 +125,8 @@ def test_workspace_sizes_and_plans(lib):
     assert b"path=decode" in plan(64, ctypes.byref(L))
     assert b"path=prefill" in plan(65, ctypes.byref(L))
     ew = _c(lib, "moe_experts_workspace_size")
-    assert ew(8, 8, ctypes.byref(L.routed), 16) == 8 * 8 * 512 * 2
+    tl = -(-(1 + 256 + 257 + 64) * 4 // 256) * 256           # compact touched-expert list
+    assert ew(8, 8, ctypes.byref(L.routed), 16) == 8 * 8 * 512 * 2 + tl
 
 
 def test_stage_events_hook_bounds(lib):
