@@ -52,7 +52,18 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--four-kernel", action="store_true", help="run decode blocks as four kernels, not the fused one")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (5 times) for the HBM counter calibration")
     return p.parse_args()
+
+
+# sources each dominant kernel is built from: a counter summary is valid only for this text
+CSRC = "speculative_verify_moe_amd/csrc/"
+KERNEL_SOURCES = {
+    "moe_decode_fused": [CSRC + "fused.hip", CSRC + "topk.h", CSRC + "device.h"],
+    "gemv_gate_up": [CSRC + "gemv.hip", CSRC + "device.h"],
+    "gemm_gate_up_mfma": [CSRC + "gemm.hip", CSRC + "device.h"],
+}
 
 
 def source_hash(paths):
@@ -63,16 +74,39 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def read_summary(path):
+    """`key: value` lines of a committed profile summary (other lines are ignored)."""
+    d = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#", "|")):
+                key, val = ln.split(":", 1)
+                d[key.strip()] = val.strip()
+    return d
+
+
 def load_traffic(kernel, workload, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it still matches the source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still matches the source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("source_hash") != src_hash:
+    d = read_summary(path)
+    if d.get("source_hash") != src_hash or "hbm_bytes_per_launch" not in d:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return int(float(d["hbm_bytes_per_launch"]))
+
+
+def calibrate_copy(mib):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
 
 
 def main():
@@ -81,6 +115,10 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import speculative_verify_moe_amd as moe
@@ -159,18 +197,21 @@ def main():
         moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events around every stage on the launch stream
+    # ---- timed region: K steps, HIP events on every stage's kernels (launch stream)
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
+    # stage s of step i: events[i][2s] at its first kernel's start, events[i][2s+1] at its last
+    # kernel's end (attached to the kernel dispatches by the library)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(K)]
     stream = torch.cuda.current_stream()
     for evs in events:
         for ev in evs:
             ev.record(stream)
+    handles = [moe.stage_event_handles(evs) for evs in events]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
         r = i % L_rep
-        moe.moe_set_stage_events(events[i])
+        moe.moe_set_stage_events(handles[i])
         moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
     moe.moe_set_stage_events(None)
     torch.cuda.synchronize()
@@ -179,8 +220,8 @@ def main():
     stage_ms = np.zeros((K, nst))
     for i in range(K):
         for s in range(nst):
-            stage_ms[i, s] = events[i][s].elapsed_time(events[i][s + 1])
-    gpu_ms = np.array([events[i][0].elapsed_time(events[i][nst]) for i in range(K)])
+            stage_ms[i, s] = events[i][2 * s].elapsed_time(events[i][2 * s + 1])
+    gpu_ms = np.array([events[i][0].elapsed_time(events[i][2 * nst - 1]) for i in range(K)])
     nt_steps = np.array([touched[i % L_rep] for i in range(K)])
 
     ms_per_step = elapsed * 1e3 / K
@@ -191,14 +232,7 @@ def main():
     dom = 0 if fused else (4 if prefill else 2)
     dom_name = stages[dom]
     dom_ms = stage_ms[:, dom]
-    csrc = "speculative_verify_moe_amd/csrc/"
-    if fused:
-        src = [csrc + "fused.hip", csrc + "topk.h", csrc + "device.h"]
-    elif prefill:
-        src = [csrc + "gemm.hip", csrc + "device.h"]
-    else:
-        src = [csrc + "gemv.hip", csrc + "device.h"]
-    src_hash = source_hash(src)
+    src_hash = source_hash(KERNEL_SOURCES[dom_name])
     if not prefill:
         per = layer_bytes if fused else gate_up_bytes
         alg_bytes = np.array([per(n) for n in nt_steps], dtype=np.float64)

@@ -178,11 +178,13 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L);
 enum { MOE_OPT_DECODE_FUSED = 1 };
 moe_status moe_set_option(int32_t key, int32_t value);
 
-/* Measurement hook.  events: n_events hipEvent_t handles (host array), or NULL to
- * turn the hook off.  While set on a thread, each moe_layer_forward call on that
- * thread records events[i] on its stream just before its stage i and
- * events[n_stages] after the last stage (only as many as n_events allows).  A stage
- * is one kernel or a fixed group of kernels; moe_describe_plan names the stages in
+/* Measurement hook.  events: n_events hipEvent_t handles (host array, created with
+ * timing enabled), or NULL to turn the hook off; at most 64.  While set on a thread,
+ * stage i of each moe_layer_forward call on that thread takes events[2i] and
+ * events[2i+1] (only as many as n_events holds): they are handed to the stage's kernel
+ * dispatches (hipExtLaunchKernel), events[2i] marking the start of its first kernel and
+ * events[2i+1] the end of its last, so their elapsed time is the stage's kernel time.  A
+ * stage is one kernel or a fixed group of kernels; moe_describe_plan names the stages in
  * launch order (fused decode: 1 stage, four-kernel decode: 4, prefill: 7). */
 moe_status moe_set_stage_events(void *const *events, int32_t n_events);
 

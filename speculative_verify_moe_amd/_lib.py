@@ -188,18 +188,27 @@ def moe_set_option(key, value):
     _check(_lib.moe_set_option(key, value))
 
 
-def moe_set_stage_events(events):
-    """events: list of torch.cuda.Event(enable_timing=True) (recorded on the layer's stream), or None."""
-    if not events:
-        _check(_lib.moe_set_stage_events(None, 0))
-        return
+def stage_event_handles(events):
+    """The HIP handles of a list of torch.cuda.Event(enable_timing=True), as the host array the
+    measurement hook takes (build it once, outside a timed loop)."""
     handles = []
     for ev in events:
         if ev.cuda_event == 0:      # torch creates the HIP event lazily
             ev.record()
         handles.append(ctypes.c_void_p(ev.cuda_event))
-    arr = (ctypes.c_void_p * len(handles))(*handles)
-    _check(_lib.moe_set_stage_events(arr, len(handles)))
+    return (_P * len(handles))(*handles), len(handles)
+
+
+def moe_set_stage_events(events):
+    """events: list of torch.cuda.Event(enable_timing=True), the (array, n) pair that
+    stage_event_handles returns, or None to turn the hook off.  Stage i of each following
+    moe_layer_forward on this thread takes events 2i (start of its first kernel) and 2i+1
+    (end of its last)."""
+    if not events:
+        _check(_lib.moe_set_stage_events(None, 0))
+        return
+    arr, n = events if isinstance(events, tuple) else stage_event_handles(events)
+    _check(_lib.moe_set_stage_events(arr, n))
 
 
 def moe_route_topk(logits, k, renormalize=True, topk_ids=None, topk_w=None):

@@ -19,6 +19,10 @@
 
 using namespace moe;
 
+namespace moe {
+thread_local hipEvent_t g_kstart = nullptr, g_kstop = nullptr;
+}
+
 namespace {
 
 thread_local char g_err[512];
@@ -68,12 +72,17 @@ moe_status check_device() {
   return MOE_OK;
 }
 
+// Stage i of a call takes events 2i (start of its first kernel) and 2i+1 (end of its last).
 struct Stager {
-  hipStream_t s;
   int i = 0;
-  explicit Stager(hipStream_t st) : s(st) {}
-  void mark() {
-    if (i < g_nevents && g_events[i] != nullptr) hipEventRecord((hipEvent_t)g_events[i], s);
+  Stager() = default;
+  ~Stager() { g_kstart = g_kstop = nullptr; }
+  void begin() {
+    g_kstart = 2 * i < g_nevents ? (hipEvent_t)g_events[2 * i] : nullptr;
+    g_kstop = 2 * i + 1 < g_nevents ? (hipEvent_t)g_events[2 * i + 1] : nullptr;
+  }
+  void end() {
+    g_kstart = g_kstop = nullptr;
     ++i;
   }
 };
@@ -456,7 +465,7 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   float *gamma = (float *)(base + p.off_gamma);
   AlignOut al{(int32_t *)(base + p.off_sorted), (int32_t *)(base + p.off_bexp), (int32_t *)(base + p.off_counts),
               (int32_t *)(base + p.off_offsets), (int32_t *)(base + p.off_np)};
-  Stager sg(s);
+  Stager sg;
 
   const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 &&
                      fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0, L->routed.wtype);
@@ -497,18 +506,19 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     f.h_s = (uint16_t *)(base + p.off_hs);
     f.out = out;
     f.bar = (unsigned *)(base + p.off_bar);
-    sg.mark();
+    sg.begin();
     if ((st = launched(launch_fused_decode(f, s, nullptr, 0), "moe_decode_fused")) != MOE_OK) return st;
-    sg.mark();
+    sg.end();
     return MOE_OK;
   }
 
   if (p.path == PATH_DECODE) {
-    sg.mark();
+    sg.begin();
     if ((st = launched(launch_router_rows(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
                                           logits, gate, s), "router_rows")) != MOE_OK)
       return st;
-    sg.mark();
+    sg.end();
+    sg.begin();
     const Touched tl = touched_at((int32_t *)(base + p.off_tl), E);
     if ((st = launched(launch_topk_align_small(logits, shared ? gate : nullptr, T, E, k, L->renormalize != 0, p.BM,
                                                p.cap, ids, w, shared ? gamma : nullptr, al, tl, s),
@@ -533,29 +543,34 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     g.h = (uint16_t *)(base + p.off_h);
     g.h_s = (uint16_t *)(base + p.off_hs);
     g.out = out;
-    sg.mark();
+    sg.end();
+    sg.begin();
     if ((st = launched(launch_gemv_gate_up(g, s, nullptr, 0), "gemv_gate_up")) != MOE_OK) return st;
-    sg.mark();
+    sg.end();
+    sg.begin();
     if ((st = launched(launch_gemv_down(g, s, nullptr, 0), "gemv_down")) != MOE_OK) return st;
-    sg.mark();
+    sg.end();
     return MOE_OK;
   }
 
   // prefill chunk
   uint16_t *w3 = (uint16_t *)(base + p.off_w3);
-  sg.mark();
+  sg.begin();
   if ((st = launched(launch_router_split(L->router_w, shared ? L->shared_gate_w : nullptr, E, H, w3, s),
                      "router_split")) != MOE_OK)
     return st;
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_router_gemm(x, T, H, w3, E, shared ? 1 : 0, L->router_b, logits, gate, s),
                      "router_gemm")) != MOE_OK)
     return st;
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_topk(logits, T, E, k, L->renormalize != 0, ids, w, shared ? gate : nullptr,
                                  shared ? gamma : nullptr, s), "topk")) != MOE_OK)
     return st;
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_align_large(ids, (int)n, E, p.BM, p.cap, al, (int32_t *)(base + p.off_hist), s),
                      "align")) != MOE_OK)
     return st;
@@ -580,15 +595,18 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   a.h_s = (uint16_t *)(base + p.off_hs);
   a.y = (uint16_t *)(base + p.off_y);
   a.y_s = (uint16_t *)(base + p.off_ys);
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
-  sg.mark();
+  sg.end();
+  sg.begin();
   if ((st = launched(launch_combine(a.y, shared ? a.y_s : nullptr, w, shared ? gamma : nullptr, T, H, k, out, s),
                      "combine")) != MOE_OK)
     return st;
-  sg.mark();
+  sg.end();
   return MOE_OK;
 }
 

@@ -37,6 +37,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
+#include <mutex>
 
 #include "device.h"
 #include "internal.h"
@@ -641,30 +642,49 @@ namespace {
 std::atomic<unsigned> g_epoch{1};
 }
 
+// Per device: the LDS size the kernel was opened up to, the CU count and how many
+// blocks of that LDS size fit on a CU (queried once per device and LDS size).
+struct FusedLaunchInfo {
+  size_t lds_allowed = 64 * 1024;
+  size_t lds_queried = 0;
+  int cus = 0, per_cu = 0;
+};
+
 template <int ESZ, int CGU, int CGD, int CR>
 static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *nb_out) {
   auto kern = moe_decode_fused_kernel<ESZ, CGU, CGD, CR>;
-  static size_t allowed = 64 * 1024;
-  if (lds > allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    allowed = lds;
-  }
-  int dev = 0, cus = 0, per_cu = 0;
+  static std::mutex mu;
+  static FusedLaunchInfo info[64];
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), kNT, lds);
-  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int cus = 0, per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    FusedLaunchInfo &d = info[dev];
+    if (lds > d.lds_allowed) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      d.lds_allowed = lds;
+    }
+    if (d.lds_queried != lds) {
+      e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu, reinterpret_cast<const void *>(kern), kNT, lds);
+      if (e != hipSuccess) return e;
+      d.lds_queried = lds;
+    }
+    cus = d.cus;
+    per_cu = d.per_cu;
+  }
   // one block per CU; the whole grid must be resident at once for the barriers
   const int nb = std::min(cus, kMaxBlocks);
   if (per_cu < 1 || (long)per_cu * cus < nb) return hipErrorInvalidConfiguration;
   *nb_out = nb;
   a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3FFFFFFFu;  // tokens 2e+1, 2e+2: never 0
-  hipLaunchKernelGGL(kern, dim3(nb), dim3(kNT), lds, s, a);
-  return hipGetLastError();
+  return launch_k(kern, dim3(nb), dim3(kNT), lds, s, a);
 }
 
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {

@@ -246,7 +246,7 @@ hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) {
   const int imax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
   const int NN = imax / (TN / 2);
   RouterArgs ra{};
-  hipLaunchKernelGGL(grouped_gemm_kernel<MODE_GATE_UP>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
+  launch_k(grouped_gemm_kernel<MODE_GATE_UP>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
                      MT_r, MT_s, NN);
   return hipGetLastError();
 }
@@ -256,7 +256,7 @@ hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) {
   const int MT_s = a.has_shared ? (a.T + TM - 1) / TM : 0;
   const int NN = a.H / TN;
   RouterArgs ra{};
-  hipLaunchKernelGGL(grouped_gemm_kernel<MODE_DOWN>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
+  launch_k(grouped_gemm_kernel<MODE_DOWN>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
                      MT_r, MT_s, NN);
   return hipGetLastError();
 }
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
 }
 
 hipError_t launch_router_split(const float *w_r, const float *w_sg, int E, int H, uint16_t *w3, hipStream_t s) {
-  hipLaunchKernelGGL(router_split_kernel, dim3(512), dim3(256), 0, s, w_r, w_sg, E, H, w3);
+  launch_k(router_split_kernel, dim3(512), dim3(256), 0, s, w_r, w_sg, E, H, w3);
   return hipGetLastError();
 }
 
@@ -298,7 +298,7 @@ hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w
   RouterArgs ra{b_r, logits, gate_logit, E, E + (has_sg ? 1 : 0)};
   const int MT = (T + TM - 1) / TM;
   const int NN = (ra.NRt + TN - 1) / TN;
-  hipLaunchKernelGGL(grouped_gemm_kernel<MODE_ROUTER>, dim3(grid_for(MT * NN)), dim3(NTHR), 0, s, a, ra, MT, 0, NN);
+  launch_k(grouped_gemm_kernel<MODE_ROUTER>, dim3(grid_for(MT * NN)), dim3(NTHR), 0, s, a, ra, MT, 0, NN);
   return hipGetLastError();
 }
 
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 
 hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
                           int H, int k, uint16_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, s, y, y_s, topk_w, gamma, T, H, k, out);
+  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, y, y_s, topk_w, gamma, T, H, k, out);
   return hipGetLastError();
 }
 

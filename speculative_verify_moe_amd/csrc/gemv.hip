@@ -27,6 +27,7 @@
 //            then the block combines out[t][row] = bf16(sum_j w[t][j] * y[t*k+j][row]
 //            + gamma_t * y_s[t][row]) in slot order.  No float atomics.
 #include <cstdio>
+#include <mutex>
 
 #include "device.h"
 #include "internal.h"
@@ -317,27 +318,42 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
 static size_t list_bytes(const GemvArgs &a) { return (((size_t)(2 * a.E + 1 + a.T * a.k) * 4) + 15) & ~(size_t)15; }
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel (gfx950 has 160 KiB per CU);
-// the largest size asked for so far is remembered per kernel instantiation.
-template <typename K>
-static hipError_t set_lds(K kernel, size_t bytes) {
-  static size_t allowed = 64 * 1024;
-  if (bytes <= allowed) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) allowed = bytes;
-  return e;
+// the largest size opened so far is remembered per (kernel, device).
+static hipError_t set_lds(const void *kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  struct Entry {
+    const void *k;
+    int dev;
+    size_t allowed;
+  };
+  static std::mutex mu;
+  static Entry table[64];
+  static int used = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  Entry *hit = nullptr;
+  for (int i = 0; i < used; ++i)
+    if (table[i].k == kernel && table[i].dev == dev) hit = &table[i];
+  if (hit != nullptr && bytes <= hit->allowed) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  if (hit == nullptr && used < 64) hit = &table[used++];
+  if (hit != nullptr) *hit = Entry{kernel, dev, bytes};
+  return hipSuccess;
 }
 
 template <int ESZ, int CG>
 static hipError_t launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, bool xlds, size_t lds) {
   if (xlds) {
     auto k = gemv_gate_up_kernel<ESZ, CG, true>;
-    hipError_t e = set_lds(k, lds);
+    hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(kGuNW * kWave), lds, s, a);
+    launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
   } else {
     auto k = gemv_gate_up_kernel<ESZ, CG, false>;
-    hipLaunchKernelGGL(k, grid, dim3(kGuNW * kWave), lds, s, a);
+    launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -370,14 +386,14 @@ template <int ESZ, int CG>
 static hipError_t launch_dn(const GemvArgs &a, hipStream_t s, dim3 grid, bool hlds, size_t lds) {
   if (hlds) {
     auto k = gemv_down_kernel<ESZ, CG, true>;
-    hipError_t e = set_lds(k, lds);
+    hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(kDnNW * kWave), lds, s, a);
+    launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
   } else {
     auto k = gemv_down_kernel<ESZ, CG, false>;
-    hipError_t e = set_lds(k, lds);
+    hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, dim3(kDnNW * kWave), lds, s, a);
+    launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
   }
   return hipGetLastError();
 }

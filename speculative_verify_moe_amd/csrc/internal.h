@@ -1,11 +1,25 @@
 // internal.h -- host-side launchers shared between the translation units of the library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Measurement hook of moe_set_stage_events: while a stage runs, its start and stop events
+// (or null).  Every kernel is launched through launch_k, which hands them to the kernel's
+// own dispatch (hipExtLaunchKernel), so they time the kernel itself: the start event is
+// consumed by the first launch of the stage, the stop event is given to every launch of
+// it and the last one's end remains.
+extern thread_local hipEvent_t g_kstart, g_kstop;
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+  hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, g_kstart, g_kstop, 0u, args...);
+  g_kstart = nullptr;
+  return hipGetLastError();
+}
 
 // Decode/verify blocks run the GEMV path when T <= kDecodeMaxT and T*k <= kSmallSlots.
 constexpr int kDecodeMaxT = 64;
