@@ -72,6 +72,22 @@ __device__ __forceinline__ void st_agent(unsigned *p, unsigned v) {
 // issue order, so this also waits for earlier loads); the clobber keeps the compiler from
 // moving memory operations across it.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Mark a register buffer as consumed here: the compiler waits for its loads at this point,
+// so no later reuse of those registers waits on the loads issued after them.
+template <int N>
+__device__ __forceinline__ void consume(const uint4 (&w)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(w[i].x), "v"(w[i].y), "v"(w[i].z), "v"(w[i].w));
+}
+
+// Barrier words (kBarrierWords in the workspace): arrival flags [kMaxBlocks], the release
+// word, the timeout count.
 
 // flags[kMaxBlocks]: per-block arrival words, then the release word and a timeout count.
 // Every wavefront that wrote data the other blocks will read calls wait_stores() first.
@@ -147,13 +163,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   unsigned *s_mlo = reinterpret_cast<unsigned *>(s_off + E + 1);  // [E] tokens 0..31 per expert
   unsigned *s_mhi = s_mlo + E;                                    // [E] tokens 32..63
   __shared__ int s_nt;
+  __shared__ int s_qa, s_qb;  // phase A / phase B entry counters
   __shared__ uint32_t s_wsum[2 * kNW];
   char *data = smem + a.lds_route;
+  // this call's barrier tokens follow the workspace's last release word: block 0 rewrites it
+  // only once every block has arrived, and a block's arrival depends on this load
+  const unsigned tok0 = ld_agent(a.bar + kMaxBlocks);
 
   // ---------------- phase 0: router rows, shared-expert prefetch, tokens to LDS
   const int NR = E + (a.w_sg != nullptr ? 1 : 0);
-  constexpr int kPrefetchWave = kNW - 1;
-  const int my_row = wave < kPrefetchWave ? wave * NB + blockIdx.x : -1;  // rows beyond NB*(kNW-1): more passes
+  const int my_row = wave * NB + blockIdx.x;  // rows beyond kNW * NB: more passes
   float4 wr[CR];
   auto load_router_row = [&](int n) {
     const float4 *row = reinterpret_cast<const float4 *>(n < E ? a.w_r + (size_t)n * H : a.w_sg);
@@ -168,33 +187,47 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  if (my_row >= 0 && my_row < NR) load_router_row(my_row);
+  if (my_row < NR) load_router_row(my_row);
 
   // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
   const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
   uint4 wa[CGU], wb[CGU];
-  auto gu_row = [&](bool shared, int e, int p) -> const uint4 * {
-    const uint8_t *bank = shared ? (const uint8_t *)a.ws_gu : (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
-    const int Iw = shared ? a.I_s : a.I;
+  // Weight rows are streamed with raw buffer loads: the expert's matrix is the buffer (base
+  // in scalar registers), the lane's row and column offset one VGPR, the column group a
+  // uniform scalar offset.  Exactly CGU (CGD per row set) load instructions, all in range:
+  // groups past the row (whole groups: H, I, I_s are multiples of 16 groups) reload the
+  // last group and are zeroed where they are used, so nothing waits for a load here;
+  // phase A counts on that number when it waits for its h stores.
+  typedef int i4_t __attribute__((ext_vector_type(4)));
+  constexpr int kNt = 2;  // cache policy: non-temporal (weights are read once)
+  auto as_u4 = [](i4_t v) { return make_uint4(v.x, v.y, v.z, v.w); };
+  // the lane's byte offset in an expert's gate/up matrix for row pair p (gate rows 2p, 2p+1,
+  // up rows Iw+2p, Iw+2p+1): fixed for the whole phase, computed once
+  auto gu_voff = [&](int Iw, int p) {
     const int row = rg < 2 ? 2 * p + rg : Iw + 2 * p + (rg - 2);
-    return reinterpret_cast<const uint4 *>(bank + (size_t)row * H * ESZ);
+    return row * H * ESZ + l16 * 16;
   };
-  auto gu_load = [&](uint4(&w)[CGU], bool shared, int e, int p) {
-    const uint4 *ptr = gu_row(shared, e, p);
-    const int G = H / VPG;
+  // valid == false: an empty descriptor, so the loads return zeros without reading memory
+  // (they still issue, which keeps every wait count the same on all paths)
+  auto gu_load = [&](uint4(&w)[CGU], bool valid, bool shared, int e, int voff) {
+    e = __builtin_amdgcn_readfirstlane(e);  // uniform (read from LDS): the descriptor stays scalar
+    const int Iw = shared ? a.I_s : a.I;
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_gu : (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
+                                                                        valid ? 2 * Iw * H * ESZ : 0, 0x00020000);
+    const int last = H / VPG / 16 - 1;
 #pragma unroll
-    for (int c = 0; c < CGU; ++c) {
-      const int g = l16 + 16 * c;
-      w[c] = g < G ? ld_stream(ptr + g) : make_uint4(0, 0, 0, 0);
-    }
+    for (int c = 0; c < CGU; ++c) w[c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff, 256 * min(c, last), kNt));
+    // the offset stays allocated past the loads, so no load lands in its register (a later
+    // write of that register would have to wait for the load)
+    asm volatile("" ::"v"(voff));
   };
-  const bool first_pair_shared = a.has_shared && 2 * (int)blockIdx.x < a.I_s;
 
-  // tokens to LDS by wavefronts 0..6 (the prefetch wavefront's loads stay in flight), in
-  // rows of xg uint4 ending in the zero pad; unguarded (clamped) loads, so they overlap
+  // tokens to LDS, in rows of xg uint4 ending in the zero pad; unguarded (clamped) loads,
+  // so they are in flight together
   uint4 *sx = reinterpret_cast<uint4 *>(data);
-  if (wave < kPrefetchWave) {
-    constexpr int kStep = kPrefetchWave * kWave, kB = 8;
+  {
+    constexpr int kStep = kNT, kB = 8;
     const uint4 *gx = reinterpret_cast<const uint4 *>(a.x);
     const int n16 = T * xg, last = T * G8 - 1;
     for (int base = tid; base < n16; base += kB * kStep) {
@@ -216,7 +249,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     s_mhi[e] = 0u;
   }
   __syncthreads();
-  if (wave == kPrefetchWave && (int)blockIdx.x < NPair && first_pair_shared) gu_load(wa, true, 0, blockIdx.x);
 
   auto router_rows = [&](int n) {
     const float bias = (n < E && a.b_r != nullptr) ? a.b_r[n] : 0.0f;
@@ -249,14 +281,14 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  if (my_row >= 0 && my_row < NR) router_rows(my_row);
-  // rows beyond the first pass (E + 1 > 7 * NB): strided passes
-  for (int n = my_row + (kNW - 1) * NB; my_row >= 0 && n < NR; n += (kNW - 1) * NB) {
+  if (my_row < NR) router_rows(my_row);
+  // rows beyond the first pass (E + 1 > kNW * NB): strided passes
+  for (int n = my_row + kNW * NB; n < NR; n += kNW * NB) {
     load_router_row(n);
     router_rows(n);
   }
-  if (wave != kPrefetchWave) wait_stores();  // the router rows' logit stores
-  grid_barrier(a.bar, 2 * a.epoch + 1);
+  wait_stores();  // the router rows' logit stores
+  grid_barrier(a.bar, tok0 + 1u);
 
   // ---------------- phase 1: routing in every block
   {
@@ -337,6 +369,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (tid == 0) {
       s_start[nt] = n_slots;
       s_nt = nt;
+      s_qa = 0;
+      s_qb = 0;
     }
     for (int i = tid; i < n_slots; i += kNT) {
       const int t = i / k, e = s_ids[i];
@@ -378,21 +412,26 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int nr = s_nt;
 
-  // ---------------- phase A: gate/up for row pairs p = b, b + NB, ...
-  for (int p = blockIdx.x; p < NPair; p += NB) {
-    const bool sh = a.has_shared && 2 * p < a.I_s;
-    const bool rt = 2 * p < a.I;
-    const int n_r = rt ? nr : 0;
-    const int NE = n_r + (sh ? 1 : 0);
-    // entry q: q == 0 is the shared expert when sh, then routed experts in ascending order
-    auto ent_shared = [&](int q) { return sh && q == 0; };
-    auto ent_index = [&](int q) { return q - (sh ? 1 : 0); };
-    auto compute = [&](const uint4(&w)[CGU], int q) {
-      const bool shared = ent_shared(q);
-      const int ri = ent_index(q);
+  // ---------------- phase A: gate/up of row pair p = b (2b, 2b+1 and I+2b, I+2b+1) for
+  // every entry: entry 0 is the shared expert when this pair has one, then the touched
+  // experts in ascending order.  The wavefronts take entries from an LDS counter, two in
+  // flight each.
+  const int pA = blockIdx.x;
+  const bool shA = a.has_shared && 2 * pA < a.I_s;
+  const int NEA = pA < NPair ? (2 * pA < a.I ? nr : 0) + (shA ? 1 : 0) : 0;
+  {
+    auto compute = [&](uint4(&w)[CGU], int q) {
+      consume(w);
+      // column groups past the row (whole groups) hold a repeated load: zero them in place
+#pragma unroll
+      for (int c = 0; c < CGU; ++c)
+        if (16 * c >= H / VPG) w[c] = make_uint4(0, 0, 0, 0);
+      const bool shared = shA && q == 0;
+      const int ri = q - (shA ? 1 : 0);
       const int e = shared ? 0 : s_e[ri];
       const int q0 = shared ? 0 : s_start[ri];
       const int q1 = shared ? T : s_start[ri + 1];
+      const int p = pA;
       float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
       if (ESZ == 1) {
         const float *sc = shared ? a.ss_gu : a.s_gu + (size_t)e * 2 * a.I;
@@ -407,36 +446,48 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int t = shared ? qq : s_stok[qq];
         const uint4 *xr = xs + (size_t)t * xg;
         float acc = 0.0f;
-        // the token's LDS reads are issued in groups of 4 ahead of their use (one
-        // accumulation chain, same order as the lane loop)
-        uint4 xv[CGU * (3 - ESZ)];
+        // the token's LDS reads in groups of 4, the next group issued before the current one
+        // is used (scheduling barriers keep at most two groups in registers); one
+        // accumulation chain in lane-loop order
+        constexpr int kGrp = 4, NG = CGU / kGrp, XPG = 3 - ESZ;  // uint4 of x per column group
+        static_assert(CGU % kGrp == 0, "column groups come in fours");
+        uint4 xv[2][kGrp * XPG];
+        auto read_group = [&](uint4(&dst)[kGrp * XPG], int gi) {
 #pragma unroll
-        for (int c = 0; c < CGU; ++c) {
-          if (c % 4 == 0) {
-#pragma unroll
-            for (int u = c; u < c + 4 && u < CGU; ++u) {
-              const int gu = min(l16 + 16 * u, H / VPG);  // H / VPG: the zero pad
-              if (ESZ == 2) {
-                xv[u] = xr[gu];
-              } else {
-                xv[2 * u] = xr[2 * gu];
-                xv[2 * u + 1] = xr[2 * gu + 1];
-              }
+          for (int u = 0; u < kGrp; ++u) {
+            const int gu = min(l16 + 16 * (gi * kGrp + u), H / VPG);  // H / VPG: the zero pad
+            if (ESZ == 2) {
+              dst[u] = xr[gu];
+            } else {
+              dst[2 * u] = xr[2 * gu];
+              dst[2 * u + 1] = xr[2 * gu + 1];
             }
           }
-          if (ESZ == 2) {
-            acc = dot8_bf16(w[c], xv[c], acc);
-          } else {
-            const uint4 x0 = xv[2 * c], x1 = xv[2 * c + 1];
-            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].x), x0.x, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].x), x0.y, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].y), x0.z, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].y), x0.w, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].z), x1.x, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].z), x1.y, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].w), x1.z, acc);
-            acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[c].w), x1.w, acc);
+        };
+        read_group(xv[0], 0);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          if (gi + 1 < NG) read_group(xv[(gi + 1) & 1], gi + 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kGrp; ++u) {
+            const int c = gi * kGrp + u;
+            const uint4 wc = w[c];
+            if (ESZ == 2) {
+              acc = dot8_bf16(wc, xv[gi & 1][u], acc);
+            } else {
+              const uint4 x0 = xv[gi & 1][2 * u], x1 = xv[gi & 1][2 * u + 1];
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.x), x0.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.x), x0.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.y), x0.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.y), x0.w, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.z), x1.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.z), x1.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.w), x1.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.w), x1.w, acc);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
         acc = row16_sum(acc);
         const float g0 = lane_value(acc, 0) * sg0, g1 = lane_value(acc, 16) * sg1;
@@ -449,95 +500,130 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     };
-    auto load = [&](uint4(&w)[CGU], int q) {
-      const bool shared = ent_shared(q);
-      gu_load(w, shared, shared ? 0 : s_e[ent_index(q)], p);
+    const int voff_r = gu_voff(a.I, pA), voff_s = gu_voff(a.I_s, pA);
+    auto load = [&](uint4(&w)[CGU], int q) {  // q >= NEA: nothing to load (an empty descriptor)
+      const bool valid = q < NEA, shared = shA && q == 0;
+      gu_load(w, valid, shared, (valid && !shared) ? s_e[q - (shA ? 1 : 0)] : 0, shared ? voff_s : voff_r);
     };
-    int q = (wave + 1) % kNW;  // the prefetch wavefront takes entry 0 (the shared expert)
-    const bool preloaded = (p == (int)blockIdx.x) && wave == kPrefetchWave && first_pair_shared;
-    if (q < NE && !preloaded) load(wa, q);
-    while (q < NE) {
-      const int q2 = q + kNW;
-      if (q2 < NE) load(wb, q2);
+    auto grab = [&]() -> int {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&s_qa, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    // every load is issued (past the last entry they read nothing), so the compiler's wait
+    // counts are the same on every path and no prefetch is waited for early
+    int q = grab();
+    int q2 = grab();
+    load(wa, q);
+    load(wb, q2);
+    while (q < NEA) {
       compute(wa, q);
-      if (q2 >= NE) break;
-      const int q3 = q2 + kNW;
-      if (q3 < NE) load(wa, q3);
+      const int q3 = grab();
+      load(wa, q3);
+      if (q2 >= NEA) break;
       compute(wb, q2);
+      const int q4 = grab();
+      load(wb, q4);
       q = q3;
+      q2 = q4;
     }
   }
 
-  // ---------------- phase B: the second grid barrier, then the first rows' loads
+  // ---------------- phase B: down + combine for output rows 8o .. 8o+7, o = b.  Entries:
+  // 0 the shared expert (with one), then the touched experts, taken from an LDS counter.
+  // Each wavefront except 0 takes its first entry and starts its weight loads before the
+  // second grid barrier (wavefront 0 polls the barrier and keeps its load queue empty).
   const int NOct = H / kOct;
-  const int NEB = nr + (a.has_shared ? 1 : 0);
+  const int oB = blockIdx.x;
+  const int NEB = oB < NOct ? nr + (a.has_shared ? 1 : 0) : 0;
   uint4 da[2][CGD], db[2][CGD];
-  auto dn_load = [&](uint4(&w)[2][CGD], int q, int o) {
+  // the lane's byte offsets in a down matrix for output rows 8o+rg and 8o+4+rg (row length
+  // I or I_s): fixed for the whole phase, computed once
+  const int dv_r0 = (kOct * oB + rg) * a.I * ESZ + l16 * 16, dv_r1 = dv_r0 + 4 * a.I * ESZ;
+  const int dv_s0 = (kOct * oB + rg) * a.I_s * ESZ + l16 * 16, dv_s1 = dv_s0 + 4 * a.I_s * ESZ;
+  auto dn_load = [&](uint4(&w)[2][CGD], int q) {  // q >= NEB: an empty descriptor (as gu_load)
+    const bool valid = q < NEB;
     const bool shared = a.has_shared && q == 0;
     const int ri = q - (a.has_shared ? 1 : 0);
-    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + (size_t)s_e[ri] * H * a.I * ESZ;
     const int K = shared ? a.I_s : a.I;
-    const int G = K / VPG;
+    const int e = (shared || !valid) ? 0 : __builtin_amdgcn_readfirstlane(s_e[ri]);  // uniform: a scalar descriptor
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + (size_t)e * H * a.I * ESZ;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
+                                                                        valid ? H * K * ESZ : 0, 0x00020000);
+    const int last = K / VPG / 16 - 1;
+    const int v0 = shared ? dv_s0 : dv_r0, v1 = shared ? dv_s1 : dv_r1;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 *ptr = reinterpret_cast<const uint4 *>(bank + (size_t)(kOct * o + 4 * s + rg) * K * ESZ);
-#pragma unroll
-      for (int c = 0; c < CGD; ++c) {
-        const int g = l16 + 16 * c;
-        w[s][c] = g < G ? ld_stream(ptr + g) : make_uint4(0, 0, 0, 0);
-      }
+    for (int c = 0; c < CGD; ++c) {
+      w[0][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v0, 256 * min(c, last), kNt));  // zeroed at use
+      w[1][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v1, 256 * min(c, last), kNt));
     }
+    asm volatile("" ::"v"(v0), "v"(v1));  // as in gu_load
+  };
+  auto grab_b = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_qb, 1);
+    return __builtin_amdgcn_readfirstlane(v);
   };
   wait_stores();  // this wavefront's h stores
-  grid_barrier(a.bar, 2 * a.epoch + 2);
-  // first phase-B rows in flight while h is staged
-  if ((int)blockIdx.x < NOct && wave < NEB) dn_load(da, wave, blockIdx.x);
-
-  // ---------------- phase B: down + combine for octets o = b, b + NB, ...
-  float *s_y = reinterpret_cast<float *>(data);               // [T*k][8]
-  float *s_ys = s_y + (size_t)n_slots * kOct;                  // [T][8]
-  // h crosses the barrier: 16-byte loads with the sc1 cache policy (coherent across the
-  // XCDs' L2s) into LDS rows of hg uint4 ending in the zero pad: rows 0..T*k-1 are the
-  // slots, then (with a shared expert) one row per token
+  int qb = wave != 0 ? grab_b() : 0;
+  if (wave != 0) dn_load(da, qb);
+  grid_barrier(a.bar, tok0 + 2u);
+  if (wave == 0) {
+    qb = grab_b();
+    dn_load(da, qb);
+  }
+  // (after the barrier the tokens are dead: y and h take the data region)
+  float *s_y = reinterpret_cast<float *>(data);  // [T*k][8]
+  float *s_ys = s_y + (size_t)n_slots * kOct;   // [T][8]
+  // h rows in LDS, hg uint4 each ending in the zero pad: row r < T*k is position r of the
+  // slots grouped by expert, row T*k + t the shared expert's token t.  h crosses the barrier:
+  // 16-byte loads with the sc1 cache policy (coherent across the XCDs' L2s).
   uint4 *hl = reinterpret_cast<uint4 *>(data + al16((size_t)(n_slots + T) * kOct * 4));
-  {
-    typedef int i4_t __attribute__((ext_vector_type(4)));
-    constexpr int kSc1 = 16;  // cache-policy bit sc1
+  if (NEB > 0) {
+    constexpr int kSc1 = 16;
     const int gr = a.I / 8, gs = a.I_s / 8;
-    const int nrows = n_slots + (a.has_shared ? T : 0);
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, n_slots * gr * 16, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(a.has_shared ? a.h_s : a.h, 0, (a.has_shared ? T * gs : 0) * 16, 0x00020000);
-    constexpr int kBatch = 8;
-    const int n16 = nrows * hg;
-    for (int base = tid; base < n16; base += kBatch * kNT) {
-      i4_t v[kBatch];
+    const int sh0 = a.has_shared ? T : 0;
+    const int nrow = n_slots + sh0;
+    constexpr int kB = 8;
+    for (int base = tid; base < nrow * hg; base += kB * kNT) {
+      i4_t v[kB];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * kNT, r = i / hg, g = i - r * hg;
-        const bool sh = r >= n_slots;
-        const bool ok = i < n16 && g < (sh ? gs : gr);
-        const int off = ok ? (sh ? (r - n_slots) * gs + g : r * gr + g) * 16 : 0;
-        if (sh) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1);
-        else v[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, kSc1);
-        if (!ok) v[j] = i4_t{0, 0, 0, 0};
+      for (int jj = 0; jj < kB; ++jj) {
+        const int idx = base + jj * kNT, r = idx / hg, g = idx - r * hg;
+        const bool shr = r >= n_slots;  // rows n_slots.. : the shared expert
+        const bool ok = idx < nrow * hg && g < (shr ? gs : gr);
+        const int off = ok ? (shr ? (r - n_slots) * gs + g : s_slots[r] * gr + g) * 16 : 0;
+        if (shr) v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1);
+        else v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, kSc1);
+        if (!ok) v[jj] = i4_t{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * kNT;
-        if (i < n16) hl[i] = make_uint4(v[j].x, v[j].y, v[j].z, v[j].w);
+      for (int jj = 0; jj < kB; ++jj) {
+        const int idx = base + jj * kNT;
+        if (idx < nrow * hg) hl[idx] = make_uint4(v[jj].x, v[jj].y, v[jj].z, v[jj].w);
       }
     }
   }
   __syncthreads();
-  for (int o = blockIdx.x; o < NOct; o += NB) {
-    auto compute = [&](const uint4(&w)[2][CGD], int q) {
+  {
+    // ---- entries from the LDS counter, two in flight per wavefront
+    auto compute = [&](uint4(&w)[2][CGD], int q) {
       const bool shared = a.has_shared && q == 0;
       const int ri = q - (a.has_shared ? 1 : 0);
       const int e = shared ? 0 : s_e[ri];
       const int q0 = shared ? 0 : s_start[ri];
       const int q1 = shared ? T : s_start[ri + 1];
       const int Kv = (shared ? a.I_s : a.I) / VPG;
+      consume(w[0]);
+      consume(w[1]);
+      // column groups past the row (whole groups) hold a repeated load: zero them in place
+#pragma unroll
+      for (int c = 0; c < CGD; ++c)
+        if (16 * c >= Kv) w[0][c] = w[1][c] = make_uint4(0, 0, 0, 0);
+      const int o = oB;
       float sc0 = 1.f, sc1 = 1.f;
       if (ESZ == 1) {
         const float *sc = shared ? a.ss_d : a.s_d + (size_t)e * H;
@@ -546,28 +632,30 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       for (int qq = q0; qq < q1; ++qq) {
         const int slot = shared ? qq : s_slots[qq];
-        const uint4 *hr = hl + (size_t)(shared ? n_slots + qq : slot) * hg;
+        const uint4 *hr = hl + (size_t)(shared ? n_slots + qq : qq) * hg;
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int c = 0; c < CGD; ++c) {
-          const int g = min(l16 + 16 * c, Kv);  // Kv: the zero pad (zero weights too)
+          const int g = min(l16 + 16 * c, Kv);  // Kv: the zero pad
+          const uint4 w0 = w[0][c], w1 = w[1][c];
           if (ESZ == 2) {
             const uint4 hv = hr[g];
-            acc0 = dot8_bf16(w[0][c], hv, acc0);
-            acc1 = dot8_bf16(w[1][c], hv, acc1);
+            acc0 = dot8_bf16(w0, hv, acc0);
+            acc1 = dot8_bf16(w1, hv, acc1);
           } else {
             const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
+              const uint4 ws = s == 0 ? w0 : w1;
               float acc = s == 0 ? acc0 : acc1;
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].x), h0.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].x), h0.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].y), h0.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].y), h0.w, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].z), h1.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].z), h1.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].w), h1.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].w), h1.w, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(ws.x), h0.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(ws.x), h0.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(ws.y), h0.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(ws.y), h0.w, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(ws.z), h1.x, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(ws.z), h1.y, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<false>(ws.w), h1.z, acc);
+              acc = dot2_bf16(fp8x2_to_bf16x2<true>(ws.w), h1.w, acc);
               if (s == 0) acc0 = acc;
               else acc1 = acc;
             }
@@ -582,27 +670,27 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     };
-    int q = wave;
-    if (q < NEB && o != (int)blockIdx.x) dn_load(da, q, o);
+    int q = qb;
     while (q < NEB) {
-      const int q2 = q + kNW;
-      if (q2 < NEB) dn_load(db, q2, o);
+      const int q2 = grab_b();
+      dn_load(db, q2);
       compute(da, q);
       if (q2 >= NEB) break;
-      const int q3 = q2 + kNW;
-      if (q3 < NEB) dn_load(da, q3, o);
+      const int q3 = grab_b();
+      dn_load(da, q3);
       compute(db, q2);
       q = q3;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (oB < NOct) {
     for (int idx = tid; idx < T * kOct; idx += kNT) {
       const int t = idx / kOct, rr = idx % kOct;
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) acc = fmaf(s_topw[t * k + j], s_y[(size_t)(t * k + j) * kOct + rr], acc);
       if (a.has_shared) acc = fmaf(s_gamma[t], s_ys[t * kOct + rr], acc);
-      a.out[(size_t)t * H + kOct * o + rr] = to_bf16(acc);
+      a.out[(size_t)t * H + kOct * oB + rr] = to_bf16(acc);
     }
-    __syncthreads();
   }
 }
 
@@ -616,30 +704,43 @@ size_t route_bytes(int T, int k, int E) {
 }
 }  // namespace
 
-size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared, int *xlds, int *hlds) {
+// LDS of one block: the routing region, then the data region -- the tokens in phases 0
+// and A, then the expert outputs y of the block's rows and the h rows in phase B.
+size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared) {
   const size_t rb = route_bytes(T, k, E);
   const size_t n = (size_t)T * k;
-  const size_t xb = (size_t)T * (H / 8 + 2) * 16;
+  const size_t xb = al16((size_t)T * (H / 8 + 2) * 16);
   const size_t yb = al16((n + T) * kOct * 4);
   const size_t hb = (n + (has_shared ? (size_t)T : 0)) * ((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16;
-  *xlds = rb + xb <= kFusedLdsMax;
-  *hlds = rb + yb + hb <= kFusedLdsMax;
   return rb + std::max(xb, yb + hb);
 }
 
-// The fused kernel's register tiles hold H <= 2048 and I, I_s <= 512; the tokens and h
-// must fit in LDS (T rows of H + 16 elements, and T * k (+ T) rows of max(I, I_s) + 16).
+namespace {
+// CU count of the current device (cached per device; 0 when it cannot be read).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+}  // namespace
+
+// The fused kernel's register tiles hold H <= 2048 and I, I_s <= 512; one block owns one
+// gate/up row pair and one octet of output rows, so the grid (one block per CU) must cover
+// max(I, I_s) / 2 pairs and H / 8 octets; the tokens, y and h must fit in LDS together.
 bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype) {
-  (void)wtype;
   if (T < 1 || T > kDecodeMaxT || T * k > kSmallSlots || E > kMaxExperts) return false;
   if (H > kXW || I > kHW || I_s > kHW) return false;
-  int xlds, hlds;
-  fused_lds_bytes(T, H, E, k, I, I_s, I_s > 0, &xlds, &hlds);
-  return xlds && hlds;
-}
-
-namespace {
-std::atomic<unsigned> g_epoch{1};
+  const int grp = 16 * (wtype == 0 ? 8 : 16);  // elements in 16 column groups of 16 bytes
+  if (H % grp != 0 || I % grp != 0 || I_s % grp != 0) return false;
+  const int nb = std::min(device_cus(), kMaxBlocks);
+  if ((I_s > I ? I_s : I) / 2 > nb || H / kOct > nb) return false;
+  return fused_lds_bytes(T, H, E, k, I, I_s, I_s > 0) <= kFusedLdsMax;
 }
 
 // Per device: the LDS size the kernel was opened up to, the CU count and how many
@@ -682,16 +783,15 @@ static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *n
   // one block per CU; the whole grid must be resident at once for the barriers
   const int nb = std::min(cus, kMaxBlocks);
   if (per_cu < 1 || (long)per_cu * cus < nb) return hipErrorInvalidConfiguration;
+  // one gate/up row pair and one output octet per block at most
+  if ((a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2 > nb || a.H / kOct > nb) return hipErrorInvalidConfiguration;
   *nb_out = nb;
-  a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3FFFFFFFu;  // tokens 2e+1, 2e+2: never 0
   return launch_k(kern, dim3(nb), dim3(kNT), lds, s, a);
 }
 
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {
-  int xlds = 0, hlds = 0;
-  const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared, &xlds, &hlds);
-  if (!xlds || !hlds) return hipErrorInvalidValue;
-  a.xlds = 1;
+  const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared);
+  if (lds > kFusedLdsMax) return hipErrorInvalidValue;
   a.lds_route = route_bytes(a.T, a.k, a.E);
   int nb = 0;
   hipError_t e;

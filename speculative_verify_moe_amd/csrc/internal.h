@@ -28,7 +28,8 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 // Slots per block of the multi-block alignment.
 constexpr int kAlignChunk = 256;
-// Blocks of the fused decode kernel at most (one per CU) and its barrier words.
+// Blocks of the fused decode kernel at most (one per CU) and its barrier words (arrival
+// flags, release word, timeout count).
 constexpr int kMaxBlocks = 1024;
 constexpr int kBarrierWords = kMaxBlocks + 64;
 
@@ -128,8 +129,6 @@ struct FusedArgs {
   uint16_t *h_s;      // [T][I_s]
   uint16_t *out;      // [T][H]
   unsigned *bar;      // barrier words: kMaxBlocks arrival flags, release word, timeout count
-  int xlds;           // set by the launcher
-  unsigned epoch;     // set by the launcher: per-call barrier token base
   size_t lds_route;   // set by the launcher
 };
 bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype);
