@@ -531,8 +531,9 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---------------- phase B: down + combine for output rows 8o .. 8o+7, o = b.  Entries:
   // 0 the shared expert (with one), then the touched experts, taken from an LDS counter.
-  // Each wavefront except 0 takes its first entry and starts its weight loads before the
-  // second grid barrier (wavefront 0 polls the barrier and keeps its load queue empty).
+  // Each wavefront except 0 takes its first two entries and starts their weight loads
+  // before the second grid barrier (wavefront 0 polls the barrier and keeps its load queue
+  // empty), so the barrier wait streams weights.
   const int NOct = H / kOct;
   const int oB = blockIdx.x;
   const int NEB = oB < NOct ? nr + (a.has_shared ? 1 : 0) : 0;
@@ -565,13 +566,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return __builtin_amdgcn_readfirstlane(v);
   };
   wait_stores();  // this wavefront's h stores
-  int qb = wave != 0 ? grab_b() : 0;
-  if (wave != 0) dn_load(da, qb);
-  grid_barrier(a.bar, tok0 + 2u);
-  if (wave == 0) {
+  int qb = 0, qb2 = 0;
+  auto first_loads = [&]() {
     qb = grab_b();
+    qb2 = grab_b();
     dn_load(da, qb);
-  }
+    dn_load(db, qb2);
+  };
+  if (wave != 0) first_loads();
+  grid_barrier(a.bar, tok0 + 2u);
+  if (wave == 0) first_loads();
   // (after the barrier the tokens are dead: y and h take the data region)
   float *s_y = reinterpret_cast<float *>(data);  // [T*k][8]
   float *s_ys = s_y + (size_t)n_slots * kOct;   // [T][8]
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_make_buffer_rsrc(a.has_shared ? a.h_s : a.h, 0, (a.has_shared ? T * gs : 0) * 16, 0x00020000);
     const int sh0 = a.has_shared ? T : 0;
     const int nrow = n_slots + sh0;
-    constexpr int kB = 8;
+    constexpr int kB = 12;  // 72 rows of 66 uint4 (T = 8) in one round
     for (int base = tid; base < nrow * hg; base += kB * kNT) {
       i4_t v[kB];
 #pragma unroll
@@ -670,16 +674,17 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     };
-    int q = qb;
+    int q = qb, q2 = qb2;
     while (q < NEB) {
-      const int q2 = grab_b();
-      dn_load(db, q2);
       compute(da, q);
-      if (q2 >= NEB) break;
       const int q3 = grab_b();
       dn_load(da, q3);
+      if (q2 >= NEB) break;
       compute(db, q2);
+      const int q4 = grab_b();
+      dn_load(db, q4);
       q = q3;
+      q2 = q4;
     }
   }
   __syncthreads();
