@@ -23,6 +23,7 @@
 // range of (N-tile major, M-tile minor) work, so the M-tiles of one expert run next
 // to each other on one XCD and share its L2 copy of the expert's weight tile.
 #include <cstdio>
+#include <mutex>
 
 #include "device.h"
 #include "internal.h"
@@ -139,7 +140,9 @@ __global__ __launch_bounds__(NTHR, 2) void grouped_gemm_kernel(GemmArgs a, Route
                                      : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rb_reg[i] = brow[i] != nullptr ? ld_stream(reinterpret_cast<const uint4 *>(brow[i] + boff + kb + 8 * lchunk))
+      // plain (temporal) loads: the expert's other M-tiles, next to this one on the same XCD,
+      // read the same weight tile from L2
+      rb_reg[i] = brow[i] != nullptr ? *reinterpret_cast<const uint4 *>(brow[i] + boff + kb + 8 * lchunk)
                                      : make_uint4(0, 0, 0, 0);
   };
   auto sstore = [&](int buf) {
@@ -240,26 +243,291 @@ __global__ __launch_bounds__(NTHR, 2) void grouped_gemm_kernel(GemmArgs a, Route
 
 static unsigned grid_for(int tiles) { return (unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds); }
 
-hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) {
-  const int MT_r = (int)(a.cap / TM);
-  const int MT_s = a.has_shared ? (a.T + TM - 1) / TM : 0;
-  const int imax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
-  const int NN = imax / (TN / 2);
-  RouterArgs ra{};
-  launch_k(grouped_gemm_kernel<MODE_GATE_UP>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
-                     MT_r, MT_s, NN);
-  return hipGetLastError();
+// ---------------------------------------------------------------- expert-stationary GEMMs
+// Gate/up and down of the prefill chunk.  A block owns one expert (or one 192-token
+// chunk of the shared expert) and one chunk of its output columns, and runs every row
+// of that expert through it (192 rows per pass), so each weight byte is read from HBM
+// once.  The chunks of one expert are neighbours in the XCD-aware order, so the
+// gathered token rows (gate/up) or h rows (down) they all read stay in that XCD's L2.
+//   GATE_UP: B = 128 gate rows + the matching 128 up rows (columns n0 .. n0+127), K = H;
+//            h[position][n0 ..] = bf16(silu(g) * u)
+//   DOWN:    B = 256 rows of W_d (outputs n0 .. n0+255), K = I; y[slot][n0 ..] = bf16(acc)
+// 512 threads = 8 wavefronts, 4 (M) x 2 (N); wavefront (wm, wn) owns the 16-row tiles
+// wm, wm+4, wm+8 of the pass and 8 tiles of 16 columns: 3 x 8 MFMA 16x16x32 bf16.
+// Global memory goes straight to LDS (buffer loads with the LDS target, 16 bytes per
+// lane): no staging registers.  K advances 64 per stage; A has two LDS buffers, B (the
+// weight stream) three.  At stage kt the loads of A(kt+1) and then B(kt+2) are issued, so
+// waiting for A(kt) leaves B(kt+1) in flight (loads complete in issue order): 64 KiB of
+// weights per block stay in flight.  LDS rows are 128 bytes with the 16-byte chunk c of
+// row r stored at chunk c ^ (r & 7) (the loads pick their source so), spreading a
+// fragment's 16 rows over the banks.  Every load is always issued: rows past the segment
+// and stages past the end read zeros from an empty descriptor, so no count depends on a
+// branch; each pass drains its loads before the buffers are reused.
+namespace {
+constexpr int EG_MR = 192;                         // rows per pass
+constexpr int EG_NB = 256;                         // B rows per block
+constexpr int EG_TK = 64;                          // K per stage (one 128-byte LDS row)
+constexpr int EG_NT = 512;
+constexpr int EG_ABUF = EG_MR * EG_TK * 2;         // bytes of one A stage (24 KiB)
+constexpr int EG_BBUF = EG_NB * EG_TK * 2;         // bytes of one B stage (32 KiB)
+constexpr size_t EG_LDS = (size_t)2 * EG_ABUF + 3 * EG_BBUF;  // 144 KiB
+constexpr int kNtPolicy = 2;                       // non-temporal (weights are read once)
+typedef __attribute__((address_space(3))) void lds_void;
+}  // namespace
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) {
-  const int MT_r = (int)(a.cap / TM);
-  const int MT_s = a.has_shared ? (a.T + TM - 1) / TM : 0;
-  const int NN = a.H / TN;
-  RouterArgs ra{};
-  launch_k(grouped_gemm_kernel<MODE_DOWN>, dim3(grid_for((MT_r + MT_s) * NN)), dim3(NTHR), 0, s, a, ra,
-                     MT_r, MT_s, NN);
-  return hipGetLastError();
+template <int MODE>
+__global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH, int NSEG_R, int NSEG_S) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t eg_lds[];
+
+  const int items = (NSEG_R + NSEG_S) * NCH;
+  const int per_xcd = (items + kXcds - 1) / kXcds;
+  const int u = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (u >= items) return;
+  const int seg = u / NCH, ch = u % NCH;
+  const bool routed = seg < NSEG_R;
+  const int n_slots = a.T * a.k;
+  int row0, nrows;  // first sorted position (routed) or token (shared), rows of the segment
+  if (routed) {
+    row0 = a.offsets[seg];
+    nrows = a.offsets[seg + 1] - row0;
+  } else {
+    row0 = (seg - NSEG_R) * EG_MR;
+    nrows = min(EG_MR, a.T - row0);
+  }
+  if (nrows <= 0) return;
+  const int e = routed ? seg : 0;
+  const int Iseg = routed ? a.I : a.I_s;
+  const int K = MODE == MODE_GATE_UP ? a.H : Iseg;
+  const int n0 = MODE == MODE_GATE_UP ? ch * (EG_NB / 2) : ch * EG_NB;
+  if (MODE == MODE_GATE_UP && n0 >= Iseg) return;
+
+  const int lane = lane_id(), wave = wave_id();
+  const int wm = wave & 3, wn = wave >> 2;
+  // load mapping: a wavefront instruction fills 8 LDS rows (1 KiB); lane L writes row
+  // L / 8, physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8)
+  const int lr = lane >> 3, lchunk = (lane & 7) ^ lr;
+
+  // ---- B: the expert's weight rows (one scalar descriptor)
+  const uint16_t *bank;
+  size_t bank_bytes;
+  if (MODE == MODE_GATE_UP) {
+    bank = routed ? a.w_gu + (size_t)e * 2 * a.I * a.H : a.ws_gu;
+    bank_bytes = (size_t)2 * Iseg * a.H * 2;
+  } else {
+    bank = routed ? a.w_d + (size_t)e * a.H * a.I : a.ws_d;
+    bank_bytes = (size_t)a.H * Iseg * 2;
+  }
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bank), 0,
+                                                                      (int)bank_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rNone = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bank), 0, 0, 0x00020000);
+  constexpr int kOff = 0x7FFFFF00;  // a row that reads zeros (past every descriptor)
+  // this lane's source in the B row of instruction i (row group wave + 8 i); columns past
+  // the segment (a partial last chunk) read zeros
+  const int ncols = MODE == MODE_GATE_UP ? Iseg : a.H;
+  int boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (wave + 8 * i) + lr;
+    const int col = MODE == MODE_GATE_UP ? n0 + (r % (EG_NB / 2)) : n0 + r;
+    const int wr = MODE == MODE_GATE_UP ? (r < EG_NB / 2 ? col : Iseg + col) : col;
+    boff[i] = col < ncols ? wr * K * 2 + lchunk * 16 : kOff;
+  }
+  // ---- A: token rows (gate/up) or h rows (down), gathered by the alignment
+  const uint16_t *abase;
+  size_t abytes;
+  if (MODE == MODE_GATE_UP) {
+    abase = a.x;
+    abytes = (size_t)a.T * a.H * 2;
+  } else if (routed) {
+    abase = a.h;
+    abytes = (size_t)a.cap * a.I * 2;
+  } else {
+    abase = a.h_s;
+    abytes = (size_t)a.T * a.I_s * 2;
+  }
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(abase), 0, (int)abytes,
+                                                                      0x00020000);
+
+  // B fragment rows of this wavefront
+  int bfr[8];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) {
+    if (MODE == MODE_GATE_UP) bfr[ni] = ni < 4 ? 64 * wn + 16 * ni : EG_NB / 2 + 64 * wn + 16 * (ni - 4);
+    else bfr[ni] = 128 * wn + 16 * ni;
+  }
+  const int KT = K / EG_TK;
+  const int fr = lane & 15, fq = lane >> 4;  // fragment row, quarter (8 bf16 of K)
+  uint8_t *const ldsA = eg_lds;
+  uint8_t *const ldsB = eg_lds + 2 * EG_ABUF;
+
+  for (int pass0 = 0; pass0 < nrows; pass0 += EG_MR) {
+    const int prow = min(EG_MR, nrows - pass0);
+    int aoff[3];  // this lane's source in the A row of instruction i (row group wave + 8 i)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int r = 8 * (wave + 8 * i) + lr;
+      int off = kOff;
+      if (r < prow) {
+        const int m = row0 + pass0 + r;
+        if (MODE == MODE_GATE_UP) {
+          if (routed) {
+            const int slot = a.sorted[m];
+            if (slot < n_slots) off = (slot / a.k) * a.H * 2;
+          } else {
+            off = m * a.H * 2;
+          }
+        } else {
+          off = m * Iseg * 2;
+        }
+      }
+      aoff[i] = off == kOff ? kOff : off + lchunk * 16;
+    }
+    const int nmt = (prow + 15) / 16;  // 16-row tiles of the pass (zero rows past prow)
+    const bool mv1 = wm + 4 < nmt, mv2 = wm + 8 < nmt;
+
+    f32x4_t acc[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) acc[j][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // (kt is uniform; readfirstlane keeps the stage offset in a scalar register)
+    auto issueA = [&](int kt) {
+      kt = __builtin_amdgcn_readfirstlane(kt);
+      const __amdgpu_buffer_rsrc_t rs = kt < KT ? rA : rNone;
+      uint8_t *buf = ldsA + (kt & 1) * EG_ABUF;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(buf + (wave + 8 * i) * 1024), 16, aoff[i],
+                                                 kt * EG_TK * 2, 0, 0);
+    };
+    auto issueB = [&](int kt) {
+      kt = __builtin_amdgcn_readfirstlane(kt);
+      const __amdgpu_buffer_rsrc_t rs = kt < KT ? rB : rNone;
+      uint8_t *buf = ldsB + (kt % 3) * EG_BBUF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(buf + (wave + 8 * i) * 1024), 16, boff[i],
+                                                 kt * EG_TK * 2, 0, kNtPolicy);
+    };
+    auto mfma_stage = [&](int kt) {
+      const uint8_t *pa = ldsA + (kt & 1) * EG_ABUF;
+      const uint8_t *pb = ldsB + (kt % 3) * EG_BBUF;
+#pragma unroll
+      for (int ks = 0; ks < EG_TK / 32; ++ks) {
+        const int sw = ((ks * 4 + fq) ^ (fr & 7)) * 16;  // swizzled chunk of this lane's 8 bf16
+        bf16x8_t bfm[8], af[3];
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+          bfm[ni] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(pb + (bfr[ni] + fr) * 128 + sw));
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          af[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(pa + ((wm + 4 * j) * 16 + fr) * 128 + sw));
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) acc[0][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], bfm[ni], acc[0][ni], 0, 0, 0);
+        if (mv1) {
+#pragma unroll
+          for (int ni = 0; ni < 8; ++ni) acc[1][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1], bfm[ni], acc[1][ni], 0, 0, 0);
+        }
+        if (mv2) {
+#pragma unroll
+          for (int ni = 0; ni < 8; ++ni) acc[2][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2], bfm[ni], acc[2][ni], 0, 0, 0);
+        }
+      }
+    };
+
+    // in flight at the top of stage kt, in issue order: B(kt), A(kt), B(kt+1)
+    issueB(0);
+    issueA(0);
+    issueB(1);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vm<4>();      // A(kt) and all before it (B(kt)) are in LDS; B(kt+1) may not be
+      // ... for every wavefront; and stage kt-1 is no longer read.  A bare barrier: the
+      // explicit count above is the wait (a fenced one would drain B(kt+1) too)
+      __builtin_amdgcn_s_barrier();
+      issueA(kt + 1);    // into A buffer (kt+1) & 1, which held stage kt-1
+      issueB(kt + 2);    // into B buffer (kt+2) % 3, which held stage kt-1
+      mfma_stage(kt);
+    }
+    wait_vm<0>();        // the loads past the end have landed before the buffers are reused
+    __syncthreads();
+
+    // ---- epilogue: lane holds C[row = 4*(lane/16) + v][col = lane%16] of each 16x16 tile
+    const int crow = 4 * (lane >> 4), ccol = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if ((j == 1 && !mv1) || (j == 2 && !mv2)) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = (wm + 4 * j) * 16 + crow + v;  // row of the pass
+        if (r >= prow) continue;
+        const int m = row0 + pass0 + r;
+        if (MODE == MODE_GATE_UP) {
+          uint16_t *dst = routed ? a.h + (size_t)m * a.I : a.h_s + (size_t)m * a.I_s;
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+            const int col = n0 + 64 * wn + 16 * ni + ccol;
+            const float g = acc[j][ni][v], uu = acc[j][ni + 4][v];
+            if (col < Iseg) dst[col] = to_bf16(g / (1.0f + expf(-g)) * uu);
+          }
+        } else {
+          uint16_t *dst = nullptr;
+          if (routed) {
+            const int slot = a.sorted[m];
+            if (slot < n_slots) dst = a.y + (size_t)slot * a.H;
+          } else {
+            dst = a.y_s + (size_t)m * a.H;
+          }
+          if (dst != nullptr) {
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni)
+              if (n0 + bfr[ni] + ccol < a.H) dst[n0 + bfr[ni] + ccol] = to_bf16(acc[j][ni][v]);
+          }
+        }
+      }
+    }
+  }
 }
+
+namespace {
+template <int MODE>
+hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
+  auto kern = expert_gemm_kernel<MODE>;
+  static std::mutex mu;
+  static bool opened[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!opened[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)EG_LDS);
+      if (e != hipSuccess) return e;
+      opened[dev] = true;
+    }
+  }
+  // the kernel addresses tokens, h and one expert's matrix through 32-bit buffer ranges
+  const int imax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
+  const size_t lim = (size_t)1 << 31;
+  if ((size_t)a.T * a.H * 2 >= lim || (size_t)a.cap * a.I * 2 >= lim || (size_t)2 * imax * a.H * 2 >= lim)
+    return hipErrorInvalidValue;
+  if (a.H % EG_TK != 0 || a.I % EG_TK != 0 || (a.has_shared && a.I_s % EG_TK != 0)) return hipErrorInvalidValue;
+  const int NCH = MODE == MODE_GATE_UP ? (imax + EG_NB / 2 - 1) / (EG_NB / 2) : (a.H + EG_NB - 1) / EG_NB;
+  const int NSEG_S = a.has_shared ? (a.T + EG_MR - 1) / EG_MR : 0;
+  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), EG_LDS, s, a, NCH, a.E, NSEG_S);
+}
+}  // namespace
+
+hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_GATE_UP>(a, s); }
+
+hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_DOWN>(a, s); }
 
 // ---------------------------------------------------------------- router on MFMA
 // Exact three-way split of each fp32 router weight into bf16 parts: hi = rne(w),
@@ -284,8 +552,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
 }
 
 hipError_t launch_router_split(const float *w_r, const float *w_sg, int E, int H, uint16_t *w3, hipStream_t s) {
-  launch_k(router_split_kernel, dim3(512), dim3(256), 0, s, w_r, w_sg, E, H, w3);
-  return hipGetLastError();
+  return launch_k(router_split_kernel, dim3(512), dim3(256), 0, s, w_r, w_sg, E, H, w3);
 }
 
 hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w3, int E, int has_sg,
@@ -298,8 +565,7 @@ hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w
   RouterArgs ra{b_r, logits, gate_logit, E, E + (has_sg ? 1 : 0)};
   const int MT = (T + TM - 1) / TM;
   const int NN = (ra.NRt + TN - 1) / TN;
-  launch_k(grouped_gemm_kernel<MODE_ROUTER>, dim3(grid_for(MT * NN)), dim3(NTHR), 0, s, a, ra, MT, 0, NN);
-  return hipGetLastError();
+  return launch_k(grouped_gemm_kernel<MODE_ROUTER>, dim3(grid_for(MT * NN)), dim3(NTHR), 0, s, a, ra, MT, 0, NN);
 }
 
 // ---------------------------------------------------------------- combine (prefill)
@@ -349,7 +615,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 
 hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
                           int H, int k, uint16_t *out, hipStream_t s) {
-  launch_k(combine_kernel, dim3(T), dim3(256), 0, s, y, y_s, topk_w, gamma, T, H, k, out);
+  return launch_k(combine_kernel, dim3(T), dim3(256), 0, s, y, y_s, topk_w, gamma, T, H, k, out);
   return hipGetLastError();
 }
 

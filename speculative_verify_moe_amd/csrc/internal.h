@@ -143,6 +143,7 @@ struct GemmArgs {
   const uint16_t *w_d;
   const int32_t *sorted;
   const int32_t *block_expert;
+  const int32_t *offsets;  // [E+1] padded expert offsets of the alignment
   int has_shared, I_s;
   const uint16_t *ws_gu;
   const uint16_t *ws_d;
