@@ -26,7 +26,7 @@ import bench  # noqa: E402  (KERNEL_SOURCES, source_hash)
 KERNEL_PATTERNS = {
     "moe_decode_fused": r"moe_decode_fused_kernel",
     "gemv_gate_up": r"gemv_gate_up_kernel",
-    "gemm_gate_up_mfma": r"grouped_gemm_kernel<0",
+    "gemm_gate_up_mfma": r"expert_gemm_kernel<0",
 }
 COPY_PATTERN = r"copy"
 
