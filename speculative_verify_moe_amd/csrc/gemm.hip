@@ -5,23 +5,21 @@
 // expert sees ~T*k/E tokens (128 at 4096 tokens, 256 experts, top-8), so the
 // per-expert contraction is a real GEMM and runs on the matrix cores.
 //
-// One kernel template covers three contractions C[64 x 128] = A[64 x K] . B[128 x K]^T:
-//   GATE_UP  A = x rows gathered through the alignment (a 64-row M-tile is one BM=64
-//            block, so it belongs to one expert), B = 64 gate rows + the matching 64
-//            up rows of that expert; epilogue h = bf16(silu(g) * u), stored by
-//            sorted position.  The shared expert is one more segment of M-tiles over
-//            the T tokens in order.
-//   DOWN     A = h rows (sorted position), B = 128 rows of W_d; epilogue y = bf16(acc)
-//            stored by slot (t*k + j), so the combine reads a token's k rows together.
-//   ROUTER   A = x, B = the fp32 router rows split exactly into three bf16 parts
-//            (w = hi + mid + lo), K = 3H: fp32 logits from bf16 products.
-// Tiles: 256 threads = 4 wavefronts in 2x2, each 32 x 64 of C as 2 x 4 MFMA
-// 16x16x32 bf16 tiles, fp32 accumulators.  K advances 64 per stage through a double
-// LDS buffer (rows padded by 16 bytes), one barrier per stage, next stage's global
-// loads in flight during the current stage's MFMAs.
-// Tile order: a block's linear id L runs on XCD L % 8; each XCD takes a contiguous
-// range of (N-tile major, M-tile minor) work, so the M-tiles of one expert run next
-// to each other on one XCD and share its L2 copy of the expert's weight tile.
+// Two kernel families:
+//   expert_gemm_kernel (below, "expert-stationary GEMMs"): gate/up with the SiLU*up
+//            epilogue and the down projection; a block owns one expert and a chunk of
+//            its output columns, so every weight byte is read from HBM once.
+//   grouped_gemm_kernel<ROUTER>: C[64 x 128] = A[64 x K] . B[128 x K]^T with A = x and
+//            B = the fp32 router rows split exactly into three bf16 parts
+//            (w = hi + mid + lo), K = 3H: fp32 logits from bf16 products.  (Its GATE_UP
+//            and DOWN branches are the earlier tile-per-block form of those
+//            contractions; no launch instantiates them.)
+// grouped_gemm_kernel tiles: 256 threads = 4 wavefronts in 2x2, each 32 x 64 of C as
+// 2 x 4 MFMA 16x16x32 bf16 tiles, fp32 accumulators.  K advances 64 per stage through
+// a double LDS buffer (rows padded by 16 bytes), one barrier per stage, next stage's
+// global loads in flight during the current stage's MFMAs.  Tile order: a block's
+// linear id L runs on XCD L % 8; each XCD takes a contiguous range of (N-tile major,
+// M-tile minor) work.
 #include <cstdio>
 #include <mutex>
 

@@ -304,3 +304,41 @@ def test_alternating_inputs_on_one_workspace():
         torch.cuda.synchronize()
         for i, o in enumerate(outs):
             assert np.array_equal(G.bf16_bits(o), ref_a if i % 2 == 0 else ref_b), f"{recipe} call {i}"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("recipe,T", [("qwen36_a3b", 8), ("flash_next_fp8", 6), ("qwen36_a3b", 32), ("prefill", 200)])
+def test_graph_replays_equal_eager(recipe, T):
+    """A layer call captured in a HIP graph: every replay (inputs changed in place between
+    replays, eager calls on the same workspace in between) equals the eager result bitwise.
+    The fused kernel's barrier tokens continue from the workspace, so replays need no reset."""
+    from speculative_verify_moe_amd import moe_layer_forward, moe_layer_workspace_size
+    cfg = configs.CONFIGS[recipe]
+    L = G.host_layer(cfg)
+    D = G.device_layer(L)
+    xa = G.to_dev_bf16(configs.make_tokens(cfg, T, replica=1))
+    xb = G.to_dev_bf16(configs.make_tokens(cfg, T, replica=2))
+    ws = torch.zeros((moe_layer_workspace_size(T, D),), dtype=torch.uint8, device="cuda")
+    ref_a = G.bf16_bits(moe_layer_forward(xa, D, ws=ws))
+    ref_b = G.bf16_bits(moe_layer_forward(xb, D, ws=ws))
+    x_static = xa.clone()
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first use on this stream outside the capture
+        moe_layer_forward(x_static, D, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe_layer_forward(x_static, D, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(6):
+        x_static.copy_(xa if i % 2 == 0 else xb)
+        g.replay()
+        torch.cuda.synchronize()
+        got = G.bf16_bits(out)
+        assert np.array_equal(got, ref_a if i % 2 == 0 else ref_b), f"{recipe} T={T} replay {i}"
+        eager = G.bf16_bits(moe_layer_forward(xb, D, ws=ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(eager, ref_b), f"{recipe} T={T} eager call after replay {i}"
