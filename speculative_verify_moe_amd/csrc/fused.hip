@@ -9,9 +9,8 @@
 // One block per CU (8 wavefronts); the grid never exceeds what the device holds resident
 // at once, so every block runs concurrently and the grid-wide barriers complete.  Four
 // phases separated by two barriers:
-//   0  tokens staged in LDS; wavefronts 0..6 of block b own router rows (row n on block
-//      n % NB, wavefront n / NB); wavefront 7 meanwhile loads the shared expert's gate/up
-//      rows it will need first in phase A.                               -- grid sync
+//   0  tokens staged in LDS; router row n runs on block n % NB, its tokens spread over
+//      the block's wavefronts.                                           -- grid sync
 //   1  every block routes all T tokens itself from the logits (top-k per wavefront,
 //      histogram, scans, stable slot lists in LDS): no launch, no second sync.  Block 0
 //      also writes the routing and the padded alignment to global memory.
@@ -134,6 +133,14 @@ __device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
   __syncthreads();
 }
 
+// Block barrier for LDS data only: waits for this wavefront's LDS operations but not for
+// its vector memory operations, so loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int ESZ, int CGU, int CGD, int CR>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void moe_decode_fused_kernel(FusedArgs a) {
   static_assert(16 * CGU * (16 / ESZ) == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
@@ -155,9 +162,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int *s_stok = s_slots + n_slots;                                // [T*k] their tokens
   float *s_gamma = reinterpret_cast<float *>(s_stok + n_slots);   // [64]
   int *s_cnt = reinterpret_cast<int *>(s_gamma + kDecodeMaxT);    // [E]
-  int *s_cs = s_cnt + E;                                          // [E+1]
-  int *s_fl = s_cs + E + 1;                                       // [E+1]
-  int *s_e = s_fl + E + 1;                                        // [E]
+  int *s_qs = s_cnt + E;                                          // [E] first position of an expert's slots
+  int *s_e = s_qs + E;                                            // [E]
   int *s_start = s_e + E;                                         // [E+1]
   int *s_off = s_start + E + 1;                                   // [E+1] padded offsets
   unsigned *s_mlo = reinterpret_cast<unsigned *>(s_off + E + 1);  // [E] tokens 0..31 per expert
@@ -172,22 +178,30 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---------------- phase 0: router rows, shared-expert prefetch, tokens to LDS
   const int NR = E + (a.w_sg != nullptr ? 1 : 0);
-  const int my_row = wave * NB + blockIdx.x;  // rows beyond kNW * NB: more passes
-  float4 wr[CR];
-  auto load_router_row = [&](int n) {
+  // Router row n runs on block n % NB; every wavefront of the block holds the row (the
+  // block's 8 loads of it share the CU's caches) and takes the tokens wave, wave + 8, ...,
+  // so each token's dot product is one short chain.  The block's first kRR rows and their
+  // biases are loaded before the tokens are staged.
+  constexpr int kRR = 3;
+  float4 wr[kRR][CR];
+  float bias[kRR];
+  auto load_router_row = [&](float4(&w)[CR], float &b, int n) {
+    b = (n < E && a.b_r != nullptr) ? a.b_r[n] : 0.0f;
     const float4 *row = reinterpret_cast<const float4 *>(n < E ? a.w_r + (size_t)n * H : a.w_sg);
 #pragma unroll
     for (int c = 0; c < CR; ++c) {
       const int g = lane + kWave * c;
       if (g < H / 4) {
         const uint4 u = ld_stream(reinterpret_cast<const uint4 *>(row + g));
-        wr[c] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+        w[c] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
       } else {
-        wr[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+        w[c] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
-  if (my_row < NR) load_router_row(my_row);
+#pragma unroll
+  for (int r = 0; r < kRR; ++r)
+    if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
 
   // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
   const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
@@ -250,42 +264,34 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
 
-  auto router_rows = [&](int n) {
-    const float bias = (n < E && a.b_r != nullptr) ? a.b_r[n] : 0.0f;
+  // per lane: the column groups in order, four products each, one accumulation chain;
+  // then the wavefront sum (the same order as the router kernel of the four-kernel path)
+  auto router_row = [&](const float4(&w)[CR], float b, int n) {
     const uint2 *x2 = reinterpret_cast<const uint2 *>(xs);
-    for (int t0 = 0; t0 < T; t0 += 4) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int t = wave; t < T; t += kNW) {
+      float acc = 0.0f;
 #pragma unroll
       for (int c = 0; c < CR; ++c) {
         const int g = min(lane + kWave * c, H / 4);  // H / 4: the zero pad (zero weights too)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 xv = x2[min(t0 + j, T - 1) * (2 * xg) + g];  // rows past T: not stored
-          float s = acc[j];
-          s = fmaf(wr[c].x, bf16_lo(xv.x), s);
-          s = fmaf(wr[c].y, bf16_hi(xv.x), s);
-          s = fmaf(wr[c].z, bf16_lo(xv.y), s);
-          s = fmaf(wr[c].w, bf16_hi(xv.y), s);
-          acc[j] = s;
-        }
+        const uint2 xv = x2[t * (2 * xg) + g];
+        acc = fmaf(w[c].x, bf16_lo(xv.x), acc);
+        acc = fmaf(w[c].y, bf16_hi(xv.x), acc);
+        acc = fmaf(w[c].z, bf16_lo(xv.y), acc);
+        acc = fmaf(w[c].w, bf16_hi(xv.y), acc);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (t0 + j < T) {
-          const float v = wave_sum(acc[j]);
-          if (lane == 0) {
-            float *dst = n < E ? a.logits + (size_t)(t0 + j) * E + n : a.gate_logit + t0 + j;
-            __hip_atomic_store(dst, n < E ? v + bias : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
+      const float v = wave_sum(acc);
+      if (lane == 0) {
+        float *dst = n < E ? a.logits + (size_t)t * E + n : a.gate_logit + t;
+        __hip_atomic_store(dst, n < E ? v + b : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };
-  if (my_row < NR) router_rows(my_row);
-  // rows beyond the first pass (E + 1 > kNW * NB): strided passes
-  for (int n = my_row + kNW * NB; n < NR; n += kNW * NB) {
-    load_router_row(n);
-    router_rows(n);
+#pragma unroll
+  for (int r = 0; r < kRR; ++r)
+    if (blockIdx.x + r * NB < NR) router_row(wr[r], bias[r], blockIdx.x + r * NB);
+  for (int n = blockIdx.x + kRR * NB; n < NR; n += NB) {  // E + 1 > kRR * NB: the rest
+    load_router_row(wr[0], bias[0], n);
+    router_row(wr[0], bias[0], n);
   }
   wait_stores();  // the router rows' logit stores
   grid_barrier(a.bar, tok0 + 1u);
@@ -313,108 +319,57 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s_gamma[tid] = 1.0f / (1.0f + expf(-z));
     }
     __syncthreads();
-    // block scan over the experts (thread tid owns experts per*tid .. per*tid+per-1) of two
-    // packed words: touched flag | slot count << 16, and the padded slot count
-    const int BM = a.BM;
-    {
-      const int per = (E + kNT - 1) / kNT;  // 1 or 2
-      const int e0 = tid * per;
-      auto word_a = [](int c) -> uint32_t { return (c > 0 ? 1u : 0u) | ((uint32_t)c << 16); };
-      auto word_b = [&](int c) -> uint32_t { return (uint32_t)((c + BM - 1) / BM * BM); };
-      uint32_t va = 0, vb = 0;
-      for (int u = 0; u < per; ++u) {
-        const int e = e0 + u;
-        if (e < E) {
-          const int c = __popc(s_mlo[e]) + __popc(s_mhi[e]);
-          s_cnt[e] = c;
-          va += word_a(c);
-          vb += word_b(c);
+    // The entries (touched experts) in order of first use: slot i = t*k + j opens one when
+    // no earlier token chose its expert.  Entry q's slots, in token order, take positions
+    // s_start[q] .. s_start[q+1] of s_slots / s_stok.  One wavefront, 64 slots a step:
+    // ballots number the entries, a scan over the opening slots places them.  (The order
+    // of entries changes no result: every h row and y row depends on its own slot only.)
+    if (wave == 0) {
+      int nq = 0, pos = 0;
+      for (int c0 = 0; c0 < n_slots; c0 += kWave) {
+        const int i = c0 + lane;
+        const bool v = i < n_slots;
+        const int e = v ? s_ids[i] : 0;
+        const int t = min(i / k, kWave - 1);
+        const uint64_t m = ((uint64_t)s_mhi[e] << 32) | s_mlo[e];
+        const bool first = v && (m & ((1ull << t) - 1ull)) == 0;
+        const uint64_t fb = __ballot(first);
+        const uint32_t cf = first ? (uint32_t)__popcll(m) : 0u;
+        const uint32_t incl = wave_incl_scan_u32(cf);
+        if (first) {
+          const int q = nq + (int)__popcll(fb & ((1ull << lane) - 1ull));
+          const int st = pos + (int)(incl - cf);
+          s_e[q] = e;
+          s_start[q] = st;
+          s_qs[e] = st;
+        }
+        nq += (int)__popcll(fb);
+        pos += __builtin_amdgcn_readlane((int)incl, kWave - 1);
+      }
+      for (int c0 = 0; c0 < n_slots; c0 += kWave) {
+        const int i = c0 + lane;
+        if (i < n_slots) {
+          const int e = s_ids[i], t = i / k;
+          const uint64_t m = ((uint64_t)s_mhi[e] << 32) | s_mlo[e];
+          const int p = s_qs[e] + (int)__popcll(m & ((1ull << t) - 1ull));
+          s_slots[p] = i;
+          s_stok[p] = t;
         }
       }
-      const uint32_t ia = wave_incl_scan_u32(va), ib = wave_incl_scan_u32(vb);
-      if (lane == kWave - 1) {
-        s_wsum[2 * wave] = ia;
-        s_wsum[2 * wave + 1] = ib;
-      }
-      __syncthreads();
-      uint32_t ra = ia - va, rb = ib - vb;
-      for (int w = 0; w < wave; ++w) {
-        ra += s_wsum[2 * w];
-        rb += s_wsum[2 * w + 1];
-      }
-      for (int u = 0; u < per; ++u) {
-        const int e = e0 + u;
-        if (e < E) {
-          s_fl[e] = (int)(ra & 0xFFFFu);
-          s_cs[e] = (int)(ra >> 16);
-          s_off[e] = (int)rb;
-          ra += word_a(s_cnt[e]);
-          rb += word_b(s_cnt[e]);
-        }
-      }
-      if (tid == kNT - 1) {
-        s_fl[E] = (int)(ra & 0xFFFFu);
-        s_cs[E] = (int)(ra >> 16);
-        s_off[E] = (int)rb;
+      if (lane == 0) {
+        s_start[nq] = n_slots;
+        s_nt = nq;
+        s_qa = 0;
+        s_qb = 0;
       }
     }
     __syncthreads();
-    const int nt = s_fl[E];
-    for (int e = tid; e < E; e += kNT) {
-      if (s_cnt[e] > 0) {
-        s_e[s_fl[e]] = e;
-        s_start[s_fl[e]] = s_cs[e];
-      }
-    }
-    if (tid == 0) {
-      s_start[nt] = n_slots;
-      s_nt = nt;
-      s_qa = 0;
-      s_qb = 0;
-    }
-    for (int i = tid; i < n_slots; i += kNT) {
-      const int t = i / k, e = s_ids[i];
-      const unsigned lo = s_mlo[e], hi = s_mhi[e];
-      const int r = t < 32 ? __popc(lo & ((1u << t) - 1u)) : __popc(lo) + __popc(hi & ((1u << (t - 32)) - 1u));
-      s_slots[s_cs[e] + r] = i;
-      s_stok[s_cs[e] + r] = t;
-    }
-    __syncthreads();
-    // the routing and the padded alignment for the caller, spread over the blocks: any
-    // position p of the padded list follows from the padded scan and the slot lists
-    {
-      const int NBk = gridDim.x, b = blockIdx.x;
-      for (int i = b * kNT + tid; i < n_slots; i += NBk * kNT) {
-        a.ids[i] = s_ids[i];
-        a.topw[i] = s_topw[i];
-      }
-      if (a.has_shared && b == NBk - 1 && tid < T) a.gamma[tid] = s_gamma[tid];
-      const int total = s_off[E];
-      for (int e = b * kNT + tid; e <= E; e += NBk * kNT) {
-        if (e < E) a.al.counts[e] = s_cnt[e];
-        a.al.offsets[e] = s_off[e];
-      }
-      if (b == 0 && tid == 0) a.al.num_padded[0] = total;
-      for (int p = b * kNT + tid; p < a.cap; p += NBk * kNT) {
-        int v = n_slots;
-        if (p < total) {
-          const int e = segment_of(s_off, E, p);
-          const int r = p - s_off[e];
-          if (r < s_cnt[e]) v = s_slots[s_cs[e] + r];
-        }
-        a.al.sorted[p] = v;
-      }
-      for (int bb = b * kNT + tid; bb < a.cap / BM; bb += NBk * kNT) {
-        const int p = bb * BM;
-        a.al.block_expert[bb] = p < total ? segment_of(s_off, E, p) : -1;
-      }
-    }
   }
   const int nr = s_nt;
 
   // ---------------- phase A: gate/up of row pair p = b (2b, 2b+1 and I+2b, I+2b+1) for
   // every entry: entry 0 is the shared expert when this pair has one, then the touched
-  // experts in ascending order.  The wavefronts take entries from an LDS counter, two in
+  // experts in order of first use.  The wavefronts take entries from an LDS counter, two in
   // flight each.
   const int pA = blockIdx.x;
   const bool shA = a.has_shared && 2 * pA < a.I_s;
@@ -537,7 +492,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int NOct = H / kOct;
   const int oB = blockIdx.x;
   const int NEB = oB < NOct ? nr + (a.has_shared ? 1 : 0) : 0;
-  uint4 da[2][CGD], db[2][CGD];
+  uint4 da[2][CGD], db[2][CGD], dc[2][CGD], dd[2][CGD];
   // the lane's byte offsets in a down matrix for output rows 8o+rg and 8o+4+rg (row length
   // I or I_s): fixed for the whole phase, computed once
   const int dv_r0 = (kOct * oB + rg) * a.I * ESZ + l16 * 16, dv_r1 = dv_r0 + 4 * a.I * ESZ;
@@ -566,54 +521,113 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return __builtin_amdgcn_readfirstlane(v);
   };
   wait_stores();  // this wavefront's h stores
-  int qb = 0, qb2 = 0;
-  auto first_loads = [&]() {
-    qb = grab_b();
+  // Four entries in flight per wavefront.  Wavefronts 1..7 issue the first two before the
+  // barrier (wavefront 0 polls it and keeps its load queue empty), so the barrier wait
+  // streams weights.  After the barrier the h loads go first and the other two entries'
+  // weights right behind them: loads return in issue order, so h is not held up by them,
+  // and the weight stream continues while h is staged.
+  int qb1 = 0, qb2 = 0, qb3 = 0, qb4 = 0;
+  const bool early = wave != 0;
+  if (early) {
+    qb1 = grab_b();
     qb2 = grab_b();
-    dn_load(da, qb);
+    dn_load(da, qb1);
     dn_load(db, qb2);
-  };
-  if (wave != 0) first_loads();
+  }
   grid_barrier(a.bar, tok0 + 2u);
-  if (wave == 0) first_loads();
   // (after the barrier the tokens are dead: y and h take the data region)
   float *s_y = reinterpret_cast<float *>(data);  // [T*k][8]
   float *s_ys = s_y + (size_t)n_slots * kOct;   // [T][8]
   // h rows in LDS, hg uint4 each ending in the zero pad: row r < T*k is position r of the
   // slots grouped by expert, row T*k + t the shared expert's token t.  h crosses the barrier:
-  // 16-byte loads with the sc1 cache policy (coherent across the XCDs' L2s).
+  // 16-byte loads with the sc1 cache policy (coherent across the XCDs' L2s).  A block with
+  // no rows in this phase reads from empty descriptors (zeros, no traffic), so every
+  // wavefront issues the same loads.
   uint4 *hl = reinterpret_cast<uint4 *>(data + al16((size_t)(n_slots + T) * kOct * 4));
-  if (NEB > 0) {
+  {
     constexpr int kSc1 = 16;
     const int gr = a.I / 8, gs = a.I_s / 8;
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, n_slots * gr * 16, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(a.has_shared ? a.h_s : a.h, 0, (a.has_shared ? T * gs : 0) * 16, 0x00020000);
+    const bool any = NEB > 0;
+    // one descriptor for h and h_s (h_s lies after h, checked by the launcher): a per-lane
+    // choice between two descriptors would become a loop over them
+    const int dsh = a.has_shared ? (int)((const char *)a.h_s - (const char *)a.h) : 0;
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        a.h, 0, any ? (a.has_shared ? dsh + T * gs * 16 : n_slots * gr * 16) : 0, 0x00020000);
     const int sh0 = a.has_shared ? T : 0;
     const int nrow = n_slots + sh0;
     constexpr int kB = 12;  // 72 rows of 66 uint4 (T = 8) in one round
-    for (int base = tid; base < nrow * hg; base += kB * kNT) {
-      i4_t v[kB];
+    i4_t v[kB];
+    // offsets first (every slot-list read in flight together), then the loads; a lane past
+    // the rows reads past the buffer, which returns zeros
+    auto stage_load = [&](int base) {
+      int off[kB];
 #pragma unroll
       for (int jj = 0; jj < kB; ++jj) {
         const int idx = base + jj * kNT, r = idx / hg, g = idx - r * hg;
         const bool shr = r >= n_slots;  // rows n_slots.. : the shared expert
+        const int sl = s_slots[min(r, n_slots - 1)];
         const bool ok = idx < nrow * hg && g < (shr ? gs : gr);
-        const int off = ok ? (shr ? (r - n_slots) * gs + g : s_slots[r] * gr + g) * 16 : 0;
-        if (shr) v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1);
-        else v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, kSc1);
-        if (!ok) v[jj] = i4_t{0, 0, 0, 0};
+        off[jj] = ok ? (shr ? dsh + ((r - n_slots) * gs + g) * 16 : (sl * gr + g) * 16) : 0x7FFFFFF0;
       }
+#pragma unroll
+      for (int jj = 0; jj < kB; ++jj) v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rh, off[jj], 0, kSc1);
+    };
+    auto stage_store = [&](int base) {
 #pragma unroll
       for (int jj = 0; jj < kB; ++jj) {
         const int idx = base + jj * kNT;
         if (idx < nrow * hg) hl[idx] = make_uint4(v[jj].x, v[jj].y, v[jj].z, v[jj].w);
       }
+    };
+    stage_load(tid);
+    if (!early) {
+      qb1 = grab_b();
+      qb2 = grab_b();
+      dn_load(da, qb1);
+      dn_load(db, qb2);
+    }
+    qb3 = grab_b();
+    qb4 = grab_b();
+    dn_load(dc, qb3);
+    dn_load(dd, qb4);
+    // while those loads are in flight: the padded counts and their block-wide scan for the
+    // caller's alignment (LDS only, so bare barriers)
+    {
+      const int BM = a.BM;
+      const int per = (E + kNT - 1) / kNT;
+      const int e0 = tid * per;
+      uint32_t vb = 0;
+      for (int u = 0; u < per; ++u) {
+        const int e = e0 + u;
+        if (e < E) {
+          const int c = __popc(s_mlo[e]) + __popc(s_mhi[e]);
+          s_cnt[e] = c;
+          vb += (uint32_t)((c + BM - 1) / BM * BM);
+        }
+      }
+      const uint32_t ib = wave_incl_scan_u32(vb);
+      if (lane == kWave - 1) s_wsum[wave] = ib;
+      lds_barrier();
+      uint32_t rb = ib - vb;
+      for (int w = 0; w < wave; ++w) rb += s_wsum[w];
+      for (int u = 0; u < per; ++u) {
+        const int e = e0 + u;
+        if (e < E) {
+          s_off[e] = (int)rb;
+          rb += (uint32_t)((s_cnt[e] + BM - 1) / BM * BM);
+        }
+      }
+      if (tid == kNT - 1) s_off[E] = (int)rb;
+    }
+    stage_store(tid);
+    for (int base = tid + kB * kNT; base < nrow * hg; base += kB * kNT) {  // larger blocks
+      stage_load(base);
+      stage_store(base);
     }
   }
-  __syncthreads();
+  lds_barrier();  // h staged; the weight loads stay in flight
   {
-    // ---- entries from the LDS counter, two in flight per wavefront
+    // ---- entries from the LDS counter, four in flight per wavefront
     auto compute = [&](uint4(&w)[2][CGD], int q) {
       const bool shared = a.has_shared && q == 0;
       const int ri = q - (a.has_shared ? 1 : 0);
@@ -674,17 +688,24 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     };
-    int q = qb, q2 = qb2;
-    while (q < NEB) {
-      compute(da, q);
-      const int q3 = grab_b();
-      dn_load(da, q3);
+    // entries are grabbed in increasing order, so the first one past the end ends the loop
+    int q1 = qb1, q2 = qb2, q3 = qb3, q4 = qb4;
+    while (q1 < NEB) {
+      compute(da, q1);
+      q1 = grab_b();
+      dn_load(da, q1);
       if (q2 >= NEB) break;
       compute(db, q2);
-      const int q4 = grab_b();
-      dn_load(db, q4);
-      q = q3;
-      q2 = q4;
+      q2 = grab_b();
+      dn_load(db, q2);
+      if (q3 >= NEB) break;
+      compute(dc, q3);
+      q3 = grab_b();
+      dn_load(dc, q3);
+      if (q4 >= NEB) break;
+      compute(dd, q4);
+      q4 = grab_b();
+      dn_load(dd, q4);
     }
   }
   __syncthreads();
@@ -697,6 +718,35 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       a.out[(size_t)t * H + kOct * oB + rr] = to_bf16(acc);
     }
   }
+  // the routing and the padded alignment for the caller, spread over the blocks: any
+  // position p of the padded list follows from the padded scan and the slot lists
+  {
+    const int NBk = gridDim.x, b = blockIdx.x, BM = a.BM;
+    for (int i = b * kNT + tid; i < n_slots; i += NBk * kNT) {
+      a.ids[i] = s_ids[i];
+      a.topw[i] = s_topw[i];
+    }
+    if (a.has_shared && b == NBk - 1 && tid < T) a.gamma[tid] = s_gamma[tid];
+    const int total = s_off[E];
+    for (int e = b * kNT + tid; e <= E; e += NBk * kNT) {
+      if (e < E) a.al.counts[e] = s_cnt[e];
+      a.al.offsets[e] = s_off[e];
+    }
+    if (b == 0 && tid == 0) a.al.num_padded[0] = total;
+    for (int p = b * kNT + tid; p < a.cap; p += NBk * kNT) {
+      int v = n_slots;
+      if (p < total) {
+        const int e = segment_of(s_off, E, p);
+        const int r = p - s_off[e];
+        if (r < s_cnt[e]) v = s_slots[s_qs[e] + r];
+      }
+      a.al.sorted[p] = v;
+    }
+    for (int bb = b * kNT + tid; bb < a.cap / BM; bb += NBk * kNT) {
+      const int p = bb * BM;
+      a.al.block_expert[bb] = p < total ? segment_of(s_off, E, p) : -1;
+    }
+  }
 }
 
 // ============================================================ host side
@@ -705,7 +755,7 @@ constexpr size_t kFusedLdsMax = 156 * 1024;
 
 size_t route_bytes(int T, int k, int E) {
   const size_t n = (size_t)T * k;
-  return al16((4 * n + kDecodeMaxT + 8 * (size_t)E + 4) * 4);
+  return al16((4 * n + kDecodeMaxT + 7 * (size_t)E + 3) * 4);
 }
 }  // namespace
 
@@ -797,6 +847,12 @@ static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *n
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {
   const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared);
   if (lds > kFusedLdsMax) return hipErrorInvalidValue;
+  // phase B reads h and h_s through one buffer descriptor based at h
+  if (a.has_shared) {
+    const ptrdiff_t d = (const char *)a.h_s - (const char *)a.h;
+    if (d < (ptrdiff_t)a.T * a.k * a.I * 2 || d + (ptrdiff_t)a.T * a.I_s * 2 >= ((ptrdiff_t)1 << 31))
+      return hipErrorInvalidValue;
+  }
   a.lds_route = route_bytes(a.T, a.k, a.E);
   int nb = 0;
   hipError_t e;

@@ -49,15 +49,15 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, in
   // the lane's best candidate: the largest code, the lowest slot among equal codes
   uint32_t bc = 0;
   int bs = -1;
+  // (selects, no branches: every lane runs it every round, only the winner's changes)
   auto lane_best = [&]() {
     bc = 0;
     bs = -1;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      if (((alive >> i) & 1u) && (bs < 0 || code[i] > bc)) {
-        bc = code[i];
-        bs = i;
-      }
+      const bool take = ((alive >> i) & 1u) != 0 && (bs < 0 || code[i] > bc);
+      bc = take ? code[i] : bc;
+      bs = take ? i : bs;
     }
   };
   lane_best();
@@ -77,14 +77,10 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, in
     }
     const float v = rank_value(m);
     if (j == 0) top = v;
-    if (lane == j) {
-      my_e = win;
-      my_v = v;
-    }
-    if (lane == (win & (kWave - 1))) {
-      alive &= ~(1u << (win / kWave));
-      lane_best();
-    }
+    my_e = lane == j ? win : my_e;
+    my_v = lane == j ? v : my_v;
+    alive = lane == (win & (kWave - 1)) ? alive & ~(1u << (win / kWave)) : alive;
+    lane_best();
   }
   const float ex = lane < k ? expf(my_v - top) : 0.0f;
   float denom;
