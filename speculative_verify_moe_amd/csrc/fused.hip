@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Router row n runs on block n % NB; every wavefront of the block holds the row (the
   // block's 8 loads of it share the CU's caches) and takes the tokens wave, wave + 8, ...,
   // so each token's dot product is one short chain.  The block's first kRR rows and their
-  // biases are loaded before the tokens are staged.
+  // biases are loaded while the tokens are staged.
   constexpr int kRR = 3;
   float4 wr[kRR][CR];
   float bias[kRR];
@@ -199,9 +199,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-#pragma unroll
-  for (int r = 0; r < kRR; ++r)
-    if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
 
   // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
   const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
@@ -238,23 +235,36 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // tokens to LDS, in rows of xg uint4 ending in the zero pad; unguarded (clamped) loads,
-  // so they are in flight together
+  // so they are in flight together.  The first round's token loads go out before the
+  // router rows (the tokens are few and usually cached, the router rows come from HBM):
+  // loads return in issue order, so the staging does not wait for the router.
   uint4 *sx = reinterpret_cast<uint4 *>(data);
   {
     constexpr int kStep = kNT, kB = 8;
     const uint4 *gx = reinterpret_cast<const uint4 *>(a.x);
     const int n16 = T * xg, last = T * G8 - 1;
-    for (int base = tid; base < n16; base += kB * kStep) {
-      uint4 v[kB];
+    uint4 v[kB];
+    auto x_load = [&](int base) {
 #pragma unroll
       for (int j = 0; j < kB; ++j) {
         const int i = base + j * kStep, t = i / xg, g = i - t * xg;
         v[j] = gx[min(t * G8 + g, last)];
         if (g >= G8) v[j] = make_uint4(0, 0, 0, 0);
       }
+    };
+    auto x_store = [&](int base) {
 #pragma unroll
       for (int j = 0; j < kB; ++j)
         if (base + j * kStep < n16) sx[base + j * kStep] = v[j];
+    };
+    x_load(tid);
+#pragma unroll
+    for (int r = 0; r < kRR; ++r)
+      if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
+    x_store(tid);
+    for (int base = tid + kB * kStep; base < n16; base += kB * kStep) {
+      x_load(base);
+      x_store(base);
     }
   }
   const uint4 *xs = sx;
