@@ -38,7 +38,7 @@ WORKLOADS = {
 
 FUSED_STAGES = ["moe_decode_fused"]
 DECODE_STAGES = ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"]
-PREFILL_STAGES = ["router_split", "router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
+PREFILL_STAGES = ["router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
                   "combine"]
 
 
@@ -229,7 +229,7 @@ def main():
 
     # dominant kernel: the fused layer kernel, the gate/up expert stream (four-kernel decode) or
     # the gate/up MFMA GEMM (prefill)
-    dom = 0 if fused else (4 if prefill else 2)
+    dom = 0 if fused else (stages.index("gemm_gate_up_mfma") if prefill else stages.index("gemv_gate_up"))
     dom_name = stages[dom]
     dom_ms = stage_ms[:, dom]
     src_hash = source_hash(KERNEL_SOURCES[dom_name])

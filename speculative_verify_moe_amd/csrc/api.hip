@@ -135,7 +135,7 @@ struct LayerPlan {
   int BM = 16;
   int64_t cap = 0;
   size_t off_logits, off_gate, off_ids, off_w, off_gamma, off_counts, off_offsets, off_np, off_sorted, off_bexp;
-  size_t off_h, off_hs, off_w3, off_hist, off_y, off_ys, off_tl, off_bar;
+  size_t off_h, off_hs, off_hist, off_y, off_ys, off_tl, off_bar;
   size_t total = 0;
 };
 
@@ -172,9 +172,8 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     p.off_hs = take((size_t)T * I_s * 2);
     p.off_tl = take(touched_ints(E, n) * 4);
     p.off_bar = take((size_t)kBarrierWords * 4);
-    p.off_w3 = p.off_hist = p.off_y = p.off_ys = 0;
+    p.off_hist = p.off_y = p.off_ys = 0;
   } else {
-    p.off_w3 = take((size_t)3 * (E + 1) * H * 2);
     p.off_hist = take(align_hist_ints(n, E) * 4);
     p.off_h = take((size_t)p.cap * I * 2);
     p.off_hs = take((size_t)T * I_s * 2);
@@ -430,9 +429,9 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
              T, E, k, p.BM, (long long)p.cap, p.total, (E + (L->shared.num_experts > 0 ? 1 : 0) + 3) / 4);
   } else {
     snprintf(g_plan, sizeof(g_plan),
-             "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_split; 1 router_gemm_mfma; "
-             "2 topk; 3 align (align_hist, align_colscan, align_offsets, align_scatter); 4 gemm_gate_up_mfma; "
-             "5 gemm_down_mfma; 6 combine",
+             "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_gemm_mfma; "
+             "1 topk; 2 align (align_hist, align_colscan, align_offsets, align_scatter); 3 gemm_gate_up_mfma; "
+             "4 gemm_down_mfma; 5 combine",
              T, E, k, p.BM, (long long)p.cap, p.total);
   }
   return g_plan;
@@ -555,14 +554,9 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   }
 
   // prefill chunk
-  uint16_t *w3 = (uint16_t *)(base + p.off_w3);
   sg.begin();
-  if ((st = launched(launch_router_split(L->router_w, shared ? L->shared_gate_w : nullptr, E, H, w3, s),
-                     "router_split")) != MOE_OK)
-    return st;
-  sg.end();
-  sg.begin();
-  if ((st = launched(launch_router_gemm(x, T, H, w3, E, shared ? 1 : 0, L->router_b, logits, gate, s),
+  if ((st = launched(launch_router_gemm(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
+                                        logits, gate, s),
                      "router_gemm")) != MOE_OK)
     return st;
   sg.end();

@@ -5,21 +5,13 @@
 // expert sees ~T*k/E tokens (128 at 4096 tokens, 256 experts, top-8), so the
 // per-expert contraction is a real GEMM and runs on the matrix cores.
 //
-// Two kernel families:
-//   expert_gemm_kernel (below, "expert-stationary GEMMs"): gate/up with the SiLU*up
+// Kernels:
+//   expert_gemm_kernel ("expert-stationary GEMMs" below): gate/up with the SiLU*up
 //            epilogue and the down projection; a block owns one expert and a chunk of
 //            its output columns, so every weight byte is read from HBM once.
-//   grouped_gemm_kernel<ROUTER>: C[64 x 128] = A[64 x K] . B[128 x K]^T with A = x and
-//            B = the fp32 router rows split exactly into three bf16 parts
-//            (w = hi + mid + lo), K = 3H: fp32 logits from bf16 products.  (Its GATE_UP
-//            and DOWN branches are the earlier tile-per-block form of those
-//            contractions; no launch instantiates them.)
-// grouped_gemm_kernel tiles: 256 threads = 4 wavefronts in 2x2, each 32 x 64 of C as
-// 2 x 4 MFMA 16x16x32 bf16 tiles, fp32 accumulators.  K advances 64 per stage through
-// a double LDS buffer (rows padded by 16 bytes), one barrier per stage, next stage's
-// global loads in flight during the current stage's MFMAs.  Tile order: a block's
-// linear id L runs on XCD L % 8; each XCD takes a contiguous range of (N-tile major,
-// M-tile minor) work.
+//   router_mfma_kernel: the fp32 router logits on the matrix cores from an exact
+//            three-way bf16 split of the weights, made while each tile is staged.
+//   combine_kernel: the weighted sum of each token's expert outputs in slot order.
 #include <cstdio>
 #include <mutex>
 
@@ -29,215 +21,9 @@
 namespace moe {
 
 namespace {
-constexpr int TM = 64;          // tile rows (== prefill BM)
-constexpr int TN = 128;         // tile B rows
-constexpr int TK = 64;          // K per LDS stage
-constexpr int LDSW = TK + 8;    // bf16 per LDS row
-constexpr int NTHR = 256;
 constexpr int kXcds = 8;
-enum { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
-
-struct RouterArgs {
-  const float *b_r;
-  float *logits;
-  float *gate_logit;
-  int E, NRt;  // experts, B rows in total (E + shared gate row)
-};
+enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
 }  // namespace
-
-template <int MODE>
-__global__ __launch_bounds__(NTHR, 2) void grouped_gemm_kernel(GemmArgs a, RouterArgs ra, int MT_r, int MT_s,
-                                                               int NN) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TM * LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TN * LDSW];
-
-  const int MT = MT_r + MT_s;
-  const int ntiles = MT * NN;
-  const int per_xcd = (ntiles + kXcds - 1) / kXcds;
-  const int u = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (u >= ntiles) return;
-  const int mtile = u % MT, ntile = u / MT;
-  const bool routed = mtile < MT_r;
-  const int n_slots = a.T * a.k;
-
-  // ---- segment: expert, K, B base, row counts
-  int e = 0, K = 0, Iseg = 0;
-  if (MODE == MODE_ROUTER) {
-    K = 3 * a.H;
-  } else if (routed) {
-    e = a.block_expert[(mtile * TM) / a.BM];  // BM is 64 or 128: one expert per tile
-    if (e < 0) return;  // past the padded total
-    Iseg = a.I;
-    K = MODE == MODE_GATE_UP ? a.H : a.I;
-  } else {
-    Iseg = a.I_s;
-    K = MODE == MODE_GATE_UP ? a.H : a.I_s;
-  }
-  const int n0 = MODE == MODE_GATE_UP ? ntile * (TN / 2) : ntile * TN;
-  if (MODE == MODE_GATE_UP && n0 >= Iseg) return;
-  const int m0 = routed ? mtile * TM : (mtile - MT_r) * TM;  // sorted position or token
-
-  const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = wave_id();
-  const int wm = wave & 1, wn = wave >> 1;
-
-  // ---- per-thread global row pointers: A rows tid/8 and 32 + tid/8, B rows tid/8 + 32i
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const uint16_t *arow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = lrow + 32 * i;
-    const uint16_t *p = nullptr;
-    if (MODE == MODE_GATE_UP) {
-      if (routed) {
-        const int slot = a.sorted[m0 + r];
-        if (slot < n_slots) p = a.x + (size_t)(slot / a.k) * a.H;
-      } else if (m0 + r < a.T) {
-        p = a.x + (size_t)(m0 + r) * a.H;
-      }
-    } else if (MODE == MODE_DOWN) {
-      if (routed) p = a.h + (size_t)(m0 + r) * a.I;
-      else if (m0 + r < a.T) p = a.h_s + (size_t)(m0 + r) * a.I_s;
-    } else {
-      if (m0 + r < a.T) p = a.x + (size_t)(m0 + r) * a.H;
-    }
-    arow[i] = p;
-  }
-  const uint16_t *brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 32 * i;
-    const uint16_t *p = nullptr;
-    if (MODE == MODE_GATE_UP) {
-      const uint16_t *bank = routed ? a.w_gu + (size_t)e * 2 * a.I * a.H : a.ws_gu;
-      const int wr = r < TN / 2 ? n0 + r : Iseg + n0 + (r - TN / 2);
-      p = bank + (size_t)wr * a.H;
-    } else if (MODE == MODE_DOWN) {
-      const uint16_t *bank = routed ? a.w_d + (size_t)e * a.H * a.I : a.ws_d;
-      p = bank + (size_t)(n0 + r) * Iseg;
-    } else {
-      if (n0 + r < ra.NRt) p = a.w_gu + (size_t)(n0 + r) * a.H;  // w3 passed in w_gu
-    }
-    brow[i] = p;
-  }
-
-  const int KT = K / TK;
-  uint4 ra_reg[2], rb_reg[4];
-  auto gload = [&](int kt) {
-    int ka = kt * TK, kb = kt * TK;
-    size_t boff = 0;
-    if (MODE == MODE_ROUTER) {
-      const int per = a.H / TK;
-      ka = (kt % per) * TK;
-      kb = ka;
-      boff = (size_t)(kt / per) * ra.NRt * a.H;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ra_reg[i] = arow[i] != nullptr ? *reinterpret_cast<const uint4 *>(arow[i] + ka + 8 * lchunk)
-                                     : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      // plain (temporal) loads: the expert's other M-tiles, next to this one on the same XCD,
-      // read the same weight tile from L2
-      rb_reg[i] = brow[i] != nullptr ? *reinterpret_cast<const uint4 *>(brow[i] + boff + kb + 8 * lchunk)
-                                     : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4 *>(&sA[buf][(lrow + 32 * i) * LDSW + 8 * lchunk]) = ra_reg[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4 *>(&sB[buf][(lrow + 32 * i) * LDSW + 8 * lchunk]) = rb_reg[i];
-  };
-
-  // B fragment rows of this wavefront
-  int bfr[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    if (MODE == MODE_GATE_UP) bfr[ni] = ni < 2 ? 32 * wn + 16 * ni : TN / 2 + 32 * wn + 16 * (ni - 2);
-    else bfr[ni] = 64 * wn + 16 * ni;
-  }
-
-  f32x4_t acc[2][4];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < TK / 32; ++ks) {
-      bf16x8_t af[2], bfm[4];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                  &sA[buf][(32 * wm + 16 * mi + fr) * LDSW + ks * 32 + fk]));
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bfm[ni] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                   &sB[buf][(bfr[ni] + fr) * LDSW + ks * 32 + fk]));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfm[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds C[row = 4*(lane/16) + v][col = lane%16] of each 16x16 tile
-  const int crow = 4 * (lane >> 4), ccol = lane & 15;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 32 * wm + 16 * mi + crow + v;
-      if (MODE == MODE_GATE_UP) {
-        uint16_t *dst;
-        if (routed) dst = a.h + (size_t)(m0 + row) * a.I;
-        else dst = (m0 + row < a.T) ? a.h_s + (size_t)(m0 + row) * a.I_s : nullptr;
-        if (dst != nullptr) {
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const float g = acc[mi][ni][v], uu = acc[mi][ni + 2][v];
-            dst[n0 + 32 * wn + 16 * ni + ccol] = to_bf16(g / (1.0f + expf(-g)) * uu);
-          }
-        }
-      } else if (MODE == MODE_DOWN) {
-        uint16_t *dst = nullptr;
-        if (routed) {
-          const int slot = a.sorted[m0 + row];
-          if (slot < n_slots) dst = a.y + (size_t)slot * a.H;
-        } else if (m0 + row < a.T) {
-          dst = a.y_s + (size_t)(m0 + row) * a.H;
-        }
-        if (dst != nullptr) {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) dst[n0 + bfr[ni] + ccol] = to_bf16(acc[mi][ni][v]);
-        }
-      } else {
-        const int t = m0 + row;
-        if (t < a.T) {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            const int ex = n0 + bfr[ni] + ccol;
-            if (ex < ra.E) ra.logits[(size_t)t * ra.E + ex] = acc[mi][ni][v] + (ra.b_r ? ra.b_r[ex] : 0.0f);
-            else if (ex < ra.NRt) ra.gate_logit[t] = acc[mi][ni][v];
-          }
-        }
-      }
-    }
-  }
-}
 
 static unsigned grid_for(int tiles) { return (unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds); }
 
@@ -528,42 +314,231 @@ hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) { return launch
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_DOWN>(a, s); }
 
 // ---------------------------------------------------------------- router on MFMA
-// Exact three-way split of each fp32 router weight into bf16 parts: hi = rne(w),
+// logits[t][e] = x_t . W_r[e] + b[e] and gate[t] = x_t . w_sg in fp32.  Each fp32 weight is
+// split exactly into three bf16 parts while its tile is staged -- hi = rne(w),
 // mid = rne(w - hi), lo = rne(w - hi - mid); each difference is exact in fp32 and
-// hi + mid + lo == w.  Row E (when present) is the shared expert's gate vector.
-__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ w_r,
-                                                           const float *__restrict__ w_sg, int E, int H,
-                                                           uint16_t *__restrict__ w3) {
-  const int NRt = E + (w_sg != nullptr ? 1 : 0);
-  const size_t total = (size_t)NRt * H;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int n = (int)(i / H), hh = (int)(i % H);
-    const float w = n < E ? w_r[(size_t)n * H + hh] : w_sg[hh];
-    const float hi = round_bf16(w);
-    const float r1 = w - hi;
-    const float mid = round_bf16(r1);
-    const float lo = round_bf16(r1 - mid);
-    w3[i] = to_bf16(hi);
-    w3[total + i] = to_bf16(mid);
-    w3[2 * total + i] = to_bf16(lo);
+// hi + mid + lo == w -- so the MFMA sums exact bf16 products x.hi + x.mid + x.lo in fp32.
+// Block: 64 tokens x 64 experts, 4 wavefronts in 2 x 2, each 32 x 32 as 2 x 2 tiles of
+// 16x16x32; K in stages of 64 through a double LDS buffer fed from two alternating register
+// sets, so two stages of loads are in flight during each stage's MFMAs.  The gate logit (fp32 FMAs on the staged
+// tokens) is split among the expert tiles of a token tile: tile j of NN takes tokens
+// j * ceil(64 / NN) .., 16 lanes per token, each lane 4 columns of every stage, then a
+// 16-lane sum.  Blocks on one XCD take consecutive (token tile, expert tile) pairs, so a
+// token tile's expert tiles share that XCD's L2 copy of its tokens.
+namespace {
+constexpr int RT_M = 64, RT_N = 64, RT_K = 64, RT_W = RT_K + 8;  // LDS row: 72 bf16 (144 bytes)
+constexpr int RT_NT = 256;
+constexpr int RT_ABUF = RT_M * RT_W, RT_BBUF = 3 * RT_N * RT_W;  // elements per stage
+constexpr size_t RT_LDS = (size_t)2 * (RT_ABUF + RT_BBUF) * 2;   // 73728 bytes
+constexpr int RT_GT = 4;                                         // gate tokens per lane at most
+}  // namespace
+
+__global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__restrict__ x, int T, int H,
+                                                            const float *__restrict__ w_r,
+                                                            const float *__restrict__ b_r, int E,
+                                                            const float *__restrict__ w_sg,
+                                                            float *__restrict__ logits,
+                                                            float *__restrict__ gate_logit, int MT, int NN) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t rt_lds[];
+  uint16_t *sA = rt_lds;                 // [2][64][72]: tokens
+  uint16_t *sB = rt_lds + 2 * RT_ABUF;  // [2][3][64][72]: hi, mid, lo of the expert rows
+  const int tiles = MT * NN;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int u = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (u >= tiles) return;
+  const int mt = u / NN, nt = u % NN;
+  const int m0 = mt * RT_M, n0 = nt * RT_N;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // staging: token rows lrow, lrow + 32 (8 bf16 each); expert rows wrow + 16 i (4 fp32 each)
+  const int lrow = tid >> 3, lch = tid & 7;
+  const int wrow = tid >> 4, wq = tid & 15;
+  // rows past T or E load the last row (every load is issued, so the wait counts are
+  // fixed) and are zeroed when staged
+  const uint16_t *xr[2];
+  bool xok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = m0 + lrow + 32 * i;
+    xok[i] = t < T;
+    xr[i] = x + (size_t)min(t, T - 1) * H + 8 * lch;
+  }
+  const float *wp[4];
+  bool wok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = n0 + wrow + 16 * i;
+    wok[i] = e < E;
+    wp[i] = w_r + (size_t)min(e, E - 1) * H + 4 * wq;
+  }
+  // gate logit: tokens g0 + gr + 16 s of this tile (s < RT_GT), lane part gq
+  const bool gate = w_sg != nullptr;
+  const float *sgp = (gate ? w_sg : w_r) + 4 * (tid & 15);  // without a gate: loaded, unused
+  const int tpb = (RT_M + NN - 1) / NN;
+  const int g0 = nt * tpb, g1 = min(g0 + tpb, RT_M);
+  const int gr = tid >> 4, gq = tid & 15;
+  float gacc[RT_GT];
+#pragma unroll
+  for (int s = 0; s < RT_GT; ++s) gacc[s] = 0.0f;
+
+  // one stage of global loads in registers; two sets alternate, so while stage kk is
+  // computed from LDS, stages kk + 1 and kk + 2 are in flight
+  struct Stage {
+    uint4 xa[2];
+    float4 wv[4];
+    float4 sg;
+  };
+  Stage st0, st1;
+  const int KT = H / RT_K;
+  auto gload = [&](Stage &S, int kt) {
+    const int k0 = min(kt, KT - 1) * RT_K;  // past the end: reload the last stage (never used)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) S.xa[i] = *reinterpret_cast<const uint4 *>(xr[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S.wv[i] = *reinterpret_cast<const float4 *>(wp[i] + k0);
+    S.sg = *reinterpret_cast<const float4 *>(sgp + k0);
+  };
+  auto split_pack = [](float a0, float a1, uint32_t &h, uint32_t &m, uint32_t &l) {
+    const float h0 = round_bf16(a0), h1 = round_bf16(a1);
+    const float r0 = a0 - h0, r1 = a1 - h1;
+    const float m0_ = round_bf16(r0), m1_ = round_bf16(r1);
+    h = (uint32_t)to_bf16(h0) | ((uint32_t)to_bf16(h1) << 16);
+    m = (uint32_t)to_bf16(m0_) | ((uint32_t)to_bf16(m1_) << 16);
+    l = (uint32_t)to_bf16(r0 - m0_) | ((uint32_t)to_bf16(r1 - m1_) << 16);
+  };
+  float4 sg_lds[2];  // the gate weights of the stage in each LDS buffer
+  auto sstore = [&](const Stage &S, int buf) {
+    uint16_t *A = sA + buf * RT_ABUF;
+    uint16_t *B = sB + buf * RT_BBUF;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4 *>(&A[(lrow + 32 * i) * RT_W + 8 * lch]) = xok[i] ? S.xa[i] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 h, m, l;
+      const float4 w = wok[i] ? S.wv[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      split_pack(w.x, w.y, h.x, m.x, l.x);
+      split_pack(w.z, w.w, h.y, m.y, l.y);
+      const int off = (wrow + 16 * i) * RT_W + 4 * wq;
+      *reinterpret_cast<uint2 *>(&B[off]) = h;
+      *reinterpret_cast<uint2 *>(&B[RT_N * RT_W + off]) = m;
+      *reinterpret_cast<uint2 *>(&B[2 * RT_N * RT_W + off]) = l;
+    }
+    sg_lds[buf] = S.sg;
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  auto compute = [&](int buf) {
+    const uint16_t *A = sA + buf * RT_ABUF;
+    const uint16_t *B = sB + buf * RT_BBUF;
+#pragma unroll
+    for (int ks = 0; ks < RT_K / 32; ++ks) {
+      bf16x8_t af[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        af[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                  &A[(32 * wm + 16 * mi + fr) * RT_W + ks * 32 + fk]));
+#pragma unroll
+      for (int part = 0; part < 3; ++part) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const bf16x8_t bf = __builtin_bit_cast(
+              bf16x8_t,
+              *reinterpret_cast<const uint4 *>(&B[(part * RT_N + 32 * wn + 16 * ni + fr) * RT_W + ks * 32 + fk]));
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf, acc[mi][ni], 0, 0, 0);
+        }
+      }
+    }
+    if (gate) {
+      const float4 sg = sg_lds[buf];
+#pragma unroll
+      for (int s = 0; s < RT_GT; ++s) {
+        const int j = g0 + gr + 16 * s;
+        if (j < g1) {
+          const uint2 xv = *reinterpret_cast<const uint2 *>(&A[j * RT_W + 4 * gq]);
+          float g = gacc[s];
+          g = fmaf(sg.x, bf16_lo(xv.x), g);
+          g = fmaf(sg.y, bf16_hi(xv.x), g);
+          g = fmaf(sg.z, bf16_lo(xv.y), g);
+          g = fmaf(sg.w, bf16_hi(xv.y), g);
+          gacc[s] = g;
+        }
+      }
+    }
+  };
+  // stage kk sits in LDS buffer kk & 1 and stage kk + 1 in a register set; stage kk + 2 is
+  // issued into the set that held stage kk.  KT is even, so the loop has no tail; the loads
+  // and the LDS store past the end touch a stage that is never computed.
+  auto step = [&](int kk, Stage &next, Stage &reuse) {
+    gload(reuse, kk + 2);
+    compute(kk & 1);
+    sstore(next, (kk + 1) & 1);
+    __syncthreads();
+  };
+  gload(st0, 0);
+  gload(st1, 1);
+  sstore(st0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, st1, st0);
+    step(kt + 1, st0, st1);
+  }
+
+  // epilogue: lane holds C[row = 4 * (lane / 16) + v][col = lane % 16] of each 16x16 tile
+  const int crow = 4 * (lane >> 4), ccol = lane & 15;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int e = n0 + 32 * wn + 16 * ni + ccol;
+    const float bias = (e < E && b_r != nullptr) ? b_r[e] : 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = m0 + 32 * wm + 16 * mi + crow + v;
+        if (t < T && e < E) logits[(size_t)t * E + e] = acc[mi][ni][v] + bias;
+      }
+  }
+  if (gate) {
+#pragma unroll
+    for (int s = 0; s < RT_GT; ++s) {
+      const float g = row16_sum(gacc[s]);  // the 16 lanes of one token are one DPP row
+      const int j = g0 + gr + 16 * s;
+      if (gq == 0 && j < g1 && m0 + j < T) gate_logit[m0 + j] = g;
+    }
   }
 }
 
-hipError_t launch_router_split(const float *w_r, const float *w_sg, int E, int H, uint16_t *w3, hipStream_t s) {
-  return launch_k(router_split_kernel, dim3(512), dim3(256), 0, s, w_r, w_sg, E, H, w3);
-}
-
-hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w3, int E, int has_sg,
-                              const float *b_r, float *logits, float *gate_logit, hipStream_t s) {
-  GemmArgs a{};
-  a.x = x;
-  a.T = T;
-  a.H = H;
-  a.w_gu = w3;
-  RouterArgs ra{b_r, logits, gate_logit, E, E + (has_sg ? 1 : 0)};
-  const int MT = (T + TM - 1) / TM;
-  const int NN = (ra.NRt + TN - 1) / TN;
-  return launch_k(grouped_gemm_kernel<MODE_ROUTER>, dim3(grid_for(MT * NN)), dim3(NTHR), 0, s, a, ra, MT, 0, NN);
+hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
+                              const float *w_sg, float *logits, float *gate_logit, hipStream_t s) {
+  static std::mutex mu;
+  static bool opened[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!opened[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(router_mfma_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)RT_LDS);
+      if (e != hipSuccess) return e;
+      opened[dev] = true;
+    }
+  }
+  if (H % (2 * RT_K) != 0) return hipErrorInvalidValue;  // an even number of stages
+  const int MT = (T + RT_M - 1) / RT_M, NN = (E + RT_N - 1) / RT_N;
+  if ((RT_M + NN - 1) / NN > 16 * RT_GT) return hipErrorInvalidValue;  // gate tokens per tile
+  return launch_k(router_mfma_kernel, dim3(grid_for(MT * NN)), dim3(RT_NT), RT_LDS, s, x, T, H, w_r, b_r, E, w_sg,
+                  logits, gate_logit, MT, NN);
 }
 
 // ---------------------------------------------------------------- combine (prefill)

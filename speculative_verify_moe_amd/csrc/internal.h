@@ -152,9 +152,8 @@ struct GemmArgs {
   uint16_t *y;    // [T*k][H], row = slot
   uint16_t *y_s;  // [T][H]
 };
-hipError_t launch_router_split(const float *w_r, const float *w_sg, int E, int H, uint16_t *w3, hipStream_t s);
-hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const uint16_t *w3, int E, int has_sg,
-                              const float *b_r, float *logits, float *gate_logit, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
+                              const float *w_sg, float *logits, float *gate_logit, hipStream_t s);
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
