@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Router row n runs on block n % NB; every wavefront of the block holds the row (the
   // block's 8 loads of it share the CU's caches) and takes the tokens wave, wave + 8, ...,
   // so each token's dot product is one short chain.  The block's first kRR rows and their
-  // biases are loaded while the tokens are staged.
+  // biases are loaded first of all.
   constexpr int kRR = 3;
   float4 wr[kRR][CR];
   float bias[kRR];
@@ -234,10 +234,42 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     asm volatile("" ::"v"(voff));
   };
 
-  // tokens to LDS, in rows of xg uint4 ending in the zero pad; unguarded (clamped) loads,
-  // so they are in flight together.  The first round's token loads go out before the
-  // router rows (the tokens are few and usually cached, the router rows come from HBM):
-  // loads return in issue order, so the staging does not wait for the router.
+  // per lane: the column groups in order, four products each, one accumulation chain;
+  // then the wavefront sum (the same order as the router kernel of the four-kernel path)
+  auto router_dot = [&](const float4(&w)[CR], float b, int n, int t, const uint2(&xv)[CR]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CR; ++c) {
+      acc = fmaf(w[c].x, bf16_lo(xv[c].x), acc);
+      acc = fmaf(w[c].y, bf16_hi(xv[c].x), acc);
+      acc = fmaf(w[c].z, bf16_lo(xv[c].y), acc);
+      acc = fmaf(w[c].w, bf16_hi(xv[c].y), acc);
+    }
+    const float v = wave_sum(acc);
+    if (lane == 0) {
+      float *dst = n < E ? a.logits + (size_t)t * E + n : a.gate_logit + t;
+      __hip_atomic_store(dst, n < E ? v + b : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  // The router's critical path: the block's rows and each wavefront's first token (t = wave)
+  // straight into registers, before the token staging's loads (loads return in issue
+  // order); column groups past the row read the last group and are zeroed (zero weights).
+#pragma unroll
+  for (int r = 0; r < kRR; ++r)
+    if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
+  uint2 xt[CR];
+  {
+    const uint2 *xrow = reinterpret_cast<const uint2 *>(a.x) + (size_t)min(wave, T - 1) * (H / 4);
+#pragma unroll
+    for (int c = 0; c < CR; ++c) {
+      const int g = lane + kWave * c;
+      xt[c] = xrow[min(g, H / 4 - 1)];
+      if (g >= H / 4) xt[c] = make_uint2(0, 0);
+    }
+  }
+
+  // tokens to LDS (for phase A and the router's later tokens), in rows of xg uint4 ending
+  // in the zero pad; unguarded (clamped) loads, so they are in flight together
   uint4 *sx = reinterpret_cast<uint4 *>(data);
   {
     constexpr int kStep = kNT, kB = 8;
@@ -258,9 +290,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (base + j * kStep < n16) sx[base + j * kStep] = v[j];
     };
     x_load(tid);
+    if (wave < T) {
 #pragma unroll
-    for (int r = 0; r < kRR; ++r)
-      if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
+      for (int r = 0; r < kRR; ++r)
+        if (blockIdx.x + r * NB < NR) router_dot(wr[r], bias[r], blockIdx.x + r * NB, wave, xt);
+    }
     x_store(tid);
     for (int base = tid + kB * kStep; base < n16; base += kB * kStep) {
       x_load(base);
@@ -274,34 +308,26 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
 
-  // per lane: the column groups in order, four products each, one accumulation chain;
-  // then the wavefront sum (the same order as the router kernel of the four-kernel path)
-  auto router_row = [&](const float4(&w)[CR], float b, int n) {
-    const uint2 *x2 = reinterpret_cast<const uint2 *>(xs);
-    for (int t = wave; t < T; t += kNW) {
-      float acc = 0.0f;
+  // the wavefront's further tokens and the rows past the first kRR, from the staged tokens
+  auto lds_token = [&](uint2(&xv)[CR], int t) {
+    const uint2 *x2 = reinterpret_cast<const uint2 *>(xs) + (size_t)t * (2 * xg);
 #pragma unroll
-      for (int c = 0; c < CR; ++c) {
-        const int g = min(lane + kWave * c, H / 4);  // H / 4: the zero pad (zero weights too)
-        const uint2 xv = x2[t * (2 * xg) + g];
-        acc = fmaf(w[c].x, bf16_lo(xv.x), acc);
-        acc = fmaf(w[c].y, bf16_hi(xv.x), acc);
-        acc = fmaf(w[c].z, bf16_lo(xv.y), acc);
-        acc = fmaf(w[c].w, bf16_hi(xv.y), acc);
-      }
-      const float v = wave_sum(acc);
-      if (lane == 0) {
-        float *dst = n < E ? a.logits + (size_t)t * E + n : a.gate_logit + t;
-        __hip_atomic_store(dst, n < E ? v + b : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    for (int c = 0; c < CR; ++c) xv[c] = x2[min(lane + kWave * c, H / 4)];  // H / 4: the zero pad
   };
+  for (int t = wave + kNW; t < T; t += kNW) {
+    uint2 xv[CR];
+    lds_token(xv, t);
 #pragma unroll
-  for (int r = 0; r < kRR; ++r)
-    if (blockIdx.x + r * NB < NR) router_row(wr[r], bias[r], blockIdx.x + r * NB);
+    for (int r = 0; r < kRR; ++r)
+      if (blockIdx.x + r * NB < NR) router_dot(wr[r], bias[r], blockIdx.x + r * NB, t, xv);
+  }
   for (int n = blockIdx.x + kRR * NB; n < NR; n += NB) {  // E + 1 > kRR * NB: the rest
     load_router_row(wr[0], bias[0], n);
-    router_row(wr[0], bias[0], n);
+    for (int t = wave; t < T; t += kNW) {
+      uint2 xv[CR];
+      lds_token(xv, t);
+      router_dot(wr[0], bias[0], n, t, xv);
+    }
   }
   wait_stores();  // the router rows' logit stores
   grid_barrier(a.bar, tok0 + 1u);
