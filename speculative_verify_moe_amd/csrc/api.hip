@@ -388,6 +388,7 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   a.sorted = sorted_ids;
   a.block_expert = block_expert;
   a.offsets = expert_offsets;
+  a.counts = expert_counts;
   a.h = (uint16_t *)ws;
   a.y = (uint16_t *)((char *)ws + align_up((size_t)cap * a.I * 2, 256));
   if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
@@ -583,6 +584,7 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   a.sorted = al.sorted;
   a.block_expert = al.block_expert;
   a.offsets = al.offsets;
+  a.counts = al.counts;
   a.has_shared = shared ? 1 : 0;
   a.I_s = shared ? L->shared.inter : 0;
   a.ws_gu = shared ? (const uint16_t *)L->shared.w_gate_up : nullptr;

@@ -78,7 +78,9 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   int row0, nrows;  // first sorted position (routed) or token (shared), rows of the segment
   if (routed) {
     row0 = a.offsets[seg];
-    nrows = a.offsets[seg + 1] - row0;
+    // the rows past the count up to the next offset are padding (and the count never
+    // reaches past the expert's padded range)
+    nrows = min(a.counts[seg], a.offsets[seg + 1] - row0);
   } else {
     row0 = (seg - NSEG_R) * EG_MR;
     nrows = min(EG_MR, a.T - row0);
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   if (MODE == MODE_GATE_UP && n0 >= Iseg) return;
 
   const int lane = lane_id(), wave = wave_id();
-  const int wm = wave & 3, wn = wave >> 2;
+  // wavefronts w and w + 4 share a SIMD: giving them different M rows (wm = w / 2)
+  // spreads a pass with a ragged tile count evenly over the SIMDs
+  const int wm = wave >> 1, wn = wave & 1;
   // load mapping: a wavefront instruction fills 8 LDS rows (1 KiB); lane L writes row
   // L / 8, physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8)
   const int lr = lane >> 3, lchunk = (lane & 7) ^ lr;

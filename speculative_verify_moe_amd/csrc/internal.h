@@ -144,6 +144,7 @@ struct GemmArgs {
   const int32_t *sorted;
   const int32_t *block_expert;
   const int32_t *offsets;  // [E+1] padded expert offsets of the alignment
+  const int32_t *counts;   // [E] tokens of each expert (its rows past them are padding)
   int has_shared, I_s;
   const uint16_t *ws_gu;
   const uint16_t *ws_d;
