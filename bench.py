@@ -34,6 +34,7 @@ WORKLOADS = {
     "flash_fp8_T1": ("flash_next_fp8", 1, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=1 decode"),
     "flash_fp8_T6": ("flash_next_fp8", 6, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=6 MTP verify block"),
     "prefill_T4096": ("prefill", 4096, "Qwen3.6-35B-A3B-like MoE layer, 4096-token prefill chunk"),
+    "prefill_fp8_T4096": ("prefill_fp8", 4096, "Qwen3.6-35B-A3B-like MoE layer with fp8 e4m3 experts, 4096-token prefill chunk"),
 }
 
 FUSED_STAGES = ["moe_decode_fused"]

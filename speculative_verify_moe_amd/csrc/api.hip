@@ -203,9 +203,6 @@ moe_status validate_layer(int T, const moe_layer *L) {
     if (!aligned16(L->shared_gate_w)) return fail(MOE_ERR_MISALIGNED, "shared_gate_w must be 16-byte aligned");
   }
   if (T > 0 && !is_decode(T, L->top_k)) {
-    if (L->routed.wtype != MOE_W_BF16)
-      return fail(MOE_ERR_UNSUPPORTED, "T = %d with top_k = %d takes the prefill (MFMA) path, which needs bf16 weights; "
-                  "fp8 weights run only for T <= %d and T*k <= %d", T, L->top_k, kDecodeMaxT, kSmallSlots);
     if (L->hidden % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", L->hidden);
   }
@@ -345,8 +342,6 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_MISALIGNED, "x and out must be 16-byte aligned");
   const bool decode = is_decode(T, k);
   if (!decode) {
-    if (routed->wtype != MOE_W_BF16)
-      return fail(MOE_ERR_UNSUPPORTED, "T = %d, k = %d takes the prefill (MFMA) path, which needs bf16 weights", T, k);
     if (BM != 64 && BM != 128) return fail(MOE_ERR_UNSUPPORTED, "the prefill path needs BM = 64 or 128 (got %d)", BM);
     if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", H);
   }
@@ -389,6 +384,9 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   a.block_expert = block_expert;
   a.offsets = expert_offsets;
   a.counts = expert_counts;
+  a.wtype = routed->wtype;
+  a.s_gu = routed->s_gate_up;
+  a.s_d = routed->s_down;
   a.h = (uint16_t *)ws;
   a.y = (uint16_t *)((char *)ws + align_up((size_t)cap * a.I * 2, 256));
   if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
@@ -589,6 +587,11 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   a.I_s = shared ? L->shared.inter : 0;
   a.ws_gu = shared ? (const uint16_t *)L->shared.w_gate_up : nullptr;
   a.ws_d = shared ? (const uint16_t *)L->shared.w_down : nullptr;
+  a.wtype = L->routed.wtype;
+  a.s_gu = L->routed.s_gate_up;
+  a.s_d = L->routed.s_down;
+  a.ss_gu = shared ? L->shared.s_gate_up : nullptr;
+  a.ss_d = shared ? L->shared.s_down : nullptr;
   a.h = (uint16_t *)(base + p.off_h);
   a.h_s = (uint16_t *)(base + p.off_hs);
   a.y = (uint16_t *)(base + p.off_y);

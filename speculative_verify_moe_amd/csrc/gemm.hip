@@ -54,7 +54,9 @@ constexpr int EG_TK = 64;                          // K per stage (one 128-byte 
 constexpr int EG_NT = 512;
 constexpr int EG_ABUF = EG_MR * EG_TK * 2;         // bytes of one A stage (24 KiB)
 constexpr int EG_BBUF = EG_NB * EG_TK * 2;         // bytes of one B stage (32 KiB)
-constexpr size_t EG_LDS = (size_t)2 * EG_ABUF + 3 * EG_BBUF;  // 144 KiB
+constexpr size_t EG_LDS = (size_t)2 * EG_ABUF + 3 * EG_BBUF;  // 144 KiB (bf16 weights)
+// fp8 weights: two A stages, two widened bf16 B stages, three stages of codes (160 KiB)
+constexpr size_t EG_LDS_FP8 = (size_t)2 * EG_ABUF + 2 * EG_BBUF + 3 * (EG_NB * EG_TK);
 constexpr int kNtPolicy = 2;                       // non-temporal (weights are read once)
 typedef __attribute__((address_space(3))) void lds_void;
 }  // namespace
@@ -64,9 +66,20 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MODE>
+// ESZ: bytes per weight (2: bf16; 1: fp8 e4m3 codes with one fp32 scale per weight row).
+// fp8 stages arrive as codes in LDS (64 bytes per row and stage, 16 rows per wavefront
+// instruction, 16-byte chunk c of row r at chunk c ^ ((r / 4) & 3)), three stages ahead;
+// during each stage the block widens the next one exactly to bf16 into a two-stage bf16
+// buffer (each code once, not once per reading wavefront), so the MFMA loop is the bf16
+// one; the row scales multiply the finished sums.
+template <int MODE, int ESZ>
 __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH, int NSEG_R, int NSEG_S) {
   extern __shared__ __attribute__((aligned(16))) uint8_t eg_lds[];
+  constexpr int BRB = EG_TK * ESZ;       // bytes of one B row in one stage
+  constexpr int RPI = 1024 / BRB;        // B rows per wavefront instruction
+  constexpr int CPR = BRB / 16;          // 16-byte chunks per B row
+  constexpr int NBI = EG_NB / RPI / 8;   // B instructions per wavefront and stage
+  constexpr int QBUF = EG_NB * BRB;      // bytes of one staged B stage (bf16, or fp8 codes)
 
   const int items = (NSEG_R + NSEG_S) * NCH;
   const int per_xcd = (items + kXcds - 1) / kXcds;
@@ -101,29 +114,34 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   const int lr = lane >> 3, lchunk = (lane & 7) ^ lr;
 
   // ---- B: the expert's weight rows (one scalar descriptor)
-  const uint16_t *bank;
+  const uint8_t *bank;
   size_t bank_bytes;
+  const float *scale = nullptr;  // fp8: the row scales of this matrix
   if (MODE == MODE_GATE_UP) {
-    bank = routed ? a.w_gu + (size_t)e * 2 * a.I * a.H : a.ws_gu;
-    bank_bytes = (size_t)2 * Iseg * a.H * 2;
+    bank = routed ? (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * a.H * ESZ : (const uint8_t *)a.ws_gu;
+    bank_bytes = (size_t)2 * Iseg * a.H * ESZ;
+    if (ESZ == 1) scale = routed ? a.s_gu + (size_t)e * 2 * a.I : a.ss_gu;
   } else {
-    bank = routed ? a.w_d + (size_t)e * a.H * a.I : a.ws_d;
-    bank_bytes = (size_t)a.H * Iseg * 2;
+    bank = routed ? (const uint8_t *)a.w_d + (size_t)e * a.H * a.I * ESZ : (const uint8_t *)a.ws_d;
+    bank_bytes = (size_t)a.H * Iseg * ESZ;
+    if (ESZ == 1) scale = routed ? a.s_d + (size_t)e * a.H : a.ss_d;
   }
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bank), 0,
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
                                                                       (int)bank_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rNone = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bank), 0, 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rNone = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0, 0, 0x00020000);
   constexpr int kOff = 0x7FFFFF00;  // a row that reads zeros (past every descriptor)
   // this lane's source in the B row of instruction i (row group wave + 8 i); columns past
   // the segment (a partial last chunk) read zeros
   const int ncols = MODE == MODE_GATE_UP ? Iseg : a.H;
-  int boff[4];
+  const int blr = lane / CPR;  // row of the instruction's group, physical chunk lane % CPR
+  const int bch = ESZ == 2 ? lchunk : (lane & 3) ^ ((blr >> 2) & 3);
+  int boff[4];  // NBI used (a template-dependent array size here leaves the host stub unemitted)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * (wave + 8 * i) + lr;
+  for (int i = 0; i < NBI; ++i) {
+    const int r = RPI * (wave + 8 * i) + blr;
     const int col = MODE == MODE_GATE_UP ? n0 + (r % (EG_NB / 2)) : n0 + r;
     const int wr = MODE == MODE_GATE_UP ? (r < EG_NB / 2 ? col : Iseg + col) : col;
-    boff[i] = col < ncols ? wr * K * 2 + lchunk * 16 : kOff;
+    boff[i] = col < ncols ? wr * K * ESZ + bch * 16 : kOff;
   }
   // ---- A: token rows (gate/up) or h rows (down), gathered by the alignment
   const uint16_t *abase;
@@ -151,7 +169,8 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   const int KT = K / EG_TK;
   const int fr = lane & 15, fq = lane >> 4;  // fragment row, quarter (8 bf16 of K)
   uint8_t *const ldsA = eg_lds;
-  uint8_t *const ldsB = eg_lds + 2 * EG_ABUF;
+  uint8_t *const ldsB = eg_lds + 2 * EG_ABUF;  // bf16 B stages: three (bf16) or two (fp8)
+  uint8_t *const ldsQ = eg_lds + 2 * EG_ABUF + 2 * EG_BBUF;  // fp8: three stages of codes
 
   for (int pass0 = 0; pass0 < nrows; pass0 += EG_MR) {
     const int prow = min(EG_MR, nrows - pass0);
@@ -197,15 +216,15 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
     auto issueB = [&](int kt) {
       kt = __builtin_amdgcn_readfirstlane(kt);
       const __amdgpu_buffer_rsrc_t rs = kt < KT ? rB : rNone;
-      uint8_t *buf = ldsB + (kt % 3) * EG_BBUF;
+      uint8_t *buf = (ESZ == 2 ? ldsB : ldsQ) + (kt % 3) * QBUF;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NBI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(buf + (wave + 8 * i) * 1024), 16, boff[i],
-                                                 kt * EG_TK * 2, 0, kNtPolicy);
+                                                 kt * EG_TK * ESZ, 0, kNtPolicy);
     };
     auto mfma_stage = [&](int kt) {
       const uint8_t *pa = ldsA + (kt & 1) * EG_ABUF;
-      const uint8_t *pb = ldsB + (kt % 3) * EG_BBUF;
+      const uint8_t *pb = ldsB + (ESZ == 2 ? kt % 3 : kt & 1) * EG_BBUF;
 #pragma unroll
       for (int ks = 0; ks < EG_TK / 32; ++ks) {
         const int sw = ((ks * 4 + fq) ^ (fr & 7)) * 16;  // swizzled chunk of this lane's 8 bf16
@@ -229,18 +248,58 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
       }
     };
 
-    // in flight at the top of stage kt, in issue order: B(kt), A(kt), B(kt+1)
-    issueB(0);
-    issueA(0);
-    issueB(1);
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_vm<4>();      // A(kt) and all before it (B(kt)) are in LDS; B(kt+1) may not be
-      // ... for every wavefront; and stage kt-1 is no longer read.  A bare barrier: the
-      // explicit count above is the wait (a fenced one would drain B(kt+1) too)
+    // fp8: thread t widens half a row of codes (row t / 2, 32 codes) of stage kt into the
+    // bf16 buffer kt & 1
+    auto widen = [&](int kt) {
+      const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
+      const uint8_t *q = ldsQ + (kt % 3) * QBUF + r * 64;
+      uint8_t *b = ldsB + (kt & 1) * EG_BBUF + r * 128;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * hf + u;  // logical 16-byte chunk of codes (codes 16 c ..)
+        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((c ^ ((r >> 2) & 3)) * 16));
+        const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x),
+                                    fp8x2_to_bf16x2<false>(v.y), fp8x2_to_bf16x2<true>(v.y));
+        const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(v.z), fp8x2_to_bf16x2<true>(v.z),
+                                    fp8x2_to_bf16x2<false>(v.w), fp8x2_to_bf16x2<true>(v.w));
+        *reinterpret_cast<uint4 *>(b + (((2 * c) ^ (r & 7)) * 16)) = lo;
+        *reinterpret_cast<uint4 *>(b + (((2 * c + 1) ^ (r & 7)) * 16)) = hi;
+      }
+    };
+    if (ESZ == 2) {
+      // in flight at the top of stage kt, in issue order: B(kt), A(kt), B(kt+1)
+      issueB(0);
+      issueA(0);
+      issueB(1);
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_vm<NBI>();    // A(kt) and all before it (B(kt)) are in LDS; B(kt+1) may not be
+        // ... for every wavefront; and stage kt-1 is no longer read.  A bare barrier: the
+        // explicit count above is the wait (a fenced one would drain B(kt+1) too)
+        __builtin_amdgcn_s_barrier();
+        issueA(kt + 1);    // into A buffer (kt+1) & 1, which held stage kt-1
+        issueB(kt + 2);    // into B buffer (kt+2) % 3, which held stage kt-1
+        mfma_stage(kt);
+      }
+    } else {
+      // codes of stage kt land three stages ahead and are widened one stage ahead; at the
+      // top of stage kt, in issue order: A(kt), Q(kt+2) (Q(kt+1) before them has landed)
+      issueA(0);
+      issueB(0);
+      issueB(1);
+      issueB(2);
+      wait_vm<2 * NBI>();  // A(0), Q(0)
       __builtin_amdgcn_s_barrier();
-      issueA(kt + 1);    // into A buffer (kt+1) & 1, which held stage kt-1
-      issueB(kt + 2);    // into B buffer (kt+2) % 3, which held stage kt-1
-      mfma_stage(kt);
+      widen(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_vm<NBI>();    // A(kt) and Q(kt+1) are in LDS; Q(kt+2) may not be
+        // ... for every wavefront; stage kt is widened; stage kt-1 is no longer read
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        issueA(kt + 1);    // into A buffer (kt+1) & 1, which held stage kt-1
+        issueB(kt + 3);    // codes into Q buffer kt % 3, widened last stage
+        widen(kt + 1);     // into bf16 buffer (kt+1) & 1, which held stage kt-1
+        mfma_stage(kt);
+      }
     }
     wait_vm<0>();        // the loads past the end have landed before the buffers are reused
     __syncthreads();
@@ -260,8 +319,14 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni) {
             const int col = n0 + 64 * wn + 16 * ni + ccol;
-            const float g = acc[j][ni][v], uu = acc[j][ni + 4][v];
-            if (col < Iseg) dst[col] = to_bf16(g / (1.0f + expf(-g)) * uu);
+            float g = acc[j][ni][v], uu = acc[j][ni + 4][v];
+            if (col < Iseg) {
+              if (ESZ == 1) {
+                g *= scale[col];
+                uu *= scale[Iseg + col];
+              }
+              dst[col] = to_bf16(g / (1.0f + expf(-g)) * uu);
+            }
           }
         } else {
           uint16_t *dst = nullptr;
@@ -273,8 +338,10 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
           }
           if (dst != nullptr) {
 #pragma unroll
-            for (int ni = 0; ni < 8; ++ni)
-              if (n0 + bfr[ni] + ccol < a.H) dst[n0 + bfr[ni] + ccol] = to_bf16(acc[j][ni][v]);
+            for (int ni = 0; ni < 8; ++ni) {
+              const int col = n0 + bfr[ni] + ccol;
+              if (col < a.H) dst[col] = to_bf16(ESZ == 1 ? acc[j][ni][v] * scale[col] : acc[j][ni][v]);
+            }
           }
         }
       }
@@ -283,9 +350,9 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 }
 
 namespace {
-template <int MODE>
-hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
-  auto kern = expert_gemm_kernel<MODE>;
+template <int MODE, int ESZ>
+hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
+  auto kern = expert_gemm_kernel<MODE, ESZ>;
   static std::mutex mu;
   static bool opened[64];
   int dev = 0;
@@ -296,7 +363,7 @@ hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
     std::lock_guard<std::mutex> lock(mu);
     if (!opened[dev]) {
       e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)EG_LDS);
+                              (int)(ESZ == 2 ? EG_LDS : EG_LDS_FP8));
       if (e != hipSuccess) return e;
       opened[dev] = true;
     }
@@ -304,14 +371,25 @@ hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
   // the kernel addresses tokens, h and one expert's matrix through 32-bit buffer ranges
   const int imax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
   const size_t lim = (size_t)1 << 31;
-  if ((size_t)a.T * a.H * 2 >= lim || (size_t)a.cap * a.I * 2 >= lim || (size_t)2 * imax * a.H * 2 >= lim)
+  if ((size_t)a.T * a.H * 2 >= lim || (size_t)a.cap * a.I * 2 >= lim || (size_t)2 * imax * a.H * ESZ >= lim)
     return hipErrorInvalidValue;
   if (a.H % EG_TK != 0 || a.I % EG_TK != 0 || (a.has_shared && a.I_s % EG_TK != 0)) return hipErrorInvalidValue;
   const int NCH = MODE == MODE_GATE_UP ? (imax + EG_NB / 2 - 1) / (EG_NB / 2) : (a.H + EG_NB - 1) / EG_NB;
   const int NSEG_S = a.has_shared ? (a.T + EG_MR - 1) / EG_MR : 0;
-  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), EG_LDS, s, a, NCH, a.E, NSEG_S);
+  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), ESZ == 2 ? EG_LDS : EG_LDS_FP8, s, a, NCH,
+                  a.E, NSEG_S);
 }
 }  // namespace
+
+template <int MODE>
+hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
+  if (a.wtype == 1) {
+    if (a.s_gu == nullptr || a.s_d == nullptr || (a.has_shared && (a.ss_gu == nullptr || a.ss_d == nullptr)))
+      return hipErrorInvalidValue;
+    return launch_expert_gemm_t<MODE, 1>(a, s);
+  }
+  return launch_expert_gemm_t<MODE, 2>(a, s);
+}
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_GATE_UP>(a, s); }
 

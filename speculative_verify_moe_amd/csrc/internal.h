@@ -148,6 +148,11 @@ struct GemmArgs {
   int has_shared, I_s;
   const uint16_t *ws_gu;
   const uint16_t *ws_d;
+  int wtype;            // 0 bf16, 1 fp8 e4m3 (the matrices are then byte codes with row scales)
+  const float *s_gu;    // fp8: [E][2I] row scales of w_gu
+  const float *s_d;     // fp8: [E][H] row scales of w_d
+  const float *ss_gu;   // fp8: [2 I_s] of the shared expert
+  const float *ss_d;    // fp8: [H]
   uint16_t *h;    // [cap][I], row = sorted position
   uint16_t *h_s;  // [T][I_s]
   uint16_t *y;    // [T*k][H], row = slot

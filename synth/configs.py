@@ -66,11 +66,13 @@ CONFIGS = {
                                   bias="normal", BM=16),
     # prefill chunk: the Qwen3.6-like shapes at T=4096 with an unbiased router, BM=64
     "prefill": LayerConfig("prefill", H=2048, E=256, k=8, I=512, I_s=512, wtype="bf16", bias="none", BM=64),
+    # the prefill chunk with fp8 e4m3 experts (row scales), the same shapes
+    "prefill_fp8": LayerConfig("prefill_fp8", H=2048, E=256, k=8, I=512, I_s=512, wtype="fp8", bias="none", BM=64),
 }
 
 # Token counts each recipe is run at.
 TOKENS = {"tiny": (4,), "qwen36_a3b": (1, 8, 32), "qwen36_a3b_zipf": (32,), "flash_next_fp8": (1, 6),
-          "prefill": (4096,)}
+          "prefill": (4096,), "prefill_fp8": (4096,)}
 
 
 def _tag(tid, replica):
