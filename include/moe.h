@@ -139,7 +139,8 @@ size_t moe_experts_workspace_size(int32_t T, int32_t k, const moe_bank *routed, 
  *   x [T][H] bf16; topk_w [T][k]; alignment arrays as moe_align wrote them;
  *   out [T][H] bf16 = bf16(sum_j w[t][j] * y_{t,j}) (no shared expert).
  * T <= 64 runs the weight-streaming GEMV path (each touched expert's rows are
- * read once); larger T runs the grouped MFMA GEMM path (bf16 weights only). */
+ * read once); larger T runs the grouped MFMA GEMM path (bf16 weights, or fp8 codes
+ * widened exactly to bf16 in LDS, with the row scales applied to the finished sums). */
 moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *routed, int32_t k,
                                const float *topk_w, const int32_t *sorted_ids, const int32_t *block_expert,
                                const int32_t *expert_counts, const int32_t *expert_offsets, int32_t BM,
@@ -157,7 +158,7 @@ size_t moe_layer_workspace_size(int32_t T, const moe_layer *L);
  *   logits_out [T][E] fp32, ids_out [T][k] int32, w_out [T][k] fp32: optional
  *   (NULL to skip) copies of the routing the layer used.
  * Decode/verify blocks (T <= 64) use BM = 16 and the GEMV path; prefill chunks
- * use BM = 64 and the MFMA path (bf16 weights only). */
+ * use BM = 64 and the MFMA path (bf16 or fp8 weights). */
 moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                              int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream);
 
