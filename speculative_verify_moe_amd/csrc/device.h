@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
@@ -216,7 +217,7 @@ __device__ __forceinline__ uint64_t rank_key(float v, int e) {
 // 16-byte load of data that is read once (weights): non-temporal, so it does not
 // push the small, reused operands (tokens, intermediates) out of the caches.
 __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }

@@ -168,6 +168,24 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   }
   const int KT = K / EG_TK;
   const int fr = lane & 15, fq = lane >> 4;  // fragment row, quarter (8 bf16 of K)
+  // epilogue: lane holds C[row = 4*(lane/16) + v][col = lane%16] of each 16x16 tile
+  const int crow = 4 * (lane >> 4), ccol = lane & 15;
+  // fp8: the row scales of this lane's output columns, loaded once before the first stage
+  // (columns past the segment take the last row's scale and are never stored)
+  float sc[8];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) sc[ni] = 1.0f;
+  if (ESZ == 1) {
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      if (MODE == MODE_GATE_UP) {
+        const int col = min(n0 + 64 * wn + 16 * (ni & 3) + ccol, Iseg - 1);
+        sc[ni] = scale[ni < 4 ? col : Iseg + col];
+      } else {
+        sc[ni] = scale[min(n0 + bfr[ni] + ccol, a.H - 1)];
+      }
+    }
+  }
   uint8_t *const ldsA = eg_lds;
   uint8_t *const ldsB = eg_lds + 2 * EG_ABUF;  // bf16 B stages: three (bf16) or two (fp8)
   uint8_t *const ldsQ = eg_lds + 2 * EG_ABUF + 2 * EG_BBUF;  // fp8: three stages of codes
@@ -194,6 +212,15 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
       }
       aoff[i] = off == kOff ? kOff : off + lchunk * 16;
     }
+    // down: the slot of each of this lane's output rows, read before the first stage
+    int oslot[3][4];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = min((wm + 4 * j) * 16 + crow + v, prow - 1);
+        oslot[j][v] = MODE == MODE_DOWN && routed ? a.sorted[row0 + pass0 + r] : 0;
+      }
     const int nmt = (prow + 15) / 16;  // 16-row tiles of the pass (zero rows past prow)
     const bool mv1 = wm + 4 < nmt, mv2 = wm + 8 < nmt;
 
@@ -254,16 +281,28 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
       const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
       const uint8_t *q = ldsQ + (kt % 3) * QBUF + r * 64;
       uint8_t *b = ldsB + (kt & 1) * EG_BBUF + r * 128;
+      // the code reads are hidden from the compiler's LDS tracking: it cannot tell them from
+      // the DMA writes into the other two code stages and would wait for every load in
+      // flight (vmcnt 0); the stage read here landed at the wait at the top of the stage
+      uint4 vv[2];
+      asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(vv[0]), "=v"(vv[1])
+                   : "v"((uint32_t)(uintptr_t)(q + (((2 * hf) ^ ((r >> 2) & 3)) * 16))),
+                     "v"((uint32_t)(uintptr_t)(q + (((2 * hf + 1) ^ ((r >> 2) & 3)) * 16)))
+                   : "memory");
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = 2 * hf + u;  // logical 16-byte chunk of codes (codes 16 c ..)
-        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((c ^ ((r >> 2) & 3)) * 16));
+        const uint4 v = vv[u];
         const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x),
                                     fp8x2_to_bf16x2<false>(v.y), fp8x2_to_bf16x2<true>(v.y));
         const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(v.z), fp8x2_to_bf16x2<true>(v.z),
                                     fp8x2_to_bf16x2<false>(v.w), fp8x2_to_bf16x2<true>(v.w));
-        *reinterpret_cast<uint4 *>(b + (((2 * c) ^ (r & 7)) * 16)) = lo;
-        *reinterpret_cast<uint4 *>(b + (((2 * c + 1) ^ (r & 7)) * 16)) = hi;
+        asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %2, %3"
+                     :
+                     : "v"((uint32_t)(uintptr_t)(b + (((2 * c) ^ (r & 7)) * 16))), "v"(__builtin_bit_cast(u32x4_t, lo)),
+                       "v"((uint32_t)(uintptr_t)(b + (((2 * c + 1) ^ (r & 7)) * 16))), "v"(__builtin_bit_cast(u32x4_t, hi))
+                     : "memory");
       }
     };
     if (ESZ == 2) {
@@ -304,8 +343,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
     wait_vm<0>();        // the loads past the end have landed before the buffers are reused
     __syncthreads();
 
-    // ---- epilogue: lane holds C[row = 4*(lane/16) + v][col = lane%16] of each 16x16 tile
-    const int crow = 4 * (lane >> 4), ccol = lane & 15;
+    // ---- epilogue
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       if ((j == 1 && !mv1) || (j == 2 && !mv2)) continue;
@@ -322,8 +360,8 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
             float g = acc[j][ni][v], uu = acc[j][ni + 4][v];
             if (col < Iseg) {
               if (ESZ == 1) {
-                g *= scale[col];
-                uu *= scale[Iseg + col];
+                g *= sc[ni];
+                uu *= sc[ni + 4];
               }
               dst[col] = to_bf16(g / (1.0f + expf(-g)) * uu);
             }
@@ -331,7 +369,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
         } else {
           uint16_t *dst = nullptr;
           if (routed) {
-            const int slot = a.sorted[m];
+            const int slot = oslot[j][v];
             if (slot < n_slots) dst = a.y + (size_t)slot * a.H;
           } else {
             dst = a.y_s + (size_t)m * a.H;
@@ -340,7 +378,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 #pragma unroll
             for (int ni = 0; ni < 8; ++ni) {
               const int col = n0 + bfr[ni] + ccol;
-              if (col < a.H) dst[col] = to_bf16(ESZ == 1 ? acc[j][ni][v] * scale[col] : acc[j][ni][v]);
+              if (col < a.H) dst[col] = to_bf16(ESZ == 1 ? acc[j][ni][v] * sc[ni] : acc[j][ni][v]);
             }
           }
         }
