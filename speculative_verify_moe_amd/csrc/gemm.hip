@@ -438,20 +438,35 @@ hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) { return launch_ex
 // split exactly into three bf16 parts while its tile is staged -- hi = rne(w),
 // mid = rne(w - hi), lo = rne(w - hi - mid); each difference is exact in fp32 and
 // hi + mid + lo == w -- so the MFMA sums exact bf16 products x.hi + x.mid + x.lo in fp32.
-// Block: 64 tokens x 64 experts, 4 wavefronts in 2 x 2, each 32 x 32 as 2 x 2 tiles of
-// 16x16x32; K in stages of 64 through a double LDS buffer fed from two alternating register
-// sets, so two stages of loads are in flight during each stage's MFMAs.  The gate logit (fp32 FMAs on the staged
-// tokens) is split among the expert tiles of a token tile: tile j of NN takes tokens
-// j * ceil(64 / NN) .., 16 lanes per token, each lane 4 columns of every stage, then a
-// 16-lane sum.  Blocks on one XCD take consecutive (token tile, expert tile) pairs, so a
-// token tile's expert tiles share that XCD's L2 copy of its tokens.
+// Block: 128 tokens x 32 experts (a tall tile: each weight is split by half as many blocks
+// as with a square one), 8 wavefronts in 4 (M) x 2 (N), each 32 x 16 as 2 x 1 tiles of
+// 16x16x32 per part.  K in stages of 64 through a double LDS buffer fed from RT_NS
+// register sets that rotate, so a stage's loads have RT_NS - 1 stages to land before they
+// are staged.  The gate logit (fp32 FMAs on the staged tokens) is split among the expert
+// tiles of a token tile: tile j of NN takes tokens j * ceil(128 / NN) .., 16 lanes per
+// token, each lane 4 columns of every stage, then a 16-lane sum.  Blocks on one XCD take
+// consecutive (token tile, expert tile) pairs, so a token tile's expert tiles share that
+// XCD's L2 copy of its tokens.
 namespace {
-constexpr int RT_M = 64, RT_N = 64, RT_K = 64, RT_W = RT_K + 8;  // LDS row: 72 bf16 (144 bytes)
-constexpr int RT_NT = 256;
+constexpr int RT_M = 128, RT_N = 32, RT_K = 64, RT_W = RT_K + 8;  // LDS row: 72 bf16 (144 bytes)
+constexpr int RT_NT = 512;
+constexpr int RT_NS = 4;                                          // register sets
 constexpr int RT_ABUF = RT_M * RT_W, RT_BBUF = 3 * RT_N * RT_W;  // elements per stage
-constexpr size_t RT_LDS = (size_t)2 * (RT_ABUF + RT_BBUF) * 2;   // 73728 bytes
+constexpr size_t RT_LDS = (size_t)2 * (RT_ABUF + RT_BBUF) * 2 + 2 * RT_K * 4;  // 65024 bytes
 constexpr int RT_GT = 4;                                         // gate tokens per lane at most
+constexpr int RT_GR = RT_NT / 16;                                // gate token groups
 }  // namespace
+
+// fp32 pair -> exact three-way bf16 split, packed pairs (v_cvt_pk_bf16_f32 rounds both
+// lanes of a pair to nearest even in one instruction)
+__device__ __forceinline__ void split3_pk(float a0, float a1, uint32_t &h, uint32_t &m, uint32_t &l) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a0, a1}, b2_t));
+  const float r0 = a0 - bf16_lo(h), r1 = a1 - bf16_hi(h);
+  m = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){r0, r1}, b2_t));
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){r0 - bf16_lo(m), r1 - bf16_hi(m)}, b2_t));
+}
 
 __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__restrict__ x, int T, int H,
                                                             const float *__restrict__ w_r,
@@ -460,8 +475,9 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
                                                             float *__restrict__ logits,
                                                             float *__restrict__ gate_logit, int MT, int NN) {
   extern __shared__ __attribute__((aligned(16))) uint16_t rt_lds[];
-  uint16_t *sA = rt_lds;                 // [2][64][72]: tokens
-  uint16_t *sB = rt_lds + 2 * RT_ABUF;  // [2][3][64][72]: hi, mid, lo of the expert rows
+  uint16_t *sA = rt_lds;                 // [2][128][72]: tokens
+  uint16_t *sB = rt_lds + 2 * RT_ABUF;  // [2][3][32][72]: hi, mid, lo of the expert rows
+  float *sG = reinterpret_cast<float *>(sB + 2 * RT_BBUF);  // [2][64]: gate weights
   const int tiles = MT * NN;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int u = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -469,9 +485,9 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
   const int mt = u / NN, nt = u % NN;
   const int m0 = mt * RT_M, n0 = nt * RT_N;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
 
-  // staging: token rows lrow, lrow + 32 (8 bf16 each); expert rows wrow + 16 i (4 fp32 each)
+  // staging: token rows lrow, lrow + 64 (8 bf16 each); expert row wrow (4 fp32)
   const int lrow = tid >> 3, lch = tid & 7;
   const int wrow = tid >> 4, wq = tid & 15;
   // rows past T or E load the last row (every load is issued, so the wait counts are
@@ -480,19 +496,13 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
   bool xok[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int t = m0 + lrow + 32 * i;
+    const int t = m0 + lrow + 64 * i;
     xok[i] = t < T;
     xr[i] = x + (size_t)min(t, T - 1) * H + 8 * lch;
   }
-  const float *wp[4];
-  bool wok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = n0 + wrow + 16 * i;
-    wok[i] = e < E;
-    wp[i] = w_r + (size_t)min(e, E - 1) * H + 4 * wq;
-  }
-  // gate logit: tokens g0 + gr + 16 s of this tile (s < RT_GT), lane part gq
+  const bool wok = n0 + wrow < E;
+  const float *wp = w_r + (size_t)min(n0 + wrow, E - 1) * H + 4 * wq;
+  // gate logit: tokens g0 + gr + RT_GR s of this tile (s < RT_GT), lane part gq
   const bool gate = w_sg != nullptr;
   const float *sgp = (gate ? w_sg : w_r) + 4 * (tid & 15);  // without a gate: loaded, unused
   const int tpb = (RT_M + NN - 1) / NN;
@@ -502,57 +512,41 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
 #pragma unroll
   for (int s = 0; s < RT_GT; ++s) gacc[s] = 0.0f;
 
-  // one stage of global loads in registers; two sets alternate, so while stage kk is
-  // computed from LDS, stages kk + 1 and kk + 2 are in flight
+  // one stage of global loads in registers
   struct Stage {
     uint4 xa[2];
-    float4 wv[4];
+    float4 wv;
     float4 sg;
   };
-  Stage st0, st1;
+  Stage st[RT_NS];
   const int KT = H / RT_K;
   auto gload = [&](Stage &S, int kt) {
     const int k0 = min(kt, KT - 1) * RT_K;  // past the end: reload the last stage (never used)
 #pragma unroll
     for (int i = 0; i < 2; ++i) S.xa[i] = *reinterpret_cast<const uint4 *>(xr[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) S.wv[i] = *reinterpret_cast<const float4 *>(wp[i] + k0);
+    S.wv = *reinterpret_cast<const float4 *>(wp + k0);
     S.sg = *reinterpret_cast<const float4 *>(sgp + k0);
   };
-  auto split_pack = [](float a0, float a1, uint32_t &h, uint32_t &m, uint32_t &l) {
-    const float h0 = round_bf16(a0), h1 = round_bf16(a1);
-    const float r0 = a0 - h0, r1 = a1 - h1;
-    const float m0_ = round_bf16(r0), m1_ = round_bf16(r1);
-    h = (uint32_t)to_bf16(h0) | ((uint32_t)to_bf16(h1) << 16);
-    m = (uint32_t)to_bf16(m0_) | ((uint32_t)to_bf16(m1_) << 16);
-    l = (uint32_t)to_bf16(r0 - m0_) | ((uint32_t)to_bf16(r1 - m1_) << 16);
-  };
-  float4 sg_lds[2];  // the gate weights of the stage in each LDS buffer
   auto sstore = [&](const Stage &S, int buf) {
     uint16_t *A = sA + buf * RT_ABUF;
     uint16_t *B = sB + buf * RT_BBUF;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4 *>(&A[(lrow + 32 * i) * RT_W + 8 * lch]) = xok[i] ? S.xa[i] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint2 h, m, l;
-      const float4 w = wok[i] ? S.wv[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      split_pack(w.x, w.y, h.x, m.x, l.x);
-      split_pack(w.z, w.w, h.y, m.y, l.y);
-      const int off = (wrow + 16 * i) * RT_W + 4 * wq;
-      *reinterpret_cast<uint2 *>(&B[off]) = h;
-      *reinterpret_cast<uint2 *>(&B[RT_N * RT_W + off]) = m;
-      *reinterpret_cast<uint2 *>(&B[2 * RT_N * RT_W + off]) = l;
-    }
-    sg_lds[buf] = S.sg;
+      *reinterpret_cast<uint4 *>(&A[(lrow + 64 * i) * RT_W + 8 * lch]) = xok[i] ? S.xa[i] : make_uint4(0, 0, 0, 0);
+    uint2 h, m, l;
+    const float4 w = wok ? S.wv : make_float4(0.f, 0.f, 0.f, 0.f);
+    split3_pk(w.x, w.y, h.x, m.x, l.x);
+    split3_pk(w.z, w.w, h.y, m.y, l.y);
+    const int off = wrow * RT_W + 4 * wq;
+    *reinterpret_cast<uint2 *>(&B[off]) = h;
+    *reinterpret_cast<uint2 *>(&B[RT_N * RT_W + off]) = m;
+    *reinterpret_cast<uint2 *>(&B[2 * RT_N * RT_W + off]) = l;
+    if (tid < RT_K / 4) *reinterpret_cast<float4 *>(&sG[buf * RT_K + 4 * tid]) = S.sg;
   };
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mi = 0; mi < 2; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fk = 8 * (lane >> 4);
   auto compute = [&](int buf) {
@@ -560,29 +554,26 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
     const uint16_t *B = sB + buf * RT_BBUF;
 #pragma unroll
     for (int ks = 0; ks < RT_K / 32; ++ks) {
-      bf16x8_t af[2];
+      bf16x8_t af[2], bf[3];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
         af[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
                                                   &A[(32 * wm + 16 * mi + fr) * RT_W + ks * 32 + fk]));
 #pragma unroll
-      for (int part = 0; part < 3; ++part) {
+      for (int part = 0; part < 3; ++part)
+        bf[part] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4 *>(&B[(part * RT_N + 16 * wn + fr) * RT_W + ks * 32 + fk]));
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const bf16x8_t bf = __builtin_bit_cast(
-              bf16x8_t,
-              *reinterpret_cast<const uint4 *>(&B[(part * RT_N + 32 * wn + 16 * ni + fr) * RT_W + ks * 32 + fk]));
+      for (int part = 0; part < 3; ++part)
 #pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf, acc[mi][ni], 0, 0, 0);
-        }
-      }
+        for (int mi = 0; mi < 2; ++mi)
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf[part], acc[mi], 0, 0, 0);
     }
     if (gate) {
-      const float4 sg = sg_lds[buf];
+      const float4 sg = *reinterpret_cast<const float4 *>(&sG[buf * RT_K + 4 * gq]);
 #pragma unroll
       for (int s = 0; s < RT_GT; ++s) {
-        const int j = g0 + gr + 16 * s;
+        const int j = g0 + gr + RT_GR * s;
         if (j < g1) {
           const uint2 xv = *reinterpret_cast<const uint2 *>(&A[j * RT_W + 4 * gq]);
           float g = gacc[s];
@@ -595,43 +586,41 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
       }
     }
   };
-  // stage kk sits in LDS buffer kk & 1 and stage kk + 1 in a register set; stage kk + 2 is
-  // issued into the set that held stage kk.  KT is even, so the loop has no tail; the loads
-  // and the LDS store past the end touch a stage that is never computed.
-  auto step = [&](int kk, Stage &next, Stage &reuse) {
-    gload(reuse, kk + 2);
-    compute(kk & 1);
-    sstore(next, (kk + 1) & 1);
-    __syncthreads();
-  };
-  gload(st0, 0);
-  gload(st1, 1);
-  sstore(st0, 0);
+  // stage kk sits in LDS buffer kk & 1 and stages kk + 1 .. kk + RT_NS - 1 in register
+  // sets; stage kk + RT_NS is issued into the set that held stage kk.  The loop runs a
+  // whole number of rotations: the steps past KT compute nothing, and their loads and LDS
+  // stores touch stages that are never computed.
+#pragma unroll
+  for (int i = 0; i < RT_NS; ++i) gload(st[i], i);
+  sstore(st[0], 0);
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, st1, st0);
-    step(kt + 1, st0, st1);
+  for (int kt0 = 0; kt0 < KT; kt0 += RT_NS) {
+#pragma unroll
+    for (int i = 0; i < RT_NS; ++i) {
+      const int kk = kt0 + i;
+      gload(st[i], kk + RT_NS);
+      if (kk < KT) compute(kk & 1);
+      sstore(st[(i + 1) % RT_NS], (kk + 1) & 1);
+      __syncthreads();
+    }
   }
 
   // epilogue: lane holds C[row = 4 * (lane / 16) + v][col = lane % 16] of each 16x16 tile
   const int crow = 4 * (lane >> 4), ccol = lane & 15;
+  const int e = n0 + 16 * wn + ccol;
+  const float bias = (e < E && b_r != nullptr) ? b_r[e] : 0.0f;
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int e = n0 + 32 * wn + 16 * ni + ccol;
-    const float bias = (e < E && b_r != nullptr) ? b_r[e] : 0.0f;
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = m0 + 32 * wm + 16 * mi + crow + v;
-        if (t < T && e < E) logits[(size_t)t * E + e] = acc[mi][ni][v] + bias;
-      }
-  }
+    for (int v = 0; v < 4; ++v) {
+      const int t = m0 + 32 * wm + 16 * mi + crow + v;
+      if (t < T && e < E) logits[(size_t)t * E + e] = acc[mi][v] + bias;
+    }
   if (gate) {
 #pragma unroll
     for (int s = 0; s < RT_GT; ++s) {
       const float g = row16_sum(gacc[s]);  // the 16 lanes of one token are one DPP row
-      const int j = g0 + gr + 16 * s;
+      const int j = g0 + gr + RT_GR * s;
       if (gq == 0 && j < g1 && m0 + j < T) gate_logit[m0 + j] = g;
     }
   }
@@ -654,9 +643,9 @@ hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const float *w_r,
       opened[dev] = true;
     }
   }
-  if (H % (2 * RT_K) != 0) return hipErrorInvalidValue;  // an even number of stages
+  if (H % RT_K != 0) return hipErrorInvalidValue;
   const int MT = (T + RT_M - 1) / RT_M, NN = (E + RT_N - 1) / RT_N;
-  if ((RT_M + NN - 1) / NN > 16 * RT_GT) return hipErrorInvalidValue;  // gate tokens per tile
+  if ((RT_M + NN - 1) / NN > RT_GR * RT_GT) return hipErrorInvalidValue;  // gate tokens per tile
   return launch_k(router_mfma_kernel, dim3(grid_for(MT * NN)), dim3(RT_NT), RT_LDS, s, x, T, H, w_r, b_r, E, w_sg,
                   logits, gate_logit, MT, NN);
 }
