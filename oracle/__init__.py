@@ -35,6 +35,10 @@ def _load():
         lib.oracle_bf16_round.argtypes = [ctypes.c_double]
         lib.oracle_fp8_value.restype = ctypes.c_double
         lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_encode.restype = ctypes.c_uint8
+        lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+        lib.oracle_quantise_row.restype = ctypes.c_double
+        lib.oracle_quantise_row.argtypes = [_I, _P, _P]
         lib.oracle_router_logits.restype = None
         lib.oracle_router_logits.argtypes = [_I, _I, _I, _P, _P, _P, _P]
         lib.oracle_shared_gate_logits.restype = None
@@ -89,6 +93,28 @@ def fp8_value(codes):
     lib = _load()
     c = np.asarray(codes, dtype=np.uint8)
     return np.array([lib.oracle_fp8_value(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def fp8_encode(values):
+    """Nearest OCP E4M3FN codes (ties to an even mantissa, saturating at 448) of fp32 values."""
+    lib = _load()
+    v = np.asarray(values, dtype=np.float32)
+    return np.array([lib.oracle_fp8_encode(float(a)) for a in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def quantise_rows(a):
+    """Per-row fp8 quantisation of activations a [n][L] (fp32-representable values):
+    (codes [n][L] uint8, scales [n] float64)."""
+    lib = _load()
+    a = _c(np.atleast_2d(a), np.float64)
+    q = np.empty(a.shape, dtype=np.uint8)
+    s = np.empty((a.shape[0],), dtype=np.float64)
+    for i in range(a.shape[0]):
+        s[i] = lib.oracle_quantise_row(a.shape[1], _ptr(a[i]), _ptr(q[i]))
+    return q, s
+
+
+WTYPES = {"bf16": 0, "fp8": 1, "fp8a8": 2}
 
 
 # ---------------------------------------------------------------- routing
@@ -156,19 +182,20 @@ def align(ids, E, BM, cap=None):
 # ---------------------------------------------------------------- experts and layer
 
 def _bank_arrays(layer, prefix):
-    wtype = 0 if layer["wtype"] == "bf16" else 1
+    wtype = WTYPES[layer["wtype"]]
     wdt = np.uint16 if wtype == 0 else np.uint8
     gu = _c(layer[prefix + "w_gate_up"], wdt)
     dn = _c(layer[prefix + "w_down"], wdt)
-    sgu = _c(layer.get(prefix + "s_gate_up"), np.float32) if wtype == 1 else None
-    sd = _c(layer.get(prefix + "s_down"), np.float32) if wtype == 1 else None
+    sgu = _c(layer.get(prefix + "s_gate_up"), np.float32) if wtype != 0 else None
+    sd = _c(layer.get(prefix + "s_down"), np.float32) if wtype != 0 else None
     return wtype, gu, dn, sgu, sd
 
 
 def moe_layer(x, layer, ids, w, tokens=None, rounding=True):
     """Layer output [n_tok][H] float64 for the given routing (ids [T][k], w [T][k]).
 
-    ``layer`` is a dict with H, E, k, I, I_s, wtype ('bf16' | 'fp8') and the weight arrays
+    ``layer`` is a dict with H, E, k, I, I_s, wtype ('bf16' | 'fp8' | 'fp8a8': fp8 weights with
+    fp8 activations, each row quantised with its own scale) and the weight arrays
     (w_gate_up [E][2I][H], w_down [E][H][I], optional s_gate_up/s_down for fp8, and
     shared_w_gate_up, shared_w_down, shared_s_*, shared_gate_w when I_s > 0).
     ``tokens`` selects which tokens to compute (default: all).  With ``rounding`` the
@@ -200,7 +227,7 @@ def moe_layer(x, layer, ids, w, tokens=None, rounding=True):
 def expert(x_t, w_gate_up, w_down, s_gate_up=None, s_down=None, wtype="bf16", rounding=True):
     """One token x_t [H] (bf16 bits) through one expert (w_gate_up [2I][H], w_down [H][I])."""
     lib = _load()
-    wt = 0 if wtype == "bf16" else 1
+    wt = WTYPES[wtype]
     wdt = np.uint16 if wt == 0 else np.uint8
     x_t = _c(x_t, np.uint16)
     gu = _c(w_gate_up, wdt)

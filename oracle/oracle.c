@@ -39,6 +39,15 @@
  *            the finished row sum.
  *   R-shared shared expert with the same form; its output is scaled by
  *            sigmoid(x . w_sg).
+ *   R-act8   wtype 2 (fp8 weights with fp8 activations, the matrix-core prefill
+ *            reading of the pages' FP8 layers): each activation row entering
+ *            an expert matrix -- the token x_t, and the bf16 h of a slot -- is
+ *            quantised on its own: s = amax_i |a_i| / 448 rounded to fp32 (1 for
+ *            an all-zero row) and code_i = E4M3FN(a_i / s), the quotient
+ *            rounded to fp32 and then to the nearest code, ties to an even
+ *            mantissa, saturating at 448.  Each dot product is the exact sum of
+ *            decoded codes times decoded weights, multiplied by the weight's
+ *            row scale and the activation row's scale.
  *   R-round  the HIP path stores h, each expert's output y and the layer
  *            output as bf16.  With `rounding` set, the oracle rounds at the
  *            same three points (fp64 -> bf16, round-to-nearest-even, single
@@ -96,7 +105,41 @@ double oracle_fp8_value(uint8_t q) {
   return s ? -mag : mag;
 }
 
-/* weight element n of a bank stored as bf16 (wtype 0) or fp8 codes (wtype 1) */
+/* value -> OCP E4M3FN code: the nearest code, ties to the code with an even
+ * mantissa; magnitudes of 448 and above give 448 (the largest finite code) and
+ * NaN gives the NaN code.  Below 2^-6 the codes are the subnormal steps of 2^-9. */
+uint8_t oracle_fp8_encode(float v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs((double)v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  if (a < 0.015625) return (uint8_t)(sign | (int)nearbyint(a * 512.0)); /* 8: the smallest normal */
+  int ex;
+  frexp(a, &ex); /* a = f * 2^ex with f in [0.5, 1) */
+  int e = ex - 1;
+  int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    e += 1;
+  }
+  return (uint8_t)(sign | ((e + 7) << 3) | m);
+}
+
+/* R-act8: one activation row (fp32-representable values) -> codes q[0..n) and the
+ * row's scale, returned.  s = fp32(amax / 448) (1 for an all-zero row); q_i =
+ * oracle_fp8_encode(fp32(a_i / s)). */
+double oracle_quantise_row(int n, const double *a, uint8_t *q) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float v = fabsf((float)a[i]);
+    if (v > amax) amax = v;
+  }
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int i = 0; i < n; ++i) q[i] = oracle_fp8_encode((float)a[i] / s);
+  return (double)s;
+}
+
+/* weight element n of a bank stored as bf16 (wtype 0) or fp8 codes (wtypes 1, 2) */
 static double weight(const void *w, int wtype, size_t n) {
   if (wtype == 0) return oracle_bf16_value(((const uint16_t *)w)[n]);
   return oracle_fp8_value(((const uint8_t *)w)[n]);
@@ -218,29 +261,48 @@ int oracle_align(int T, int k, int E, int BM, int64_t cap, const int32_t *ids, i
  * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down projections).
  *   x [H] bf16 bits; w_gu [2I][H], w_d [H][I] (this expert's slices);
  *   s_gu [2I], s_d [H] row scales for fp8 (ignored for bf16);
- *   y [H] output in fp64 (bf16-rounded values when rounding != 0). */
+ *   y [H] output in fp64 (bf16-rounded values when rounding != 0).
+ * wtype 2 quantises x before the gate/up sums and h before the down sums (R-act8). */
 static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w_gu, const void *w_d,
                        const float *s_gu, const float *s_d, int rounding, double *hbuf, double *y) {
+  double *xa = (double *)calloc((size_t)H, sizeof(double));
+  uint8_t *q = (uint8_t *)malloc((size_t)(H > I ? H : I));
+  for (int h = 0; h < H; ++h) xa[h] = oracle_bf16_value(x[h]);
+  double sx = 1.0, sh = 1.0;
+  if (wtype == 2) {
+    sx = oracle_quantise_row(H, xa, q);
+    for (int h = 0; h < H; ++h) xa[h] = oracle_fp8_value(q[h]);
+  }
   for (int r = 0; r < I; ++r) {
     double g = 0.0, u = 0.0;
     for (int h = 0; h < H; ++h) {
-      double xv = oracle_bf16_value(x[h]);
-      g += xv * weight(w_gu, wtype, (size_t)r * H + h);
-      u += xv * weight(w_gu, wtype, (size_t)(I + r) * H + h);
+      g += xa[h] * weight(w_gu, wtype, (size_t)r * H + h);
+      u += xa[h] * weight(w_gu, wtype, (size_t)(I + r) * H + h);
     }
-    if (wtype == 1) {
+    if (wtype != 0) {
       g *= (double)s_gu[r];
       u *= (double)s_gu[I + r];
+    }
+    if (wtype == 2) {
+      g *= sx;
+      u *= sx;
     }
     double a = silu(g) * u;
     hbuf[r] = rounding ? oracle_bf16_rounded(a) : a;
   }
+  if (wtype == 2) {
+    sh = oracle_quantise_row(I, hbuf, q);
+    for (int r = 0; r < I; ++r) hbuf[r] = oracle_fp8_value(q[r]);
+  }
   for (int o = 0; o < H; ++o) {
     double acc = 0.0;
     for (int r = 0; r < I; ++r) acc += hbuf[r] * weight(w_d, wtype, (size_t)o * I + r);
-    if (wtype == 1) acc *= (double)s_d[o];
+    if (wtype != 0) acc *= (double)s_d[o];
+    if (wtype == 2) acc *= sh;
     y[o] = rounding ? oracle_bf16_rounded(acc) : acc;
   }
+  free(xa);
+  free(q);
 }
 
 static size_t elem_bytes(int wtype) { return wtype == 0 ? 2 : 1; }
@@ -274,8 +336,8 @@ void oracle_moe_layer(int T, int H, int E, int k, int I, int wtype, const uint16
       int e = ids[(size_t)t * k + j];
       const char *gu = (const char *)w_gu + (size_t)e * 2 * I * H * eb;
       const char *dn = (const char *)w_d + (size_t)e * H * I * eb;
-      const float *sg = wtype == 1 ? s_gu + (size_t)e * 2 * I : NULL;
-      const float *sd = wtype == 1 ? s_d + (size_t)e * H : NULL;
+      const float *sg = wtype != 0 ? s_gu + (size_t)e * 2 * I : NULL;
+      const float *sd = wtype != 0 ? s_d + (size_t)e * H : NULL;
       expert_ffn(H, I, wtype, xt, gu, dn, sg, sd, rounding, hbuf, y);
       double wj = w[(size_t)t * k + j];
       for (int o = 0; o < H; ++o) acc[o] += wj * y[o];

@@ -40,7 +40,7 @@ class LayerConfig:
     k: int
     I: int
     I_s: int          # 0: no shared expert
-    wtype: str        # 'bf16' | 'fp8'
+    wtype: str        # 'bf16' | 'fp8' | 'fp8a8' (fp8 weights; the prefill path also quantises activations)
     bias: str         # 'none' | 'normal' | 'zipf'
     BM: int
     bias_std: float = 0.5
@@ -68,11 +68,14 @@ CONFIGS = {
     "prefill": LayerConfig("prefill", H=2048, E=256, k=8, I=512, I_s=512, wtype="bf16", bias="none", BM=64),
     # the prefill chunk with fp8 e4m3 experts (row scales), the same shapes
     "prefill_fp8": LayerConfig("prefill_fp8", H=2048, E=256, k=8, I=512, I_s=512, wtype="fp8", bias="none", BM=64),
+    # the same fp8 experts with fp8 activations (one scale per token row and per h row)
+    "prefill_fp8a8": LayerConfig("prefill_fp8a8", H=2048, E=256, k=8, I=512, I_s=512, wtype="fp8a8", bias="none",
+                                 BM=64),
 }
 
 # Token counts each recipe is run at.
 TOKENS = {"tiny": (4,), "qwen36_a3b": (1, 8, 32), "qwen36_a3b_zipf": (32,), "flash_next_fp8": (1, 6),
-          "prefill": (4096,), "prefill_fp8": (4096,)}
+          "prefill": (4096,), "prefill_fp8": (4096,), "prefill_fp8a8": (4096,)}
 
 
 def _tag(tid, replica):

@@ -34,11 +34,11 @@ MUTANTS = [
     ("block map shifted", "block_expert[p / BM] = e;", "block_expert[p / BM] = e + 1;"),
     ("capacity ignores padding", "int64_t c = n + touched * (BM - 1);", "int64_t c = n + touched;"),
     ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
-    ("gate reads the up rows", "g += xv * weight(w_gu, wtype, (size_t)r * H + h);",
-     "g += xv * weight(w_gu, wtype, (size_t)(I + r) * H + h);"),
+    ("gate reads the up rows", "g += xa[h] * weight(w_gu, wtype, (size_t)r * H + h);",
+     "g += xa[h] * weight(w_gu, wtype, (size_t)(I + r) * H + h);"),
     ("down operand transposed", "acc += hbuf[r] * weight(w_d, wtype, (size_t)o * I + r);",
      "acc += hbuf[r] * weight(w_d, wtype, (size_t)r * H + o);"),
-    ("fp8 down scale dropped", "if (wtype == 1) acc *= (double)s_d[o];", "if (wtype == 1) acc *= 1.0;"),
+    ("fp8 down scale dropped", "if (wtype != 0) acc *= (double)s_d[o];", "if (wtype != 0) acc *= 1.0;"),
     ("fp8 up scale from the gate row", "u *= (double)s_gu[I + r];", "u *= (double)s_gu[r];"),
     ("combine weight dropped", "acc[o] += wj * y[o];", "acc[o] += y[o];"),
     ("shared gate dropped", "acc[o] += gamma * y[o];", "acc[o] += y[o];"),
@@ -50,6 +50,17 @@ MUTANTS = [
      "else mag = ldexp(1.0 + (double)m / 8.0, E - 8);"),
     ("fp8 subnormal scale", "if (E == 0) mag = ldexp((double)m / 8.0, -6);",
      "if (E == 0) mag = ldexp((double)m / 8.0, -7);"),
+    ("fp8 encoder truncates", "int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);",
+     "int m = (int)floor((ldexp(a, -e) - 1.0) * 8.0);"),
+    ("fp8 encoder subnormal step", "nearbyint(a * 512.0)", "nearbyint(a * 256.0)"),
+    ("fp8 encoder saturates low", "if (a >= 448.0) return", "if (a >= 416.0) return"),
+    ("activation scale off by one", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f"),
+    ("token scale dropped from the gate sums", "      g *= sx;\n", "      g *= 1.0;\n"),
+    ("h scale dropped", "if (wtype == 2) acc *= sh;", "if (wtype == 2) acc *= 1.0;"),
+    ("token not quantised", "    for (int h = 0; h < H; ++h) xa[h] = oracle_fp8_value(q[h]);\n",
+     "    for (int h = 0; h < H; ++h) xa[h] = xa[h] / sx;\n"),
+    ("h not quantised", "    for (int r = 0; r < I; ++r) hbuf[r] = oracle_fp8_value(q[r]);\n",
+     "    for (int r = 0; r < I; ++r) hbuf[r] = hbuf[r] / sh;\n"),
     ("h not rounded", "hbuf[r] = rounding ? oracle_bf16_rounded(a) : a;", "hbuf[r] = a;"),
     ("expert output not rounded", "y[o] = rounding ? oracle_bf16_rounded(acc) : acc;", "y[o] = acc;"),
 ]

@@ -166,6 +166,171 @@ def test_fp8_value_all_codes_closed_form_and_torch():
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
 
 
+def _fp8_finite_table():
+    """(codes, values) of every finite E4M3FN code, from torch's own float8 type."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    return codes, fp8_codes_to_f64(codes)
+
+
+def _fp8_brute_encode(v):
+    """Nearest finite code by search over all codes; a tie goes to the even mantissa."""
+    codes, vals = _fp8_finite_table()
+    d = np.abs(vals - float(v))
+    best = d.min()
+    cand = [int(c) for c, dd in zip(codes, d) if dd == best]
+    if len(cand) > 1:  # +0 / -0, or a true tie between neighbours
+        same_sign = [c for c in cand if (c >> 7) == (1 if math.copysign(1.0, v) < 0 else 0)]
+        cand = same_sign or cand
+        cand = [c for c in cand if c & 1 == 0] or cand
+    return cand[0]
+
+
+def _fp8_test_values(seed=0):
+    rng = np.random.default_rng(seed)
+    codes, vals = _fp8_finite_table()
+    pos = np.unique(vals[vals > 0])
+    mids = (pos[:-1] + pos[1:]) / 2  # exact ties (representable in fp32)
+    v = [0.0, -0.0, 448.0, 448.5, 464.0, 470.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6 - 2.0 ** -11]
+    v += list(mids) + list(-mids)
+    v += [np.nextafter(np.float32(m), np.float32(0)) for m in mids[::3]]
+    v += [np.nextafter(np.float32(m), np.float32(1e9)) for m in mids[::3]]
+    v += list(np.exp(rng.uniform(np.log(2.0 ** -12), np.log(600.0), 400)) * rng.choice([-1, 1], 400))
+    return np.array(v, dtype=np.float32)
+
+
+def test_fp8_encode_is_the_nearest_code_with_ties_to_even():
+    v = _fp8_test_values()
+    got = oracle.fp8_encode(v)
+    for a, c in zip(v, got):
+        assert c == _fp8_brute_encode(a), (float(a), int(c))
+
+
+def test_fp8_encode_matches_torch_cast_in_range():
+    v = _fp8_test_values(1)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.fp8_encode(v), ref)
+
+
+def test_fp8_encode_round_trips_every_finite_code():
+    codes, vals = _fp8_finite_table()
+    np.testing.assert_array_equal(oracle.fp8_encode(vals.astype(np.float32)), codes)
+
+
+def test_activation_scale_is_row_amax_over_448():
+    a = np.array([[28.0, 1.0, -2.0, 0.5], [0.0, -3.0, 1.5, 2.0], [0.0, 0.0, 0.0, 0.0]])
+    q, s = oracle.quantise_rows(a)
+    assert s[0] == 0.0625 and s[1] == float(np.float32(3.0) / np.float32(448.0)) and s[2] == 1.0
+    # row 0: 28, 1, -2, 0.5 over 1/16 -> 448, 16, -32, 8 (codes 0x7E, 0x58, 0xE0, 0x50)
+    np.testing.assert_array_equal(q[0], [0x7E, 0x58, 0xE0, 0x50])
+    assert abs(fp8_codes_to_f64(q[1])[1]) == 448.0
+    np.testing.assert_array_equal(q[2], 0)
+
+
+def _torch_fp8_dequant(v, s):
+    """fp32(v / s) to the nearest e4m3 through torch's float8 cast, times s (float64)."""
+    qv = torch.from_numpy((np.float32(v) / np.float32(s)).astype(np.float32)).to(torch.float8_e4m3fn)
+    return qv.to(torch.float64).numpy() * float(s)
+
+
+def _bf16_bits(v):
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _act8_expert(seed, up_weight=1.0):
+    """One fp8 expert and one token on which every quantisation step can be followed by hand:
+    x sits on the e4m3 grid times 2^-4 with amax 28 = 448 / 16 (scale 1/16 exactly); the gate
+    rows pick x[1] = 16 with weight 4 (g = 64, and silu(64) == 64 in fp64); up row r picks
+    x[src[r]] with weight wu[r] (row 0: x[0] = 28 with weight 1; the others ``up_weight``), so
+    h_r = 64 * wu[r] * x[src[r]] exactly and the h row's amax is 64 * 28 (scale 4)."""
+    rng = np.random.default_rng(seed)
+    H, I = 64, 64
+    codes, vals = _fp8_finite_table()
+    ok = vals[(np.abs(vals) <= 256) & (np.abs(vals) >= 2.0 ** -3)]
+    xv = rng.choice(ok, H) / 16.0
+    xv[0], xv[1], xv[2] = 28.0, 16.0, 1.0
+    x = _bf16_bits(xv)
+    assert np.array_equal(bf16_codes_to_f64(x), xv)
+    enc = {float(v): int(c) for c, v in zip(codes, vals)}
+    w_gu = np.zeros((2 * I, H), np.uint8)
+    w_gu[:I, 1] = enc[4.0]
+    src = rng.integers(1, H, I)  # only row 0 reads x[0] = 28
+    src[0], src[1] = 0, 2
+    wu = np.full(I, up_weight)
+    wu[0] = 1.0
+    w_gu[I + np.arange(I), src] = [enc[float(v)] for v in wu]
+    s_gu = np.ones(2 * I, np.float32)
+    w_d = rng.choice(codes[(codes & 0x7F) < 0x70], (H, I)).astype(np.uint8)
+    s_d = rng.uniform(0.5, 2.0, H).astype(np.float32)
+    return xv, x, src, wu, w_gu, w_d, s_gu, s_d
+
+
+def test_fp8_activations_are_exact_on_the_scaled_grid():
+    for seed in range(3):
+        _, x, _, _, w_gu, w_d, s_gu, s_d = _act8_expert(seed)
+        a8 = oracle.expert(x, w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True)
+        w8 = oracle.expert(x, w_gu, w_d, s_gu, s_d, wtype="fp8", rounding=True)
+        np.testing.assert_array_equal(a8, w8)
+
+
+def test_fp8_token_quantisation_against_torch_fp8_cast():
+    """x[2] moved off the grid: the fp8a8 expert equals the weights-only fp8 expert on the token
+    that torch's e4m3 cast makes of it (every later step stays exact)."""
+    for seed in range(3):
+        xv, x, _, _, w_gu, w_d, s_gu, s_d = _act8_expert(seed)
+        xv2 = xv.copy()
+        xv2[2] = float(bf16_codes_to_f64(_bf16_bits([1.03]))[0])
+        x2 = _bf16_bits(xv2)
+        xq = _torch_fp8_dequant(xv2, np.float32(28.0) / np.float32(448.0))
+        assert xq[2] != xv2[2] and np.array_equal(xq[[0, 1]], xv2[[0, 1]])
+        a8 = oracle.expert(x2, w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True)
+        w8 = oracle.expert(_bf16_bits(xq), w_gu, w_d, s_gu, s_d, wtype="fp8", rounding=True)
+        np.testing.assert_array_equal(a8, w8)
+    # up weight 1.5 puts h off the token's grid: the token is quantised before h is formed
+    # (x[2] = 1.1 -> 1.125, h_1 = 96 * 1.125 = 108 -> 112; from 1.1 it would be 105.6 -> 104)
+    for seed in range(3):
+        xv, x, _, _, w_gu, w_d, s_gu, s_d = _act8_expert(seed, up_weight=1.5)
+        xv2 = xv.copy()
+        xv2[2] = float(bf16_codes_to_f64(_bf16_bits([1.1]))[0])
+        xq = _torch_fp8_dequant(xv2, np.float32(28.0) / np.float32(448.0))
+        assert xq[2] == 1.125
+        np.testing.assert_array_equal(
+            oracle.expert(_bf16_bits(xv2), w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True),
+            oracle.expert(_bf16_bits(xq), w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True))
+
+
+def test_fp8_h_quantisation_against_torch_fp8_cast():
+    """Up weight 1.125 puts h off the grid (x stays on it): the down sums run over torch's e4m3
+    cast of h / s_h times s_h, s_h = fp32(amax / 448)."""
+    for seed in range(3):
+        xv, x, src, wu, w_gu, w_d, s_gu, s_d = _act8_expert(seed, up_weight=1.125)
+        h = 64.0 * wu * xv[src]
+        assert np.abs(h).max() == 64.0 * 28.0
+        s_h = np.float32(np.float32(np.abs(h).max()) / np.float32(448.0))
+        hq = _torch_fp8_dequant(h, s_h)
+        assert not np.array_equal(hq, h)
+        ref = (fp8_codes_to_f64(w_d) @ hq) * s_d.astype(np.float64)
+        got = oracle.expert(x, w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=False)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=0)
+
+
+def test_fp8a8_layer_is_the_fp8a8_experts_combined():
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="fp8a8", I_s=32, k=2)
+    L = configs.make_layer(cfg, seed=12)
+    x = configs.make_tokens(cfg, 3, seed=12)
+    ids, w = oracle.route_topk(oracle.router_logits(x, L["router_w"]).astype(np.float32), cfg.k)
+    got = oracle.moe_layer(x, L, ids, w, rounding=False)
+    z = oracle.shared_gate_logits(x, L["shared_gate_w"])
+    for t in range(3):
+        ref = sum(w[t, j] * oracle.expert(x[t], L["w_gate_up"][ids[t, j]], L["w_down"][ids[t, j]],
+                                          L["s_gate_up"][ids[t, j]], L["s_down"][ids[t, j]], "fp8a8", False)
+                  for j in range(cfg.k))
+        ref = ref + scipy.special.expit(z[t]) * oracle.expert(x[t], L["shared_w_gate_up"], L["shared_w_down"],
+                                                                L["shared_s_gate_up"], L["shared_s_down"], "fp8a8",
+                                                                False)
+        np.testing.assert_allclose(got[t], ref, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- routing
 
 def _golden_route_cases():
