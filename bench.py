@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak) at T=8 verify block, bf16"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 
 WORKLOADS = {
     # name: (recipe, T, description)
@@ -35,12 +36,16 @@ WORKLOADS = {
     "flash_fp8_T6": ("flash_next_fp8", 6, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=6 MTP verify block"),
     "prefill_T4096": ("prefill", 4096, "Qwen3.6-35B-A3B-like MoE layer, 4096-token prefill chunk"),
     "prefill_fp8_T4096": ("prefill_fp8", 4096, "Qwen3.6-35B-A3B-like MoE layer with fp8 e4m3 experts, 4096-token prefill chunk"),
+    "prefill_fp8a8_T4096": ("prefill_fp8a8", 4096, "Qwen3.6-35B-A3B-like MoE layer with fp8 e4m3 experts and fp8 "
+                            "activations (per-row scales), 4096-token prefill chunk"),
 }
 
 FUSED_STAGES = ["moe_decode_fused"]
 DECODE_STAGES = ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"]
 PREFILL_STAGES = ["router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
                   "combine"]
+PREFILL_A8_STAGES = ["router_gemm_mfma", "topk", "align", "quant_tokens", "gemm_gate_up_mfma", "quant_h",
+                     "gemm_down_mfma", "combine"]
 
 
 def parse():
@@ -142,14 +147,15 @@ def main():
     layers, xs, outs, wss, host_routers, host_x = [], [], [], [], [], []
     for r in range(L_rep):
         hr = configs.make_layer(cfg, seed=0, replica=r, with_experts=False)
+        act8 = base.routed.wtype == moe.MOE_W_FP8_E4M3_A8
         routed = moe.Bank(base.routed.w_gate_up.clone(), base.routed.w_down.clone(),
                           None if base.routed.s_gate_up is None else base.routed.s_gate_up.clone(),
-                          None if base.routed.s_down is None else base.routed.s_down.clone())
+                          None if base.routed.s_down is None else base.routed.s_down.clone(), act8)
         shared = None
         if base.shared is not None:
             shared = moe.Bank(base.shared.w_gate_up.clone(), base.shared.w_down.clone(),
                               None if base.shared.s_gate_up is None else base.shared.s_gate_up.clone(),
-                              None if base.shared.s_down is None else base.shared.s_down.clone())
+                              None if base.shared.s_down is None else base.shared.s_down.clone(), act8)
         rb = None if hr["router_b"] is None else torch.from_numpy(hr["router_b"]).to(dev)
         sg = None if cfg.I_s == 0 else torch.from_numpy(hr["shared_gate_w"]).to(dev)
         lay = moe.Layer(torch.from_numpy(hr["router_w"]).to(dev), rb, routed, cfg.k, shared, sg, cfg.renormalize)
@@ -165,7 +171,10 @@ def main():
     setup_s = time.time() - t0
     plan = moe.moe_describe_plan(T, layers[0])
     fused = "decode-fused" in plan
-    stages = PREFILL_STAGES if prefill else (FUSED_STAGES if fused else DECODE_STAGES)
+    if prefill:
+        stages = PREFILL_A8_STAGES if "quant_tokens" in plan else PREFILL_STAGES
+    else:
+        stages = FUSED_STAGES if fused else DECODE_STAGES
     nst = len(stages)
 
     # realised routing per replica (touched experts) for the algorithmic byte counts
@@ -178,7 +187,7 @@ def main():
 
     bw = 2 if cfg.wtype == "bf16" else 1
     H, I, I_s, E, k = cfg.H, cfg.I, cfg.I_s, cfg.E, cfg.k
-    srow = 4 if cfg.wtype == "fp8" else 0
+    srow = 4 if cfg.wtype in ("fp8", "fp8a8") else 0  # fp32 row scales
 
     def gate_up_bytes(nt):
         # weights of every touched expert (+ shared) once, tokens read, h written
@@ -231,6 +240,8 @@ def main():
     # dominant kernel: the fused layer kernel, the gate/up expert stream (four-kernel decode) or
     # the gate/up MFMA GEMM (prefill)
     dom = 0 if fused else (stages.index("gemm_gate_up_mfma") if prefill else stages.index("gemv_gate_up"))
+    # the matrix cores' dense peak for the operand type the prefill GEMMs run in
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if cfg.wtype == "fp8a8" else MFMA_BF16_PEAK_TFLOPS
     dom_name = stages[dom]
     dom_ms = stage_ms[:, dom]
     src_hash = source_hash(KERNEL_SOURCES[dom_name])
@@ -247,8 +258,8 @@ def main():
         # gate/up GEMM flops: every routed slot and every token through the shared expert
         fl = 2 * T * k * 2 * H * I + 2 * T * 2 * H * I_s
         achieved = fl / (dom_ms.mean() * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4),
                     "traffic": load_traffic(dom_name, args.workload, src_hash), "kernel": dom_name,
                     "avg_us": round(float(dom_ms.mean()) * 1e3, 2), "alg_flops_per_launch": int(fl)}
 
@@ -258,7 +269,7 @@ def main():
              "alg_bytes_per_layer": int(lb.mean()),
              "hbm_gbs_gpu": round(lb.sum() / (gpu_ms.sum() * 1e-3) / 1e9, 1),
              "hbm_frac_gpu": round(lb.sum() / (gpu_ms.sum() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-             "mfma_frac_gpu": round(flops_layer / (gpu_ms.mean() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+             "mfma_frac_gpu": round(flops_layer / (gpu_ms.mean() * 1e-3) / 1e12 / mfma_peak, 4),
              "touched_experts_mean": round(float(nt_steps.mean()), 2),
              "stage_us": {s: round(float(stage_ms[:, j].mean()) * 1e3, 2) for j, s in enumerate(stages)}}
 
@@ -295,7 +306,9 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.wtype if cfg.wtype == "bf16" else "fp8-e4m3 weights, bf16 activations",
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
+                                               "fp8a8": "fp8-e4m3 weights and activations (row scales), "
+                                                        "fp32 accumulate"}[cfg.wtype],
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
                    "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep,

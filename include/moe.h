@@ -67,7 +67,18 @@ typedef enum {
   MOE_ERR_DEVICE = 5       /* a HIP call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1 } moe_wtype;
+/* Weight (and activation) types of a bank.
+ *   MOE_W_BF16: bf16 weights and activations.
+ *   MOE_W_FP8_E4M3: OCP E4M3FN weight codes with one fp32 scale per weight row
+ *     (s_gate_up, s_down); bf16 activations.
+ *   MOE_W_FP8_E4M3_A8: the same weight storage.  On the prefill path the activations
+ *     entering each expert matrix are quantised too -- every token row, and every
+ *     slot's bf16 h row, to E4M3FN codes with one fp32 scale per row (amax / 448, the
+ *     nearest code, ties to an even mantissa) -- and the expert GEMMs run on the fp8
+ *     matrix cores (Qwen3.8 Flash-Next . GB10 UltraFast and veloGB10 README, FP8
+ *     layers; gfx950 fp8 MFMA).  The decode path (T <= 64) streams the same weights
+ *     with bf16 activations, exactly as MOE_W_FP8_E4M3. */
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1, MOE_W_FP8_E4M3_A8 = 2 } moe_wtype;
 
 /* A bank of experts of one form (routed: n = E experts; shared: n = 1).
  * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down per expert). */
@@ -140,7 +151,9 @@ size_t moe_experts_workspace_size(int32_t T, int32_t k, const moe_bank *routed, 
  *   out [T][H] bf16 = bf16(sum_j w[t][j] * y_{t,j}) (no shared expert).
  * T <= 64 runs the weight-streaming GEMV path (each touched expert's rows are
  * read once); larger T runs the grouped MFMA GEMM path (bf16 weights, or fp8 codes
- * widened exactly to bf16 in LDS, with the row scales applied to the finished sums). */
+ * widened exactly to bf16 in LDS, with the row scales applied to the finished sums;
+ * MOE_W_FP8_E4M3_A8 quantises the token and h rows and runs fp8 x fp8 MFMAs, and
+ * then needs inter % 128 == 0). */
 moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *routed, int32_t k,
                                const float *topk_w, const int32_t *sorted_ids, const int32_t *block_expert,
                                const int32_t *expert_counts, const int32_t *expert_offsets, int32_t BM,
@@ -158,7 +171,8 @@ size_t moe_layer_workspace_size(int32_t T, const moe_layer *L);
  *   logits_out [T][E] fp32, ids_out [T][k] int32, w_out [T][k] fp32: optional
  *   (NULL to skip) copies of the routing the layer used.
  * Decode/verify blocks (T <= 64) use BM = 16 and the GEMV path; prefill chunks
- * use BM = 64 and the MFMA path (bf16 or fp8 weights). */
+ * use BM = 64 and the MFMA path (bf16 or fp8 weights; fp8 activations as well
+ * for MOE_W_FP8_E4M3_A8, which then needs inter % 128 == 0). */
 moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                              int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream);
 

@@ -42,10 +42,13 @@
  *   R-act8   wtype 2 (fp8 weights with fp8 activations, the matrix-core prefill
  *            reading of the pages' FP8 layers): each activation row entering
  *            an expert matrix -- the token x_t, and the bf16 h of a slot -- is
- *            quantised on its own: s = amax_i |a_i| / 448 rounded to fp32 (1 for
- *            an all-zero row) and code_i = E4M3FN(a_i / s), the quotient
- *            rounded to fp32 and then to the nearest code, ties to an even
- *            mantissa, saturating at 448.  Each dot product is the exact sum of
+ *            quantised on its own: s = the smallest power of two with
+ *            amax_i |a_i| <= 448 s (1 for an all-zero row) and code_i =
+ *            E4M3FN(a_i / s), the nearest code, ties to an even mantissa (the
+ *            quotient is exact: s is a power of two).  A power of two costs
+ *            the e4m3 codes nothing -- they are floating point, every element
+ *            keeps its three mantissa bits -- and it is the gfx950 matrix
+ *            cores' own (E8M0) scale format.  Each dot product is the exact sum of
  *            decoded codes times decoded weights, multiplied by the weight's
  *            row scale and the activation row's scale.
  *   R-round  the HIP path stores h, each expert's output y and the layer
@@ -126,17 +129,22 @@ uint8_t oracle_fp8_encode(float v) {
 }
 
 /* R-act8: one activation row (fp32-representable values) -> codes q[0..n) and the
- * row's scale, returned.  s = fp32(amax / 448) (1 for an all-zero row); q_i =
- * oracle_fp8_encode(fp32(a_i / s)). */
+ * row's scale, returned: s = 2^e for the least e with amax <= 448 * 2^e (e = 0 for
+ * an all-zero row); q_i = oracle_fp8_encode(a_i * 2^-e), an exact product. */
 double oracle_quantise_row(int n, const double *a, uint8_t *q) {
-  float amax = 0.0f;
+  double amax = 0.0;
   for (int i = 0; i < n; ++i) {
-    float v = fabsf((float)a[i]);
+    double v = fabs((double)(float)a[i]);
     if (v > amax) amax = v;
   }
-  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  for (int i = 0; i < n; ++i) q[i] = oracle_fp8_encode((float)a[i] / s);
-  return (double)s;
+  int e = 0;
+  if (amax > 0.0) {
+    int ex;
+    double f = frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1); 448 / 512 = 0.875 */
+    e = f <= 0.875 ? ex - 9 : ex - 8;
+  }
+  for (int i = 0; i < n; ++i) q[i] = oracle_fp8_encode((float)ldexp((double)(float)a[i], -e));
+  return ldexp(1.0, e);
 }
 
 /* weight element n of a bank stored as bf16 (wtype 0) or fp8 codes (wtypes 1, 2) */

@@ -94,8 +94,9 @@ moe_status launched(hipError_t e, const char *what) {
 
 // ---------------------------------------------------------------- bank validation
 moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, int n_expected) {
-  if (b->wtype != MOE_W_BF16 && b->wtype != MOE_W_FP8_E4M3)
-    return fail(MOE_ERR_INVALID_ARG, "%s.wtype = %d: must be MOE_W_BF16 (0) or MOE_W_FP8_E4M3 (1)", name, b->wtype);
+  if (b->wtype != MOE_W_BF16 && b->wtype != MOE_W_FP8_E4M3 && b->wtype != MOE_W_FP8_E4M3_A8)
+    return fail(MOE_ERR_INVALID_ARG, "%s.wtype = %d: must be MOE_W_BF16 (0), MOE_W_FP8_E4M3 (1) or MOE_W_FP8_E4M3_A8 (2)",
+                name, b->wtype);
   if (need_n && b->num_experts != n_expected)
     return fail(MOE_ERR_INVALID_ARG, "%s.num_experts = %d: expected %d", name, b->num_experts, n_expected);
   if (b->hidden != H) return fail(MOE_ERR_INVALID_ARG, "%s.hidden = %d: expected H = %d", name, b->hidden, H);
@@ -105,7 +106,7 @@ moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, i
     return fail(MOE_ERR_INVALID_ARG, "%s: w_gate_up and w_down are required", name);
   if (!aligned16(b->w_gate_up) || !aligned16(b->w_down))
     return fail(MOE_ERR_MISALIGNED, "%s: weight pointers must be 16-byte aligned", name);
-  if (b->wtype == MOE_W_FP8_E4M3) {
+  if (b->wtype != MOE_W_BF16) {
     if (b->s_gate_up == nullptr || b->s_down == nullptr)
       return fail(MOE_ERR_INVALID_ARG, "%s: fp8 weights need s_gate_up and s_down row scales", name);
     if (!aligned4(b->s_gate_up) || !aligned4(b->s_down))
@@ -136,6 +137,7 @@ struct LayerPlan {
   int64_t cap = 0;
   size_t off_logits, off_gate, off_ids, off_w, off_gamma, off_counts, off_offsets, off_np, off_sorted, off_bexp;
   size_t off_h, off_hs, off_hist, off_y, off_ys, off_tl, off_bar;
+  size_t off_x8 = 0, off_sx = 0, off_h8 = 0, off_sh = 0, off_hs8 = 0, off_shs = 0;  // fp8 activations
   size_t total = 0;
 };
 
@@ -180,6 +182,14 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     p.off_y = take((size_t)n * H * 2);
     p.off_ys = take((size_t)T * H * 2);
     p.off_tl = p.off_bar = 0;
+    if (L->routed.wtype == MOE_W_FP8_E4M3_A8) {
+      p.off_x8 = take((size_t)T * H);
+      p.off_sx = take((size_t)T * 4);
+      p.off_h8 = take((size_t)p.cap * I);
+      p.off_sh = take((size_t)p.cap * 4);
+      p.off_hs8 = take((size_t)T * I_s);
+      p.off_shs = take((size_t)T * 4);
+    }
   }
   p.total = o;
   return p;
@@ -205,9 +215,18 @@ moe_status validate_layer(int T, const moe_layer *L) {
   if (T > 0 && !is_decode(T, L->top_k)) {
     if (L->hidden % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", L->hidden);
+    // fp8 activations: 128 codes of K per stage in both expert GEMMs
+    if (L->routed.wtype == MOE_W_FP8_E4M3_A8 &&
+        (L->routed.inter % 128 != 0 || (L->shared.num_experts != 0 && L->shared.inter % 128 != 0)))
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 activations on the prefill path need inter %% 128 == 0 (inter = %d%s)",
+                  L->routed.inter, L->shared.num_experts != 0 ? ", or the shared expert's" : "");
   }
   return MOE_OK;
 }
+
+// The decode kernels read fp8 banks of either fp8 type the same way: GEMVs stream the
+// weights with bf16 activations (quantising the activations saves no bytes there).
+int decode_wtype(int wtype) { return wtype == MOE_W_FP8_E4M3_A8 ? MOE_W_FP8_E4M3 : wtype; }
 
 void fill_gemv(GemvArgs &g, const uint16_t *x, int T, int H, int k, const moe_bank *routed, int E) {
   memset(&g, 0, sizeof(g));
@@ -215,7 +234,7 @@ void fill_gemv(GemvArgs &g, const uint16_t *x, int T, int H, int k, const moe_ba
   g.T = T;
   g.H = H;
   g.k = k;
-  g.wtype = routed->wtype;
+  g.wtype = decode_wtype(routed->wtype);
   g.E = E;
   g.I = routed->inter;
   g.w_gu = routed->w_gate_up;
@@ -315,7 +334,11 @@ size_t moe_experts_workspace_size(int32_t T, int32_t k, const moe_bank *routed, 
   const size_t I = (size_t)routed->inter, H = (size_t)routed->hidden;
   if (is_decode(T, k)) return align_up((size_t)n * I * 2, 256) + align_up(touched_ints(routed->num_experts, n) * 4, 256);
   const int64_t cap = capacity(T, k, routed->num_experts, BM);
-  return align_up((size_t)cap * I * 2, 256) + align_up((size_t)n * H * 2, 256);
+  size_t total = align_up((size_t)cap * I * 2, 256) + align_up((size_t)n * H * 2, 256);
+  if (routed->wtype == MOE_W_FP8_E4M3_A8)  // tokens and h as fp8 codes with row scales
+    total += align_up((size_t)T * H, 256) + align_up((size_t)T * 4, 256) + align_up((size_t)cap * I, 256) +
+             align_up((size_t)cap * 4, 256);
+  return total;
 }
 
 moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *routed, int32_t k, const float *topk_w,
@@ -344,6 +367,9 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   if (!decode) {
     if (BM != 64 && BM != 128) return fail(MOE_ERR_UNSUPPORTED, "the prefill path needs BM = 64 or 128 (got %d)", BM);
     if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", H);
+    if (routed->wtype == MOE_W_FP8_E4M3_A8 && routed->inter % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 activations on the prefill path need inter %% 128 == 0 (inter = %d)",
+                  routed->inter);
   }
   const size_t wsz = moe_experts_workspace_size(T, k, routed, BM);
   if (ws == nullptr || ws_bytes < wsz)
@@ -389,7 +415,21 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   a.s_d = routed->s_down;
   a.h = (uint16_t *)ws;
   a.y = (uint16_t *)((char *)ws + align_up((size_t)cap * a.I * 2, 256));
+  const bool act8 = routed->wtype == MOE_W_FP8_E4M3_A8;
+  if (act8) {
+    char *q = (char *)a.y + align_up((size_t)T * k * H * 2, 256);
+    a.x8 = (const uint8_t *)q;
+    q += align_up((size_t)T * H, 256);
+    a.sx = (const float *)q;
+    q += align_up((size_t)T * 4, 256);
+    a.h8 = (uint8_t *)q;
+    q += align_up((size_t)cap * a.I, 256);
+    a.sh = (float *)q;
+    if ((st = launched(launch_quant_tokens(x, T, H, (uint8_t *)a.x8, (float *)a.sx, s), "quant_tokens")) != MOE_OK)
+      return st;
+  }
   if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
+  if (act8 && (st = launched(launch_quant_h(a, s), "quant_h")) != MOE_OK) return st;
   if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
   return launched(launch_combine(a.y, nullptr, topk_w, nullptr, T, H, k, out, s), "combine");
 }
@@ -414,7 +454,8 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
   const int E = L->num_experts, k = L->top_k;
   const bool shared = L->shared.num_experts > 0;
   if (p.path == PATH_DECODE && g_opt_fused != 0 &&
-      fused_decode_fits(T, L->hidden, E, k, L->routed.inter, shared ? L->shared.inter : 0, L->routed.wtype)) {
+      fused_decode_fits(T, L->hidden, E, k, L->routed.inter, shared ? L->shared.inter : 0,
+                        decode_wtype(L->routed.wtype))) {
     snprintf(g_plan, sizeof(g_plan),
              "path=decode-fused T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 moe_decode_fused "
              "(router, top-k, alignment, gate/up, down, combine; one kernel, two grid barriers)",
@@ -426,6 +467,12 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
              "path=decode T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_rows grid=%d; "
              "1 topk_align_small grid=1x1024; 2 gemv_gate_up; 3 gemv_down_combine",
              T, E, k, p.BM, (long long)p.cap, p.total, (E + (L->shared.num_experts > 0 ? 1 : 0) + 3) / 4);
+  } else if (L->routed.wtype == MOE_W_FP8_E4M3_A8) {
+    snprintf(g_plan, sizeof(g_plan),
+             "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu fp8 activations; stages: 0 router_gemm_mfma; "
+             "1 topk; 2 align (align_hist, align_colscan, align_offsets, align_scatter); 3 quant_tokens; "
+             "4 gemm_gate_up_mfma (fp8 x fp8); 5 quant_h; 6 gemm_down_mfma (fp8 x fp8); 7 combine",
+             T, E, k, p.BM, (long long)p.cap, p.total);
   } else {
     snprintf(g_plan, sizeof(g_plan),
              "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_gemm_mfma; "
@@ -467,7 +514,8 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   Stager sg;
 
   const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 &&
-                     fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0, L->routed.wtype);
+                     fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0,
+                                       decode_wtype(L->routed.wtype));
   if (fused) {
     FusedArgs f{};
     f.x = x;
@@ -481,7 +529,7 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     f.has_shared = shared ? 1 : 0;
     f.BM = p.BM;
     f.cap = (int)p.cap;
-    f.wtype = L->routed.wtype;
+    f.wtype = decode_wtype(L->routed.wtype);
     f.w_r = L->router_w;
     f.b_r = L->router_b;
     f.w_sg = shared ? L->shared_gate_w : nullptr;
@@ -596,10 +644,30 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   a.h_s = (uint16_t *)(base + p.off_hs);
   a.y = (uint16_t *)(base + p.off_y);
   a.y_s = (uint16_t *)(base + p.off_ys);
+  const bool act8 = L->routed.wtype == MOE_W_FP8_E4M3_A8;
+  if (act8) {
+    a.x8 = (const uint8_t *)(base + p.off_x8);
+    a.sx = (const float *)(base + p.off_sx);
+    a.h8 = (uint8_t *)(base + p.off_h8);
+    a.sh = (float *)(base + p.off_sh);
+    a.hs8 = shared ? (uint8_t *)(base + p.off_hs8) : nullptr;
+    a.shs = shared ? (float *)(base + p.off_shs) : nullptr;
+  }
   sg.end();
+  if (act8) {
+    sg.begin();
+    if ((st = launched(launch_quant_tokens(x, T, H, (uint8_t *)a.x8, (float *)a.sx, s), "quant_tokens")) != MOE_OK)
+      return st;
+    sg.end();
+  }
   sg.begin();
   if ((st = launched(launch_gemm_gate_up(a, s), "gemm_gate_up")) != MOE_OK) return st;
   sg.end();
+  if (act8) {
+    sg.begin();
+    if ((st = launched(launch_quant_h(a, s), "quant_h")) != MOE_OK) return st;
+    sg.end();
+  }
   sg.begin();
   if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
   sg.end();

@@ -23,6 +23,11 @@ namespace moe {
 namespace {
 constexpr int kXcds = 8;
 enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
+// operand kinds of the expert GEMMs: bf16 weights and activations; fp8 weights widened to
+// bf16 in LDS; fp8 weights and fp8 activations (one scale per activation row) on the fp8
+// matrix cores
+enum { KIND_BF16 = 0, KIND_FP8W = 1, KIND_A8 = 2 };
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 }  // namespace
 
 static unsigned grid_for(int tiles) { return (unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds); }
@@ -66,16 +71,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// ESZ: bytes per weight (2: bf16; 1: fp8 e4m3 codes with one fp32 scale per weight row).
-// fp8 stages arrive as codes in LDS (64 bytes per row and stage, 16 rows per wavefront
-// instruction, 16-byte chunk c of row r at chunk c ^ ((r / 4) & 3)), three stages ahead;
-// during each stage the block widens the next one exactly to bf16 into a two-stage bf16
-// buffer (each code once, not once per reading wavefront), so the MFMA loop is the bf16
-// one; the row scales multiply the finished sums.
-template <int MODE, int ESZ>
+// KIND_FP8W: fp8 e4m3 weight codes with one fp32 scale per weight row.  The stages arrive
+// as codes in LDS (64 bytes per row and stage, 16 rows per wavefront instruction, 16-byte
+// chunk c of row r at chunk c ^ ((r / 4) & 3)), three stages ahead; during each stage the
+// block widens the next one exactly to bf16 into a two-stage bf16 buffer (each code once,
+// not once per reading wavefront), so the MFMA loop is the bf16 one; the row scales
+// multiply the finished sums.
+// KIND_A8: fp8 weights and fp8 activation rows (tokens, or h), each activation row with its
+// own fp32 scale.  A stage is 128 codes of K: 128 bytes per row for both operands, the bf16
+// layout byte for byte, and one 16x16x128 fp8 MFMA per tile and stage; the weight-row scale
+// and the activation-row scale multiply the finished sums.
+template <int MODE, int KIND>
 __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH, int NSEG_R, int NSEG_S) {
   extern __shared__ __attribute__((aligned(16))) uint8_t eg_lds[];
-  constexpr int BRB = EG_TK * ESZ;       // bytes of one B row in one stage
+  __shared__ float s_rsc[KIND == KIND_A8 ? EG_MR : 1];  // KIND_A8: activation scale of each row
+  // down: slot of each row (KIND_FP8W uses all 160 KiB of LDS and keeps them in registers)
+  __shared__ int s_slot[MODE == MODE_DOWN && KIND != KIND_FP8W ? EG_MR : 1];
+  constexpr int ESZ = KIND == KIND_BF16 ? 2 : 1;   // bytes per weight
+  constexpr int AESZ = KIND == KIND_A8 ? 1 : 2;    // bytes per activation
+  constexpr int TKE = KIND == KIND_A8 ? 128 : EG_TK;  // K per stage
+  constexpr int BRB = TKE * ESZ;         // bytes of one B row in one stage
   constexpr int RPI = 1024 / BRB;        // B rows per wavefront instruction
   constexpr int CPR = BRB / 16;          // 16-byte chunks per B row
   constexpr int NBI = EG_NB / RPI / 8;   // B instructions per wavefront and stage
@@ -134,7 +149,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   // the segment (a partial last chunk) read zeros
   const int ncols = MODE == MODE_GATE_UP ? Iseg : a.H;
   const int blr = lane / CPR;  // row of the instruction's group, physical chunk lane % CPR
-  const int bch = ESZ == 2 ? lchunk : (lane & 3) ^ ((blr >> 2) & 3);
+  const int bch = BRB == 128 ? lchunk : (lane & 3) ^ ((blr >> 2) & 3);
   int boff[4];  // NBI used (a template-dependent array size here leaves the host stub unemitted)
 #pragma unroll
   for (int i = 0; i < NBI; ++i) {
@@ -143,20 +158,21 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
     const int wr = MODE == MODE_GATE_UP ? (r < EG_NB / 2 ? col : Iseg + col) : col;
     boff[i] = col < ncols ? wr * K * ESZ + bch * 16 : kOff;
   }
-  // ---- A: token rows (gate/up) or h rows (down), gathered by the alignment
-  const uint16_t *abase;
+  // ---- A: token rows (gate/up) or h rows (down), gathered by the alignment (bf16, or
+  // fp8 codes for KIND_A8)
+  const uint8_t *abase;
   size_t abytes;
   if (MODE == MODE_GATE_UP) {
-    abase = a.x;
-    abytes = (size_t)a.T * a.H * 2;
+    abase = KIND == KIND_A8 ? a.x8 : (const uint8_t *)a.x;
+    abytes = (size_t)a.T * a.H * AESZ;
   } else if (routed) {
-    abase = a.h;
-    abytes = (size_t)a.cap * a.I * 2;
+    abase = KIND == KIND_A8 ? a.h8 : (const uint8_t *)a.h;
+    abytes = (size_t)a.cap * a.I * AESZ;
   } else {
-    abase = a.h_s;
-    abytes = (size_t)a.T * a.I_s * 2;
+    abase = KIND == KIND_A8 ? a.hs8 : (const uint8_t *)a.h_s;
+    abytes = (size_t)a.T * a.I_s * AESZ;
   }
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(abase), 0, (int)abytes,
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(abase), 0, (int)abytes,
                                                                       0x00020000);
 
   // B fragment rows of this wavefront
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
     if (MODE == MODE_GATE_UP) bfr[ni] = ni < 4 ? 64 * wn + 16 * ni : EG_NB / 2 + 64 * wn + 16 * (ni - 4);
     else bfr[ni] = 128 * wn + 16 * ni;
   }
-  const int KT = K / EG_TK;
+  const int KT = K / TKE;
   const int fr = lane & 15, fq = lane >> 4;  // fragment row, quarter (8 bf16 of K)
   // epilogue: lane holds C[row = 4*(lane/16) + v][col = lane%16] of each 16x16 tile
   const int crow = 4 * (lane >> 4), ccol = lane & 15;
@@ -202,25 +218,39 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
         if (MODE == MODE_GATE_UP) {
           if (routed) {
             const int slot = a.sorted[m];
-            if (slot < n_slots) off = (slot / a.k) * a.H * 2;
+            if (slot < n_slots) off = (slot / a.k) * a.H * AESZ;
           } else {
-            off = m * a.H * 2;
+            off = m * a.H * AESZ;
           }
         } else {
-          off = m * Iseg * 2;
+          off = m * Iseg * AESZ;
         }
       }
       aoff[i] = off == kOff ? kOff : off + lchunk * 16;
     }
-    // down: the slot of each of this lane's output rows, read before the first stage
-    int oslot[3][4];
+    // per row of the pass, read into LDS before the first stage (after the previous pass's
+    // epilogue has read them): down, the slot of the row; KIND_A8, the activation scale (a
+    // token's, or an h row's)
+    int oslot[3][4];  // KIND_FP8W, down: the slot of each of this lane's output rows
+    if (MODE == MODE_DOWN && KIND == KIND_FP8W) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = min((wm + 4 * j) * 16 + crow + v, prow - 1);
-        oslot[j][v] = MODE == MODE_DOWN && routed ? a.sorted[row0 + pass0 + r] : 0;
+        for (int v = 0; v < 4; ++v)
+          oslot[j][v] = routed ? a.sorted[row0 + pass0 + min((wm + 4 * j) * 16 + crow + v, prow - 1)] : 0;
+    }
+    if ((MODE == MODE_DOWN && KIND != KIND_FP8W) || KIND == KIND_A8) {
+      if (pass0 > 0) __syncthreads();
+      const int t = threadIdx.x;
+      if (t < prow) {
+        const int m = row0 + pass0 + t;
+        if (MODE == MODE_DOWN && KIND != KIND_FP8W) s_slot[t] = routed ? a.sorted[m] : 0;
+        if (KIND == KIND_A8) {
+          if (MODE == MODE_GATE_UP) s_rsc[t] = routed ? a.sx[min(a.sorted[m], n_slots - 1) / a.k] : a.sx[m];
+          else s_rsc[t] = routed ? a.sh[m] : a.shs[m];
+        }
       }
+    }
     const int nmt = (prow + 15) / 16;  // 16-row tiles of the pass (zero rows past prow)
     const bool mv1 = wm + 4 < nmt, mv2 = wm + 8 < nmt;
 
@@ -238,20 +268,43 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 #pragma unroll
       for (int i = 0; i < 3; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(buf + (wave + 8 * i) * 1024), 16, aoff[i],
-                                                 kt * EG_TK * 2, 0, 0);
+                                                 kt * TKE * AESZ, 0, 0);
     };
     auto issueB = [&](int kt) {
       kt = __builtin_amdgcn_readfirstlane(kt);
       const __amdgpu_buffer_rsrc_t rs = kt < KT ? rB : rNone;
-      uint8_t *buf = (ESZ == 2 ? ldsB : ldsQ) + (kt % 3) * QBUF;
+      uint8_t *buf = (KIND == KIND_FP8W ? ldsQ : ldsB) + (kt % 3) * QBUF;
 #pragma unroll
       for (int i = 0; i < NBI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(buf + (wave + 8 * i) * 1024), 16, boff[i],
-                                                 kt * EG_TK * ESZ, 0, kNtPolicy);
+                                                 kt * BRB, 0, kNtPolicy);
     };
     auto mfma_stage = [&](int kt) {
       const uint8_t *pa = ldsA + (kt & 1) * EG_ABUF;
-      const uint8_t *pb = ldsB + (ESZ == 2 ? kt % 3 : kt & 1) * EG_BBUF;
+      const uint8_t *pb = ldsB + (KIND == KIND_FP8W ? kt & 1 : kt % 3) * EG_BBUF;
+      if (KIND == KIND_A8) {
+        // lane (fr, fq) holds the 32 codes of K 32 fq .. 32 fq + 31 of its row (logical
+        // chunks 2 fq and 2 fq + 1), for the activation and the weight fragments alike
+        const int c0 = ((2 * fq) ^ (fr & 7)) * 16, c1 = ((2 * fq + 1) ^ (fr & 7)) * 16;
+        auto frag = [&](const uint8_t *row) {
+          const uint4 lo = *reinterpret_cast<const uint4 *>(row + c0), hi = *reinterpret_cast<const uint4 *>(row + c1);
+          return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        i32x8_t aq[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) aq[j] = frag(pa + ((wm + 4 * j) * 16 + fr) * 128);
+        // operand formats 0 (e4m3) for both; block scales 127 (2^0): plain products
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          const i32x8_t bq = frag(pb + (bfr[ni] + fr) * 128);
+          acc[0][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[0], bq, acc[0][ni], 0, 0, 0, 127, 0, 127);
+          if (mv1)
+            acc[1][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[1], bq, acc[1][ni], 0, 0, 0, 127, 0, 127);
+          if (mv2)
+            acc[2][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2], bq, acc[2][ni], 0, 0, 0, 127, 0, 127);
+        }
+        return;
+      }
 #pragma unroll
       for (int ks = 0; ks < EG_TK / 32; ++ks) {
         const int sw = ((ks * 4 + fq) ^ (fr & 7)) * 16;  // swizzled chunk of this lane's 8 bf16
@@ -305,7 +358,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
                      : "memory");
       }
     };
-    if (ESZ == 2) {
+    if (KIND != KIND_FP8W) {
       // in flight at the top of stage kt, in issue order: B(kt), A(kt), B(kt+1)
       issueB(0);
       issueA(0);
@@ -363,13 +416,17 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
                 g *= sc[ni];
                 uu *= sc[ni + 4];
               }
+              if (KIND == KIND_A8) {
+                g *= s_rsc[r];
+                uu *= s_rsc[r];
+              }
               dst[col] = to_bf16(g / (1.0f + expf(-g)) * uu);
             }
           }
         } else {
           uint16_t *dst = nullptr;
           if (routed) {
-            const int slot = oslot[j][v];
+            const int slot = KIND == KIND_FP8W ? oslot[j][v] : s_slot[r];
             if (slot < n_slots) dst = a.y + (size_t)slot * a.H;
           } else {
             dst = a.y_s + (size_t)m * a.H;
@@ -378,7 +435,10 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 #pragma unroll
             for (int ni = 0; ni < 8; ++ni) {
               const int col = n0 + bfr[ni] + ccol;
-              if (col < a.H) dst[col] = to_bf16(ESZ == 1 ? acc[j][ni][v] * sc[ni] : acc[j][ni][v]);
+              float o = acc[j][ni][v];
+              if (ESZ == 1) o *= sc[ni];
+              if (KIND == KIND_A8) o *= s_rsc[r];
+              if (col < a.H) dst[col] = to_bf16(o);
             }
           }
         }
@@ -388,9 +448,12 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 }
 
 namespace {
-template <int MODE, int ESZ>
+template <int MODE, int KIND>
 hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
-  auto kern = expert_gemm_kernel<MODE, ESZ>;
+  auto kern = expert_gemm_kernel<MODE, KIND>;
+  constexpr size_t lds = KIND == KIND_FP8W ? EG_LDS_FP8 : EG_LDS;
+  constexpr size_t ESZ = KIND == KIND_BF16 ? 2 : 1;
+  constexpr int TKE = KIND == KIND_A8 ? 128 : EG_TK;
   static std::mutex mu;
   static bool opened[64];
   int dev = 0;
@@ -401,7 +464,7 @@ hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
     std::lock_guard<std::mutex> lock(mu);
     if (!opened[dev]) {
       e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(ESZ == 2 ? EG_LDS : EG_LDS_FP8));
+                              (int)lds);
       if (e != hipSuccess) return e;
       opened[dev] = true;
     }
@@ -411,27 +474,138 @@ hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
   const size_t lim = (size_t)1 << 31;
   if ((size_t)a.T * a.H * 2 >= lim || (size_t)a.cap * a.I * 2 >= lim || (size_t)2 * imax * a.H * ESZ >= lim)
     return hipErrorInvalidValue;
-  if (a.H % EG_TK != 0 || a.I % EG_TK != 0 || (a.has_shared && a.I_s % EG_TK != 0)) return hipErrorInvalidValue;
+  if (a.H % TKE != 0 || a.I % TKE != 0 || (a.has_shared && a.I_s % TKE != 0)) return hipErrorInvalidValue;
   const int NCH = MODE == MODE_GATE_UP ? (imax + EG_NB / 2 - 1) / (EG_NB / 2) : (a.H + EG_NB - 1) / EG_NB;
   const int NSEG_S = a.has_shared ? (a.T + EG_MR - 1) / EG_MR : 0;
-  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), ESZ == 2 ? EG_LDS : EG_LDS_FP8, s, a, NCH,
+  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), lds, s, a, NCH,
                   a.E, NSEG_S);
 }
 }  // namespace
 
 template <int MODE>
 hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
-  if (a.wtype == 1) {
+  if (a.wtype == 1 || a.wtype == 2) {
     if (a.s_gu == nullptr || a.s_d == nullptr || (a.has_shared && (a.ss_gu == nullptr || a.ss_d == nullptr)))
       return hipErrorInvalidValue;
-    return launch_expert_gemm_t<MODE, 1>(a, s);
+    if (a.wtype == 1) return launch_expert_gemm_t<MODE, KIND_FP8W>(a, s);
+    if (a.sx == nullptr || (MODE == MODE_GATE_UP ? a.x8 == nullptr : (a.h8 == nullptr || a.sh == nullptr)) ||
+        (MODE == MODE_DOWN && a.has_shared && (a.hs8 == nullptr || a.shs == nullptr)))
+      return hipErrorInvalidValue;
+    return launch_expert_gemm_t<MODE, KIND_A8>(a, s);
   }
-  return launch_expert_gemm_t<MODE, 2>(a, s);
+  return launch_expert_gemm_t<MODE, KIND_BF16>(a, s);
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_GATE_UP>(a, s); }
 
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_DOWN>(a, s); }
+
+// ---------------------------------------------------------------- activation rows to fp8
+// One wavefront per row of L bf16 values: s = 2^e for the least e with amax <= 448 * 2^e
+// (1 for an all-zero row), code_i = the e4m3 code nearest a_i * 2^-e (an exact product),
+// ties to an even mantissa, saturating at 448.  A power-of-two scale costs the codes nothing
+// (they are floating point) and makes every quotient exact.
+// Rows whose `sorted` entry is the sentinel (padding of the alignment) are skipped.
+__device__ __forceinline__ uint32_t e4m3_nearest(float v) {
+  // both candidates are formed and one selected, so the code has no branches
+  const float a = fabsf(v);
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // 23 mantissa bits to 3, nearest, ties to even
+  const uint32_t nrm = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // exponent bias 127 -> 7
+  const uint32_t sub = (uint32_t)__float2int_rn(a * 512.0f);  // below 2^-6: steps of 2^-9 (8 is 2^-6)
+  uint32_t c = a < 0.015625f ? sub : nrm;
+  c = a < 448.0f ? c : 0x7Eu;  // saturate
+  return a != a ? 0x7Fu : (c | ((__float_as_uint(v) >> 24) & 0x80u));
+}
+
+// NG: 8-value groups per lane (L <= 512 NG); RPW rows per wavefront, all their loads in
+// flight together; each row stays in registers between its amax and its encoding.
+template <int NG, int RPW>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *__restrict__ src, int L, int R,
+                                                         const int32_t *__restrict__ sorted, int n_slots,
+                                                         uint8_t *__restrict__ dst, float *__restrict__ scale) {
+  const int row0 = (blockIdx.x * 4 + wave_id()) * RPW, lane = lane_id();
+  const int G = L / 8;
+  uint4 v[RPW][NG];
+  bool ok[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int row = row0 + rr;
+    ok[rr] = row < R && (sorted == nullptr || sorted[row] < n_slots);
+    const uint4 *r = reinterpret_cast<const uint4 *>(src + (size_t)row * L);
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      v[rr][i] = ok[rr] && lane + kWave * i < G ? r[lane + kWave * i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    if (!ok[rr]) continue;  // uniform over the wavefront
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const uint32_t w[4] = {v[rr][i].x, v[rr][i].y, v[rr][i].z, v[rr][i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
+    }
+    // wavefront maximum: DPP within each 16-lane row, then the four rows' lane 0
+    amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppHalfMirror>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppMirror>(amax));
+    amax = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, amax), 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, amax), 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, amax), 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, amax), 48))));
+    int ex = 0;
+    const float f = frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1); 448 / 512 = 0.875
+    const int e = amax > 0.0f ? (f <= 0.875f ? ex - 9 : ex - 8) : 0;
+    const int row = row0 + rr;
+    uint2 *d = reinterpret_cast<uint2 *>(dst + (size_t)row * L);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (lane + kWave * i >= G) continue;
+      const uint32_t w[4] = {v[rr][i].x, v[rr][i].y, v[rr][i].z, v[rr][i].w};
+      uint32_t c[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        c[q] = e4m3_nearest(ldexpf(bf16_lo(w[q]), -e)) | (e4m3_nearest(ldexpf(bf16_hi(w[q]), -e)) << 8);
+      d[lane + kWave * i] = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+    }
+    if (lane == 0) scale[row] = ldexpf(1.0f, e);
+  }
+}
+
+namespace {
+template <int NG, int RPW>
+hipError_t launch_quant_rows_t(const uint16_t *src, int L, int R, const int32_t *sorted, int n_slots, uint8_t *dst,
+                               float *scale, hipStream_t s) {
+  const int waves = (R + RPW - 1) / RPW;
+  return launch_k(quant_rows_kernel<NG, RPW>, dim3((waves + 3) / 4), dim3(256), 0, s, src, L, R, sorted, n_slots,
+                  dst, scale);
+}
+
+hipError_t launch_quant_rows(const uint16_t *src, int L, int R, const int32_t *sorted, int n_slots, uint8_t *dst,
+                             float *scale, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (L % 8 != 0 || L > 8192) return hipErrorInvalidValue;
+  // one row per wavefront: the rows are short, so many wavefronts in flight hide the latency
+  if (L <= 512) return launch_quant_rows_t<1, 1>(src, L, R, sorted, n_slots, dst, scale, s);
+  if (L <= 1024) return launch_quant_rows_t<2, 1>(src, L, R, sorted, n_slots, dst, scale, s);
+  if (L <= 2048) return launch_quant_rows_t<4, 1>(src, L, R, sorted, n_slots, dst, scale, s);
+  if (L <= 4096) return launch_quant_rows_t<8, 1>(src, L, R, sorted, n_slots, dst, scale, s);
+  return launch_quant_rows_t<16, 1>(src, L, R, sorted, n_slots, dst, scale, s);
+}
+}  // namespace
+
+hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, uint8_t *x8, float *sx, hipStream_t s) {
+  return launch_quant_rows(x, H, T, nullptr, 0, x8, sx, s);
+}
+
+hipError_t launch_quant_h(const GemmArgs &a, hipStream_t s) {
+  hipError_t e = launch_quant_rows((const uint16_t *)a.h, a.I, (int)a.cap, a.sorted, a.T * a.k, a.h8, a.sh, s);
+  if (e != hipSuccess || !a.has_shared) return e;
+  return launch_quant_rows((const uint16_t *)a.h_s, a.I_s, a.T, nullptr, 0, a.hs8, a.shs, s);
+}
 
 // ---------------------------------------------------------------- router on MFMA
 // logits[t][e] = x_t . W_r[e] + b[e] and gate[t] = x_t . w_sg in fp32.  Each fp32 weight is

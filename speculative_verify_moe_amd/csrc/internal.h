@@ -148,7 +148,8 @@ struct GemmArgs {
   int has_shared, I_s;
   const uint16_t *ws_gu;
   const uint16_t *ws_d;
-  int wtype;            // 0 bf16, 1 fp8 e4m3 (the matrices are then byte codes with row scales)
+  int wtype;            // 0 bf16, 1 fp8 e4m3 (the matrices are then byte codes with row scales),
+                        // 2 fp8 e4m3 with fp8 activations (x8 / h8 / hs8 below)
   const float *s_gu;    // fp8: [E][2I] row scales of w_gu
   const float *s_d;     // fp8: [E][H] row scales of w_d
   const float *ss_gu;   // fp8: [2 I_s] of the shared expert
@@ -157,11 +158,22 @@ struct GemmArgs {
   uint16_t *h_s;  // [T][I_s]
   uint16_t *y;    // [T*k][H], row = slot
   uint16_t *y_s;  // [T][H]
+  // wtype 2: the activations as fp8 codes with one fp32 scale per row
+  const uint8_t *x8;  // [T][H]
+  const float *sx;    // [T]
+  uint8_t *h8;        // [cap][I], row = sorted position (rows of real slots only)
+  float *sh;          // [cap]
+  uint8_t *hs8;       // [T][I_s]
+  float *shs;         // [T]
 };
 hipError_t launch_router_gemm(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
                               const float *w_sg, float *logits, float *gate_logit, hipStream_t s);
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s);
+// wtype 2: the tokens, and the h rows of the real slots plus the shared h rows, to fp8 codes
+// with one scale per row
+hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, uint8_t *x8, float *sx, hipStream_t s);
+hipError_t launch_quant_h(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
                           int H, int k, uint16_t *out, hipStream_t s);
 

@@ -8,7 +8,26 @@ import torch
 import oracle
 from synth import configs
 
-TOL = {"bf16": 1e-3, "fp8": 5e-3}
+TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3}
+# max-abs bars, as a fraction of max |ref|.  fp8 activations on the prefill path: the device's
+# h (fp32 sums rounded to bf16) can differ from the oracle's (fp64 sums) by one bf16 step,
+# which now and then moves an h code by one e4m3 step (at most 1/8 of that element) or a row's
+# scale (every code of the row by at most one step); one slot's output then moves by a few
+# percent of max |ref|.  The relL2 bar still binds the whole output.
+MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 5e-2}
+
+
+def runs_decode_path(T, k):
+    """The library's dispatch: T <= 64 tokens with T*k <= 1024 slots take the GEMV path."""
+    return T <= 64 and T * k <= 1024
+
+
+def oracle_layer_for_path(L, T):
+    """fp8a8 banks quantise activations on the prefill path only; decode streams the same
+    weights with bf16 activations (the fp8 reading)."""
+    if L["wtype"] == "fp8a8" and runs_decode_path(T, L["k"]):
+        return dict(L, wtype="fp8")
+    return L
 
 
 def bf16_bits(t):
@@ -87,13 +106,16 @@ def check_layer(L, x_bits, tokens=None, report=None):
     assert np.array_equal(ids, ids_ref), "top-k ids differ from the oracle"
     assert np.max(np.abs(w.astype(np.float64) - w_ref)) <= 1e-6
     # layer output on the sampled tokens, routed as the device routed
-    ref = oracle.moe_layer(x_bits, L, ids_ref, w_ref, tokens=tokens, rounding=True)
+    ref = oracle.moe_layer(x_bits, oracle_layer_for_path(L, T), ids_ref, w_ref, tokens=tokens, rounding=True)
     got = bf16_values(out_bits[tokens])
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
     mx = np.max(np.abs(got - ref))
-    tol = TOL[L["wtype"]]
+    Lref = oracle_layer_for_path(L, T)
+    tol = TOL[Lref["wtype"]]
     if report is not None:
-        report.update(rel_l2=rel, max_abs=mx, max_ref=np.max(np.abs(ref)))
+        report.update(rel_l2=rel, max_abs=mx, max_ref=np.max(np.abs(ref)), ref=ref, got=got, ids=ids_ref, w=w_ref,
+                      tokens=tokens)
     assert rel <= tol, f"relL2 {rel:.3e} > {tol}"
-    assert mx <= 1e-2 * np.max(np.abs(ref)), f"max-abs {mx:.3e} > 1e-2 * {np.max(np.abs(ref)):.3e}"
+    mtol = MAX_ABS[Lref["wtype"]]
+    assert mx <= mtol * np.max(np.abs(ref)), f"max-abs {mx:.3e} > {mtol} * {np.max(np.abs(ref)):.3e}"
     return out_bits

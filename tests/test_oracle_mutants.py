@@ -54,7 +54,8 @@ MUTANTS = [
      "int m = (int)floor((ldexp(a, -e) - 1.0) * 8.0);"),
     ("fp8 encoder subnormal step", "nearbyint(a * 512.0)", "nearbyint(a * 256.0)"),
     ("fp8 encoder saturates low", "if (a >= 448.0) return", "if (a >= 416.0) return"),
-    ("activation scale off by one", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f"),
+    ("activation scale one binade high", "e = f <= 0.875 ? ex - 9 : ex - 8;", "e = f < 0.875 ? ex - 9 : ex - 8;"),
+    ("activation scale threshold wrong", "e = f <= 0.875 ? ex - 9 : ex - 8;", "e = f <= 0.75 ? ex - 9 : ex - 8;"),
     ("token scale dropped from the gate sums", "      g *= sx;\n", "      g *= 1.0;\n"),
     ("h scale dropped", "if (wtype == 2) acc *= sh;", "if (wtype == 2) acc *= 1.0;"),
     ("token not quantised", "    for (int h = 0; h < H; ++h) xa[h] = oracle_fp8_value(q[h]);\n",

@@ -217,18 +217,23 @@ def test_fp8_encode_round_trips_every_finite_code():
     np.testing.assert_array_equal(oracle.fp8_encode(vals.astype(np.float32)), codes)
 
 
-def test_activation_scale_is_row_amax_over_448():
-    a = np.array([[28.0, 1.0, -2.0, 0.5], [0.0, -3.0, 1.5, 2.0], [0.0, 0.0, 0.0, 0.0]])
+def test_activation_scale_is_the_least_power_of_two_covering_the_row():
+    a = np.array([[28.0, 1.0, -2.0, 0.5], [0.0, -3.0, 1.5, 2.0], [0.0, 0.0, 0.0, 0.0],
+                  [28.5, 1.0, 0.0, 0.0], [448.0, -1.0, 0.0, 0.0], [449.0, 0.0, 0.0, 0.0]])
     q, s = oracle.quantise_rows(a)
-    assert s[0] == 0.0625 and s[1] == float(np.float32(3.0) / np.float32(448.0)) and s[2] == 1.0
-    # row 0: 28, 1, -2, 0.5 over 1/16 -> 448, 16, -32, 8 (codes 0x7E, 0x58, 0xE0, 0x50)
+    # 28 = 448 / 16 exactly; 3 <= 448 / 128 = 3.5 but > 448 / 256; 28.5 > 448 / 16; 449 > 448
+    np.testing.assert_array_equal(s, [2.0 ** -4, 2.0 ** -7, 1.0, 2.0 ** -3, 1.0, 2.0])
+    # row 0: 28, 1, -2, 0.5 times 16 -> 448, 16, -32, 8 (codes 0x7E, 0x58, 0xE0, 0x50)
     np.testing.assert_array_equal(q[0], [0x7E, 0x58, 0xE0, 0x50])
-    assert abs(fp8_codes_to_f64(q[1])[1]) == 448.0
+    # row 1: -3 * 128 = -384 (0xFC), 1.5 * 128 = 192 (0x74), 2 * 128 = 256 (0x78)
+    np.testing.assert_array_equal(q[1], [0x00, 0xFC, 0x74, 0x78])
     np.testing.assert_array_equal(q[2], 0)
+    for r in range(a.shape[0]):
+        assert np.abs(a[r]).max() <= 448.0 * s[r] and not np.abs(a[r]).max() <= 224.0 * s[r] or s[r] == 1.0
 
 
 def _torch_fp8_dequant(v, s):
-    """fp32(v / s) to the nearest e4m3 through torch's float8 cast, times s (float64)."""
+    """v / s (exact: s is a power of two) to the nearest e4m3 through torch's float8 cast, times s."""
     qv = torch.from_numpy((np.float32(v) / np.float32(s)).astype(np.float32)).to(torch.float8_e4m3fn)
     return qv.to(torch.float64).numpy() * float(s)
 
@@ -281,7 +286,7 @@ def test_fp8_token_quantisation_against_torch_fp8_cast():
         xv2 = xv.copy()
         xv2[2] = float(bf16_codes_to_f64(_bf16_bits([1.03]))[0])
         x2 = _bf16_bits(xv2)
-        xq = _torch_fp8_dequant(xv2, np.float32(28.0) / np.float32(448.0))
+        xq = _torch_fp8_dequant(xv2, 2.0 ** -4)
         assert xq[2] != xv2[2] and np.array_equal(xq[[0, 1]], xv2[[0, 1]])
         a8 = oracle.expert(x2, w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True)
         w8 = oracle.expert(_bf16_bits(xq), w_gu, w_d, s_gu, s_d, wtype="fp8", rounding=True)
@@ -292,7 +297,7 @@ def test_fp8_token_quantisation_against_torch_fp8_cast():
         xv, x, _, _, w_gu, w_d, s_gu, s_d = _act8_expert(seed, up_weight=1.5)
         xv2 = xv.copy()
         xv2[2] = float(bf16_codes_to_f64(_bf16_bits([1.1]))[0])
-        xq = _torch_fp8_dequant(xv2, np.float32(28.0) / np.float32(448.0))
+        xq = _torch_fp8_dequant(xv2, 2.0 ** -4)
         assert xq[2] == 1.125
         np.testing.assert_array_equal(
             oracle.expert(_bf16_bits(xv2), w_gu, w_d, s_gu, s_d, wtype="fp8a8", rounding=True),
@@ -301,12 +306,12 @@ def test_fp8_token_quantisation_against_torch_fp8_cast():
 
 def test_fp8_h_quantisation_against_torch_fp8_cast():
     """Up weight 1.125 puts h off the grid (x stays on it): the down sums run over torch's e4m3
-    cast of h / s_h times s_h, s_h = fp32(amax / 448)."""
+    cast of h / s_h times s_h, s_h = 4 (the h row's amax is 448 * 4)."""
     for seed in range(3):
         xv, x, src, wu, w_gu, w_d, s_gu, s_d = _act8_expert(seed, up_weight=1.125)
         h = 64.0 * wu * xv[src]
         assert np.abs(h).max() == 64.0 * 28.0
-        s_h = np.float32(np.float32(np.abs(h).max()) / np.float32(448.0))
+        s_h = 4.0  # amax 64 * 28 = 448 * 4
         hq = _torch_fp8_dequant(h, s_h)
         assert not np.array_equal(hq, h)
         ref = (fp8_codes_to_f64(w_d) @ hq) * s_d.astype(np.float64)
