@@ -37,6 +37,10 @@ def _load():
         lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
         lib.oracle_fp8_encode.restype = ctypes.c_uint8
         lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+        lib.oracle_fp4_value.restype = ctypes.c_double
+        lib.oracle_fp4_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         lib.oracle_quantise_row.restype = ctypes.c_double
         lib.oracle_quantise_row.argtypes = [_I, _P, _P]
         lib.oracle_router_logits.restype = None
@@ -114,7 +118,21 @@ def quantise_rows(a):
     return q, s
 
 
-WTYPES = {"bf16": 0, "fp8": 1, "fp8a8": 2}
+WTYPES = {"bf16": 0, "fp8": 1, "fp8a8": 2, "mxfp4": 3}
+
+
+def fp4_value(codes):
+    """Value of E2M1 codes (the low 4 bits of uint8) as float64."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_fp4_value(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e8m0_value(codes):
+    """Value of E8M0 scale bytes as float64."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e8m0_value(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
 
 
 # ---------------------------------------------------------------- routing
@@ -186,8 +204,9 @@ def _bank_arrays(layer, prefix):
     wdt = np.uint16 if wtype == 0 else np.uint8
     gu = _c(layer[prefix + "w_gate_up"], wdt)
     dn = _c(layer[prefix + "w_down"], wdt)
-    sgu = _c(layer.get(prefix + "s_gate_up"), np.float32) if wtype != 0 else None
-    sd = _c(layer.get(prefix + "s_down"), np.float32) if wtype != 0 else None
+    sdt = np.uint8 if wtype == 3 else np.float32
+    sgu = _c(layer.get(prefix + "s_gate_up"), sdt) if wtype != 0 else None
+    sd = _c(layer.get(prefix + "s_down"), sdt) if wtype != 0 else None
     return wtype, gu, dn, sgu, sd
 
 
@@ -234,8 +253,9 @@ def expert(x_t, w_gate_up, w_down, s_gate_up=None, s_down=None, wtype="bf16", ro
     dn = _c(w_down, wdt)
     H = x_t.shape[0]
     I = gu.shape[0] // 2
-    sgu = _c(s_gate_up, np.float32)
-    sdn = _c(s_down, np.float32)
+    sdt = np.uint8 if wt == 3 else np.float32
+    sgu = _c(s_gate_up, sdt)
+    sdn = _c(s_down, sdt)
     y = np.empty((H,), dtype=np.float64)
     lib.oracle_expert(H, I, wt, _ptr(x_t), _ptr(gu), _ptr(dn), _ptr(sgu), _ptr(sdn), 1 if rounding else 0, _ptr(y))
     return y

@@ -51,6 +51,11 @@
  *            cores' own (E8M0) scale format.  Each dot product is the exact sum of
  *            decoded codes times decoded weights, multiplied by the weight's
  *            row scale and the activation row's scale.
+ *   R-mx4    wtype 3 (MXFP4, OCP Microscaling Formats v1.0, the pages' 4-bit
+ *            routed experts in the gfx950-native form): weight (row, col) is
+ *            the E2M1 code in nibble col & 1 (low nibble first) of byte
+ *            col / 2 of the row, times 2^(X - 127) for the E8M0 byte X of
+ *            block col / 32 of the row; no other scale.
  *   R-round  the HIP path stores h, each expert's output y and the layer
  *            output as bf16.  With `rounding` set, the oracle rounds at the
  *            same three points (fp64 -> bf16, round-to-nearest-even, single
@@ -147,10 +152,25 @@ double oracle_quantise_row(int n, const double *a, uint8_t *q) {
   return ldexp(1.0, e);
 }
 
-/* weight element n of a bank stored as bf16 (wtype 0) or fp8 codes (wtypes 1, 2) */
-static double weight(const void *w, int wtype, size_t n) {
-  if (wtype == 0) return oracle_bf16_value(((const uint16_t *)w)[n]);
-  return oracle_fp8_value(((const uint8_t *)w)[n]);
+/* E2M1 code (low 4 bits): sign bit 3, exponent field E = bits 2..1 (bias 1), mantissa m =
+ * bit 0; E == 0 gives (-1)^s * m / 2, otherwise (-1)^s * 2^(E-1) * (1 + m/2). */
+double oracle_fp4_value(uint8_t c) {
+  int s = (c >> 3) & 1, E = (c >> 1) & 3, m = c & 1;
+  double mag = E == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, E - 1);
+  return s ? -mag : mag;
+}
+
+/* E8M0 scale byte: 2^(X - 127); 0xFF is NaN. */
+double oracle_e8m0_value(uint8_t X) { return X == 0xFF ? NAN : ldexp(1.0, (int)X - 127); }
+
+/* weight (row, col) of a matrix with `cols` columns: bf16 (wtype 0), fp8 codes (1, 2), or
+ * MXFP4 (3: codes two per byte, with the E8M0 block scales `sc`) -- R-mx4 above */
+static double weight(const void *w, const void *sc, int wtype, size_t row, size_t col, size_t cols) {
+  if (wtype == 0) return oracle_bf16_value(((const uint16_t *)w)[row * cols + col]);
+  if (wtype != 3) return oracle_fp8_value(((const uint8_t *)w)[row * cols + col]);
+  uint8_t b = ((const uint8_t *)w)[(row * cols + col) / 2];
+  uint8_t code = (col & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+  return oracle_fp4_value(code) * oracle_e8m0_value(((const uint8_t *)sc)[row * (cols / 32) + col / 32]);
 }
 
 static double silu(double g) { return g / (1.0 + exp(-g)); }
@@ -268,11 +288,13 @@ int oracle_align(int T, int k, int E, int BM, int64_t cap, const int32_t *ids, i
 /* One token through one SwiGLU expert of a bank (R-ffn, R-round).
  * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down projections).
  *   x [H] bf16 bits; w_gu [2I][H], w_d [H][I] (this expert's slices);
- *   s_gu [2I], s_d [H] row scales for fp8 (ignored for bf16);
+ *   s_gu [2I], s_d [H] row scales for fp8 (ignored for bf16); for MXFP4 the E8M0 block
+ *   scales, [2I][H/32] and [H][I/32] bytes;
  *   y [H] output in fp64 (bf16-rounded values when rounding != 0).
  * wtype 2 quantises x before the gate/up sums and h before the down sums (R-act8). */
 static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w_gu, const void *w_d,
-                       const float *s_gu, const float *s_d, int rounding, double *hbuf, double *y) {
+                       const void *sgu, const void *sd, int rounding, double *hbuf, double *y) {
+  const float *s_gu = (const float *)sgu, *s_d = (const float *)sd; /* fp8 row scales */
   double *xa = (double *)calloc((size_t)H, sizeof(double));
   uint8_t *q = (uint8_t *)malloc((size_t)(H > I ? H : I));
   for (int h = 0; h < H; ++h) xa[h] = oracle_bf16_value(x[h]);
@@ -284,10 +306,10 @@ static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w
   for (int r = 0; r < I; ++r) {
     double g = 0.0, u = 0.0;
     for (int h = 0; h < H; ++h) {
-      g += xa[h] * weight(w_gu, wtype, (size_t)r * H + h);
-      u += xa[h] * weight(w_gu, wtype, (size_t)(I + r) * H + h);
+      g += xa[h] * weight(w_gu, sgu, wtype, (size_t)r, (size_t)h, (size_t)H);
+      u += xa[h] * weight(w_gu, sgu, wtype, (size_t)(I + r), (size_t)h, (size_t)H);
     }
-    if (wtype != 0) {
+    if (wtype == 1 || wtype == 2) {
       g *= (double)s_gu[r];
       u *= (double)s_gu[I + r];
     }
@@ -304,8 +326,8 @@ static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w
   }
   for (int o = 0; o < H; ++o) {
     double acc = 0.0;
-    for (int r = 0; r < I; ++r) acc += hbuf[r] * weight(w_d, wtype, (size_t)o * I + r);
-    if (wtype != 0) acc *= (double)s_d[o];
+    for (int r = 0; r < I; ++r) acc += hbuf[r] * weight(w_d, sd, wtype, (size_t)o, (size_t)r, (size_t)I);
+    if (wtype == 1 || wtype == 2) acc *= (double)s_d[o];
     if (wtype == 2) acc *= sh;
     y[o] = rounding ? oracle_bf16_rounded(acc) : acc;
   }
@@ -313,7 +335,12 @@ static void expert_ffn(int H, int I, int wtype, const uint16_t *x, const void *w
   free(q);
 }
 
-static size_t elem_bytes(int wtype) { return wtype == 0 ? 2 : 1; }
+/* bytes of an n-element matrix, and of its scales (per-row fp32 for fp8; one E8M0 byte per
+ * 32 elements for MXFP4) for `rows` rows */
+static size_t matrix_bytes(int wtype, size_t n) { return wtype == 0 ? 2 * n : wtype == 3 ? n / 2 : n; }
+static size_t scale_bytes(int wtype, size_t rows, size_t n) {
+  return wtype == 3 ? n / 32 : (wtype == 1 || wtype == 2) ? 4 * rows : 0;
+}
 
 /* The layer for a list of tokens, routed by the given ids and gate weights:
  *   out[t] = sum_{j<k} w[t][j] * y_{e(t,j)}(x_t) + sigmoid(x_t . w_sg) * y_shared(x_t)
@@ -321,13 +348,14 @@ static size_t elem_bytes(int wtype) { return wtype == 0 ? 2 : 1; }
  * bf16 when rounding != 0 (R-round).  The shared expert is absent when I_s == 0.
  * Qwen3.8 Flash-Next . GB10 UltraFast, first bullet (combine without float
  * atomics: a fixed order); veloGB10 README, "The model" (shared expert).
- *   x [T][H] bf16; w_gu [E][2I][H]; w_d [E][H][I]; s_gu [E][2I]; s_d [E][H];
+ *   x [T][H] bf16; w_gu [E][2I][H]; w_d [E][H][I]; s_gu [E][2I]; s_d [E][H] (MXFP4:
+ *   [E][2I][H/32], [E][H][I/32] scale bytes);
  *   ids [T][k]; w [T][k] fp64; shared: ws_gu [2I_s][H], ws_d [H][I_s],
  *   ss_gu [2I_s], ss_d [H], w_sg [H] fp32;
  *   tokens [n_tok] (token indices to compute); out [n_tok][H] fp64. */
 void oracle_moe_layer(int T, int H, int E, int k, int I, int wtype, const uint16_t *x, const void *w_gu,
-                      const void *w_d, const float *s_gu, const float *s_d, const int32_t *ids, const double *w,
-                      int I_s, const void *ws_gu, const void *ws_d, const float *ss_gu, const float *ss_d,
+                      const void *w_d, const void *s_gu, const void *s_d, const int32_t *ids, const double *w,
+                      int I_s, const void *ws_gu, const void *ws_d, const void *ss_gu, const void *ss_d,
                       const float *w_sg, int n_tok, const int32_t *tokens, int rounding, double *out) {
   (void)T;
   (void)E;
@@ -335,17 +363,17 @@ void oracle_moe_layer(int T, int H, int E, int k, int I, int wtype, const uint16
   double *hbuf = (double *)malloc(sizeof(double) * (size_t)Imax);
   double *y = (double *)malloc(sizeof(double) * (size_t)H);
   double *acc = (double *)malloc(sizeof(double) * (size_t)H);
-  size_t eb = elem_bytes(wtype);
+  const size_t ngu = (size_t)2 * I * H, nd = (size_t)H * I;
   for (int q = 0; q < n_tok; ++q) {
     int t = tokens[q];
     const uint16_t *xt = x + (size_t)t * H;
     for (int o = 0; o < H; ++o) acc[o] = 0.0;
     for (int j = 0; j < k; ++j) {
       int e = ids[(size_t)t * k + j];
-      const char *gu = (const char *)w_gu + (size_t)e * 2 * I * H * eb;
-      const char *dn = (const char *)w_d + (size_t)e * H * I * eb;
-      const float *sg = wtype != 0 ? s_gu + (size_t)e * 2 * I : NULL;
-      const float *sd = wtype != 0 ? s_d + (size_t)e * H : NULL;
+      const char *gu = (const char *)w_gu + (size_t)e * matrix_bytes(wtype, ngu);
+      const char *dn = (const char *)w_d + (size_t)e * matrix_bytes(wtype, nd);
+      const char *sg = wtype != 0 ? (const char *)s_gu + (size_t)e * scale_bytes(wtype, 2 * (size_t)I, ngu) : NULL;
+      const char *sd = wtype != 0 ? (const char *)s_d + (size_t)e * scale_bytes(wtype, (size_t)H, nd) : NULL;
       expert_ffn(H, I, wtype, xt, gu, dn, sg, sd, rounding, hbuf, y);
       double wj = w[(size_t)t * k + j];
       for (int o = 0; o < H; ++o) acc[o] += wj * y[o];
@@ -366,7 +394,7 @@ void oracle_moe_layer(int T, int H, int E, int k, int I, int wtype, const uint16
 
 /* One expert applied to one token, exposed for the pins (y [H] fp64). */
 void oracle_expert(int H, int I, int wtype, const uint16_t *x, const void *w_gu, const void *w_d,
-                   const float *s_gu, const float *s_d, int rounding, double *y) {
+                   const void *s_gu, const void *s_d, int rounding, double *y) {
   double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
   expert_ffn(H, I, wtype, x, w_gu, w_d, s_gu, s_d, rounding, hbuf, y);
   free(hbuf);

@@ -33,10 +33,12 @@ def _load():
         lib.synth_normal_f32.argtypes = [_U64, _U64, _U64, _I64, ctypes.c_double, _P, ctypes.c_int]
         lib.synth_normal_bf16.argtypes = [_U64, _U64, _U64, _I64, ctypes.c_double, _P, ctypes.c_int]
         lib.synth_normal_fp8_rows.argtypes = [_U64, _U64, _U64, _I64, _I64, ctypes.c_double, _P, _P, ctypes.c_int]
+        lib.synth_normal_mxfp4_rows.argtypes = [_U64, _U64, _U64, _I64, _I64, ctypes.c_double, _P, _P, ctypes.c_int]
         lib.synth_uniform_f64.argtypes = [_U64, _U64, _U64, _I64, _P]
         lib.synth_permutation.argtypes = [_U64, _U64, ctypes.c_int32, _P]
         lib.synth_u64.argtypes = [_U64, _U64, _U64, _I64, _P]
-        for f in (lib.synth_normal_f32, lib.synth_normal_bf16, lib.synth_normal_fp8_rows, lib.synth_uniform_f64,
+        for f in (lib.synth_normal_f32, lib.synth_normal_bf16, lib.synth_normal_fp8_rows, lib.synth_normal_mxfp4_rows,
+                  lib.synth_uniform_f64,
                   lib.synth_permutation, lib.synth_u64):
             f.restype = None
         _lib = lib
@@ -63,6 +65,19 @@ def normal_fp8_rows(seed, tag, shape, std, first=0):
     scales = np.empty(shape[:-1], dtype=np.float32)
     _load().synth_normal_fp8_rows(seed, tag, first, rows, shape[-1], float(std), codes.ctypes.data,
                                   scales.ctypes.data, _threads())
+    return codes, scales
+
+
+def normal_mxfp4_rows(seed, tag, shape, std, first=0):
+    """MXFP4 of N(0, std^2) draws along the last axis: code bytes [..., L/2] (even value in the low
+    nibble) and E8M0 scale bytes [..., L/32], one per block of 32 values."""
+    L = shape[-1]
+    assert L % 32 == 0
+    rows = int(np.prod(shape[:-1]))
+    codes = np.empty(tuple(shape[:-1]) + (L // 2,), dtype=np.uint8)
+    scales = np.empty(tuple(shape[:-1]) + (L // 32,), dtype=np.uint8)
+    _load().synth_normal_mxfp4_rows(seed, tag, first, rows, L, float(std), codes.ctypes.data, scales.ctypes.data,
+                                    _threads())
     return codes, scales
 
 

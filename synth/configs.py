@@ -26,7 +26,7 @@ import math
 
 import numpy as np
 
-from . import normal_bf16, normal_f32, normal_fp8_rows, permutation
+from . import normal_bf16, normal_f32, normal_fp8_rows, normal_mxfp4_rows, permutation
 
 TAG_X, TAG_RW, TAG_RB, TAG_GU, TAG_DN, TAG_SGU, TAG_SDN, TAG_SG, TAG_PERM = range(1, 10)
 REPLICA_STRIDE = 100
@@ -41,6 +41,7 @@ class LayerConfig:
     I: int
     I_s: int          # 0: no shared expert
     wtype: str        # 'bf16' | 'fp8' | 'fp8a8' (fp8 weights; the prefill path also quantises activations)
+                      # | 'mxfp4' (4-bit E2M1 codes with an E8M0 scale per 32 values; decode path only)
     bias: str         # 'none' | 'normal' | 'zipf'
     BM: int
     bias_std: float = 0.5
@@ -68,6 +69,9 @@ CONFIGS = {
     "prefill": LayerConfig("prefill", H=2048, E=256, k=8, I=512, I_s=512, wtype="bf16", bias="none", BM=64),
     # the prefill chunk with fp8 e4m3 experts (row scales), the same shapes
     "prefill_fp8": LayerConfig("prefill_fp8", H=2048, E=256, k=8, I=512, I_s=512, wtype="fp8", bias="none", BM=64),
+    # the T=8 verify layer with MXFP4 routed and shared experts (4-bit decode GEMV)
+    "qwen36_a3b_mxfp4": LayerConfig("qwen36_a3b_mxfp4", H=2048, E=256, k=8, I=512, I_s=512, wtype="mxfp4",
+                                    bias="normal", BM=16),
     # the same fp8 experts with fp8 activations (one scale per token row and per h row)
     "prefill_fp8a8": LayerConfig("prefill_fp8a8", H=2048, E=256, k=8, I=512, I_s=512, wtype="fp8a8", bias="none",
                                  BM=64),
@@ -75,7 +79,7 @@ CONFIGS = {
 
 # Token counts each recipe is run at.
 TOKENS = {"tiny": (4,), "qwen36_a3b": (1, 8, 32), "qwen36_a3b_zipf": (32,), "flash_next_fp8": (1, 6),
-          "prefill": (4096,), "prefill_fp8": (4096,), "prefill_fp8a8": (4096,)}
+          "prefill": (4096,), "prefill_fp8": (4096,), "prefill_fp8a8": (4096,), "qwen36_a3b_mxfp4": (1, 8)}
 
 
 def _tag(tid, replica):
@@ -85,6 +89,8 @@ def _tag(tid, replica):
 def _weights(cfg, seed, tid, replica, shape, std):
     if cfg.wtype == "bf16":
         return normal_bf16(seed, _tag(tid, replica), shape, std), None
+    if cfg.wtype == "mxfp4":
+        return normal_mxfp4_rows(seed, _tag(tid, replica), shape, std)
     return normal_fp8_rows(seed, _tag(tid, replica), shape, std)
 
 

@@ -26,6 +26,13 @@
  *     finite 448): per row of `cols` values, scale s = max|w| / 448 as float
  *     (s = 1 when the row is all zero), code = round-to-nearest-even of w / s,
  *     saturated at +-448.
+ *   - MXFP4 (OCP Microscaling Formats v1.0): blocks of 32 consecutive values of
+ *     a row share one E8M0 scale byte X (value 2^(X-127)), X - 127 =
+ *     floor(log2(max|w| of the block)) - 2 (2 being the largest exponent of
+ *     E2M1), or X = 0 for an all-zero block; each value is stored as the E2M1
+ *     code (sign, 2 exponent bits, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5,
+ *     2, 3, 4, 6) nearest w / 2^(X-127), ties to an even mantissa, saturating
+ *     at 6.  Two codes per byte, the even-indexed value in the low nibble.
  */
 #include <math.h>
 #include <pthread.h>
@@ -96,11 +103,25 @@ static uint8_t encode_e4m3fn(float v) {
   return sign | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
 }
 
+/* E2M1 code of v (already divided by its block scale): nearest magnitude, ties to the code
+ * with an even mantissa bit, saturating at 6. */
+static uint8_t encode_e2m1(double v) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  uint8_t sign = (v < 0.0 || (v == 0.0 && signbit(v))) ? 0x8 : 0x0;
+  double a = fabs(v);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double d = fabs(mag[c] - a), db = fabs(mag[best] - a);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)(sign | best);
+}
+
 /* ------------------------------------------------------------------------ */
 /* threaded fill                                                              */
 
 typedef struct {
-  int kind;            /* 0 f32, 1 bf16, 2 fp8 rows */
+  int kind;            /* 0 f32, 1 bf16, 2 fp8 rows, 3 MXFP4 rows */
   uint64_t key;
   uint64_t first;      /* stream index of element 0 */
   int64_t lo, hi;      /* element range (rows for kind 2) */
@@ -119,6 +140,33 @@ static void *fill_worker(void *arg) {
     uint16_t *o = (uint16_t *)j->out;
     for (int64_t i = j->lo; i < j->hi; ++i)
       o[i] = float_to_bf16_rne((float)(draw_normal(j->key, j->first + (uint64_t)i) * j->std));
+  } else if (j->kind == 3) {
+    uint8_t *o = (uint8_t *)j->out, *sc = (uint8_t *)j->scales;
+    const int64_t nb = j->cols / 32;
+    float blk[32];
+    for (int64_t r = j->lo; r < j->hi; ++r) {
+      for (int64_t b = 0; b < nb; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+          uint64_t n = j->first + (uint64_t)(r * j->cols + b * 32 + i);
+          blk[i] = (float)(draw_normal(j->key, n) * j->std);
+          if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+        }
+        int X = 0;
+        if (amax > 0.0f) {
+          int e;
+          frexp((double)amax, &e); /* amax in [2^(e-1), 2^e) */
+          X = (e - 1) - 2 + 127;
+          if (X < 0) X = 0;
+          if (X > 254) X = 254;
+        }
+        sc[r * nb + b] = (uint8_t)X;
+        const double inv = ldexp(1.0, 127 - X);
+        for (int i = 0; i < 32; i += 2)
+          o[(r * j->cols + b * 32 + i) / 2] =
+              (uint8_t)(encode_e2m1(blk[i] * inv) | (encode_e2m1(blk[i + 1] * inv) << 4));
+      }
+    }
   } else {
     uint8_t *o = (uint8_t *)j->out;
     float *row = (float *)malloc(sizeof(float) * (size_t)j->cols);
@@ -142,8 +190,8 @@ static void *fill_worker(void *arg) {
 static void run_fill(fill_job base, int64_t n_items, int threads) {
   if (threads < 1) threads = 1;
   if (threads > 64) threads = 64;
-  if (n_items < 65536 * (int64_t)threads && base.kind != 2) threads = (int)(n_items / 65536) + 1;
-  if (base.kind == 2 && n_items < threads) threads = (int)(n_items > 0 ? n_items : 1);
+  if (n_items < 65536 * (int64_t)threads && base.kind < 2) threads = (int)(n_items / 65536) + 1;
+  if (base.kind >= 2 && n_items < threads) threads = (int)(n_items > 0 ? n_items : 1);
   pthread_t tid[64];
   fill_job jobs[64];
   for (int t = 0; t < threads; ++t) {
@@ -175,6 +223,14 @@ void synth_normal_bf16(uint64_t seed, uint64_t tag, uint64_t first, int64_t n, d
 void synth_normal_fp8_rows(uint64_t seed, uint64_t tag, uint64_t first, int64_t rows, int64_t cols, double std,
                            uint8_t *codes, float *scales, int threads) {
   fill_job j = {2, stream_key(seed, tag), first, 0, rows, std, cols, codes, scales};
+  run_fill(j, rows, threads);
+}
+
+/* rows x cols normal draws times std as MXFP4: cols / 2 code bytes and cols / 32 E8M0
+ * scale bytes per row (cols a multiple of 32). */
+void synth_normal_mxfp4_rows(uint64_t seed, uint64_t tag, uint64_t first, int64_t rows, int64_t cols, double std,
+                             uint8_t *codes, uint8_t *scales, int threads) {
+  fill_job j = {3, stream_key(seed, tag), first, 0, rows, std, cols, codes, (float *)(void *)scales};
   run_fill(j, rows, threads);
 }
 

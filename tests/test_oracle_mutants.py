@@ -34,11 +34,12 @@ MUTANTS = [
     ("block map shifted", "block_expert[p / BM] = e;", "block_expert[p / BM] = e + 1;"),
     ("capacity ignores padding", "int64_t c = n + touched * (BM - 1);", "int64_t c = n + touched;"),
     ("silu sign flipped", "return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
-    ("gate reads the up rows", "g += xa[h] * weight(w_gu, wtype, (size_t)r * H + h);",
-     "g += xa[h] * weight(w_gu, wtype, (size_t)(I + r) * H + h);"),
-    ("down operand transposed", "acc += hbuf[r] * weight(w_d, wtype, (size_t)o * I + r);",
-     "acc += hbuf[r] * weight(w_d, wtype, (size_t)r * H + o);"),
-    ("fp8 down scale dropped", "if (wtype != 0) acc *= (double)s_d[o];", "if (wtype != 0) acc *= 1.0;"),
+    ("gate reads the up rows", "g += xa[h] * weight(w_gu, sgu, wtype, (size_t)r, (size_t)h, (size_t)H);",
+     "g += xa[h] * weight(w_gu, sgu, wtype, (size_t)(I + r), (size_t)h, (size_t)H);"),
+    ("down operand transposed", "acc += hbuf[r] * weight(w_d, sd, wtype, (size_t)o, (size_t)r, (size_t)I);",
+     "acc += hbuf[r] * weight(w_d, sd, wtype, (size_t)r, (size_t)o, (size_t)H);"),
+    ("fp8 down scale dropped", "if (wtype == 1 || wtype == 2) acc *= (double)s_d[o];",
+     "if (wtype == 1 || wtype == 2) acc *= 1.0;"),
     ("fp8 up scale from the gate row", "u *= (double)s_gu[I + r];", "u *= (double)s_gu[r];"),
     ("combine weight dropped", "acc[o] += wj * y[o];", "acc[o] += y[o];"),
     ("shared gate dropped", "acc[o] += gamma * y[o];", "acc[o] += y[o];"),
@@ -62,6 +63,13 @@ MUTANTS = [
      "    for (int h = 0; h < H; ++h) xa[h] = xa[h] / sx;\n"),
     ("h not quantised", "    for (int r = 0; r < I; ++r) hbuf[r] = oracle_fp8_value(q[r]);\n",
      "    for (int r = 0; r < I; ++r) hbuf[r] = hbuf[r] / sh;\n"),
+    ("fp4 nibble order swapped", "(col & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15)",
+     "(col & 1) ? (uint8_t)(b & 15) : (uint8_t)(b >> 4)"),
+    ("fp4 subnormal step", "double mag = E == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, E - 1);",
+     "double mag = E == 0 ? 1.0 * m : ldexp(1.0 + 0.5 * m, E - 1);"),
+    ("e8m0 bias", "ldexp(1.0, (int)X - 127)", "ldexp(1.0, (int)X - 126)"),
+    ("mxfp4 scale block of the wrong row", "((const uint8_t *)sc)[row * (cols / 32) + col / 32]",
+     "((const uint8_t *)sc)[col / 32]"),
     ("h not rounded", "hbuf[r] = rounding ? oracle_bf16_rounded(a) : a;", "hbuf[r] = a;"),
     ("expert output not rounded", "y[o] = rounding ? oracle_bf16_rounded(acc) : acc;", "y[o] = acc;"),
 ]

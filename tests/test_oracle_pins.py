@@ -319,6 +319,70 @@ def test_fp8_h_quantisation_against_torch_fp8_cast():
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=0)
 
 
+# ---------------------------------------------------------------- MXFP4 (4-bit experts)
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX v1.0, the E2M1 magnitudes by code
+
+
+def test_fp4_value_all_codes():
+    codes = np.arange(16, dtype=np.uint8)
+    got = oracle.fp4_value(codes)
+    ref = np.array(E2M1 + [-v for v in E2M1])
+    np.testing.assert_array_equal(got, ref)
+    assert math.copysign(1.0, got[8]) < 0  # -0
+
+
+def test_e8m0_value_is_a_power_of_two():
+    X = np.arange(256, dtype=np.uint8)
+    got = oracle.e8m0_value(X)
+    np.testing.assert_array_equal(got[:255], [math.ldexp(1.0, int(x) - 127) for x in range(255)])
+    assert math.isnan(got[255])
+
+
+def mxfp4_dequant(codes, scales):
+    """[rows][L/2] code bytes (low nibble first) and [rows][L/32] E8M0 bytes -> [rows][L] float64,
+    by a table and numpy's ldexp (independent of the oracle)."""
+    lut = np.array(E2M1 + [-v for v in E2M1])
+    lo = lut[codes & 15]
+    hi = lut[codes >> 4]
+    vals = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return vals * np.repeat(sc, 32, axis=-1)
+
+
+def test_single_mxfp4_expert_is_textbook_swiglu_on_dequantised_weights():
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], E=1, k=1, wtype="mxfp4")
+    L = configs.make_layer(cfg, seed=8)
+    x = configs.make_tokens(cfg, 3, seed=8)
+    got = oracle.moe_layer(x, L, np.zeros((3, 1), np.int32), np.ones((3, 1)), rounding=False)
+    Wgu = mxfp4_dequant(L["w_gate_up"][0], L["s_gate_up"][0])
+    Wd = mxfp4_dequant(L["w_down"][0], L["s_down"][0])
+    ref = _torch_swiglu(torch.from_numpy(bf16_codes_to_f64(x)), torch.from_numpy(Wgu), torch.from_numpy(Wd),
+                        cfg.I).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_mxfp4_layer_with_shared_equals_dense_dequantised():
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="mxfp4", I_s=64, k=2)
+    L = configs.make_layer(cfg, seed=9)
+    x = configs.make_tokens(cfg, 4, seed=9)
+    ids, w = oracle.route_topk(oracle.router_logits(x, L["router_w"]).astype(np.float32), cfg.k)
+    got = oracle.moe_layer(x, L, ids, w, rounding=False)
+    X = torch.from_numpy(bf16_codes_to_f64(x))
+    ref = np.zeros_like(got)
+    for t in range(4):
+        for j in range(cfg.k):
+            e = ids[t, j]
+            y = _torch_swiglu(X[t:t + 1], torch.from_numpy(mxfp4_dequant(L["w_gate_up"][e], L["s_gate_up"][e])),
+                              torch.from_numpy(mxfp4_dequant(L["w_down"][e], L["s_down"][e])), cfg.I).numpy()[0]
+            ref[t] += w[t, j] * y
+    z = (bf16_codes_to_f64(x) @ L["shared_gate_w"].astype(np.float64))
+    ys = _torch_swiglu(X, torch.from_numpy(mxfp4_dequant(L["shared_w_gate_up"], L["shared_s_gate_up"])),
+                       torch.from_numpy(mxfp4_dequant(L["shared_w_down"], L["shared_s_down"])), cfg.I_s).numpy()
+    ref += scipy.special.expit(z)[:, None] * ys
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
 def test_fp8a8_layer_is_the_fp8a8_experts_combined():
     cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="fp8a8", I_s=32, k=2)
     L = configs.make_layer(cfg, seed=12)

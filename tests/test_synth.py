@@ -45,6 +45,25 @@ def test_fp8_rows_match_torch_cast_and_scale_rule():
     assert np.all((codes & 0x7F) != 0x7F)                # never NaN
 
 
+def test_mxfp4_rows_follow_the_mx_scale_rule_and_nearest_codes():
+    codes, scales = synth.normal_mxfp4_rows(2, 7, (16, 256), 0.05)
+    f = synth.normal_f32(2, 7, (16, 256), 0.05).astype(np.float64)
+    blocks = f.reshape(16, 8, 32)
+    amax = np.abs(blocks).max(axis=2)
+    # X - 127 = floor(log2(amax)) - 2: each block's largest value over 2^(X-127) is in [4, 8)
+    r = amax / np.ldexp(1.0, scales.astype(np.int64) - 127)
+    assert np.all((r >= 4.0) & (r < 8.0))
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    v = blocks / np.ldexp(1.0, scales.astype(np.int64) - 127)[:, :, None]
+    d = np.abs(np.abs(v)[..., None] - mags)                     # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    tie_even = np.where(d == best, np.arange(8) % 2, 9)         # among the nearest, the even code
+    m = np.where((d == best).sum(-1) > 1, np.argmin(tie_even, axis=-1), np.argmin(d, axis=-1))
+    ref = (m | np.where(v < 0, 8, 0)).reshape(16, 256).astype(np.uint8)
+    got = np.stack([codes & 15, codes >> 4], axis=-1).reshape(16, 256)
+    assert np.array_equal(got, ref)
+
+
 def test_permutation_is_a_permutation():
     p = synth.permutation(0, 9, 512)
     assert sorted(p.tolist()) == list(range(512))
