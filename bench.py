@@ -33,6 +33,9 @@ WORKLOADS = {
     "qwen36_T32": ("qwen36_a3b", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32 (two 16-position blocks)"),
     "qwen36_zipf_T32": ("qwen36_a3b_zipf", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32, Zipf(1.1) expert load"),
     "flash_fp8_T1": ("flash_next_fp8", 1, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=1 decode"),
+    "qwen36_mxfp4_T8": ("qwen36_a3b_mxfp4", 8, "Qwen3.6-35B-A3B-like MoE layer with MXFP4 (4-bit) experts, "
+                        "T=8 verify block"),
+    "qwen36_mxfp4_T1": ("qwen36_a3b_mxfp4", 1, "Qwen3.6-35B-A3B-like MoE layer with MXFP4 (4-bit) experts, T=1 decode"),
     "flash_fp8_T6": ("flash_next_fp8", 6, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=6 MTP verify block"),
     "prefill_T4096": ("prefill", 4096, "Qwen3.6-35B-A3B-like MoE layer, 4096-token prefill chunk"),
     "prefill_fp8_T4096": ("prefill_fp8", 4096, "Qwen3.6-35B-A3B-like MoE layer with fp8 e4m3 experts, 4096-token prefill chunk"),
@@ -148,14 +151,15 @@ def main():
     for r in range(L_rep):
         hr = configs.make_layer(cfg, seed=0, replica=r, with_experts=False)
         act8 = base.routed.wtype == moe.MOE_W_FP8_E4M3_A8
+        mx = base.routed.wtype == moe.MOE_W_MXFP4
         routed = moe.Bank(base.routed.w_gate_up.clone(), base.routed.w_down.clone(),
                           None if base.routed.s_gate_up is None else base.routed.s_gate_up.clone(),
-                          None if base.routed.s_down is None else base.routed.s_down.clone(), act8)
+                          None if base.routed.s_down is None else base.routed.s_down.clone(), act8, mx)
         shared = None
         if base.shared is not None:
             shared = moe.Bank(base.shared.w_gate_up.clone(), base.shared.w_down.clone(),
                               None if base.shared.s_gate_up is None else base.shared.s_gate_up.clone(),
-                              None if base.shared.s_down is None else base.shared.s_down.clone(), act8)
+                              None if base.shared.s_down is None else base.shared.s_down.clone(), act8, mx)
         rb = None if hr["router_b"] is None else torch.from_numpy(hr["router_b"]).to(dev)
         sg = None if cfg.I_s == 0 else torch.from_numpy(hr["shared_gate_w"]).to(dev)
         lay = moe.Layer(torch.from_numpy(hr["router_w"]).to(dev), rb, routed, cfg.k, shared, sg, cfg.renormalize)
@@ -185,17 +189,24 @@ def main():
         torch.cuda.synchronize()
         touched.append(len(np.unique(ids.cpu().numpy())))
 
-    bw = 2 if cfg.wtype == "bf16" else 1
     H, I, I_s, E, k = cfg.H, cfg.I, cfg.I_s, cfg.E, cfg.k
-    srow = 4 if cfg.wtype in ("fp8", "fp8a8") else 0  # fp32 row scales
+
+    def mat(rows, cols):
+        # bytes of a weight matrix with its scales: bf16; fp8 codes + one fp32 per row; MXFP4
+        # codes (half a byte) + one E8M0 byte per 32 weights
+        if cfg.wtype == "bf16":
+            return rows * cols * 2
+        if cfg.wtype == "mxfp4":
+            return rows * cols // 2 + rows * cols // 32
+        return rows * cols + rows * 4
 
     def gate_up_bytes(nt):
         # weights of every touched expert (+ shared) once, tokens read, h written
-        w = nt * (2 * I * H * bw + 2 * I * srow) + (2 * I_s * H * bw + 2 * I_s * srow if I_s else 0)
+        w = nt * mat(2 * I, H) + (mat(2 * I_s, H) if I_s else 0)
         return w + T * H * 2 + T * k * I * 2 + T * I_s * 2
 
     def layer_bytes(nt):
-        w = nt * (3 * I * H * bw + (2 * I + H) * srow) + ((3 * I_s * H * bw + (2 * I_s + H) * srow) if I_s else 0)
+        w = nt * (mat(2 * I, H) + mat(H, I)) + ((mat(2 * I_s, H) + mat(H, I_s)) if I_s else 0)
         router = E * H * 4 + (E * 4 if host_routers[0]["router_b"] is not None else 0) + (H * 4 if I_s else 0)
         return w + router + 2 * T * H * 2
 
@@ -308,7 +319,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
                                                "fp8a8": "fp8-e4m3 weights and activations (row scales), "
-                                                        "fp32 accumulate"}[cfg.wtype],
+                                                        "fp32 accumulate",
+                                               "mxfp4": "mxfp4 (e2m1 + e8m0 block scales) weights, bf16 "
+                                                        "activations"}[cfg.wtype],
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "hidden": H, "experts": E, "top_k": k, "inter": I,
                    "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep,

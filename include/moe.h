@@ -77,8 +77,17 @@ typedef enum {
  *     nearest code, ties to an even mantissa) -- and the expert GEMMs run on the fp8
  *     matrix cores (Qwen3.8 Flash-Next . GB10 UltraFast and veloGB10 README, FP8
  *     layers; gfx950 fp8 MFMA).  The decode path (T <= 64) streams the same weights
- *     with bf16 activations, exactly as MOE_W_FP8_E4M3. */
-typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1, MOE_W_FP8_E4M3_A8 = 2 } moe_wtype;
+ *     with bf16 activations, exactly as MOE_W_FP8_E4M3.
+ *   MOE_W_MXFP4: OCP MX (Microscaling) FP4 -- E2M1 codes, two per byte with the
+ *     even-indexed weight in the low nibble, w_gate_up [n][2I][H/2] and w_down
+ *     [n][H][I/2] bytes; s_gate_up [n][2I][H/32] and s_down [n][H][I/32] hold one
+ *     E8M0 scale byte (2^(X-127)) per block of 32 consecutive weights of a row (the
+ *     scale pointers are then byte arrays, no alignment needed).  4-bit routed experts
+ *     with 16-bit activations (Qwen3.8 Flash-Next . GB10 UltraFast, "Target
+ *     precision"; Qwen3.6-35B-A3B for NInfer, "Artifact"; veloGB10 README, NVFP4 packs),
+ *     in the format gfx950 converts natively.  Decode path only (T <= 64): a prefill
+ *     chunk returns MOE_ERR_UNSUPPORTED. */
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1, MOE_W_FP8_E4M3_A8 = 2, MOE_W_MXFP4 = 3 } moe_wtype;
 
 /* A bank of experts of one form (routed: n = E experts; shared: n = 1).
  * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down per expert). */
@@ -89,8 +98,8 @@ typedef struct {
   int32_t inter;           /* I, multiple of 64 */
   const void *w_gate_up;   /* [n][2I][H]: rows [0,I) gate, rows [I,2I) up */
   const void *w_down;      /* [n][H][I] */
-  const float *s_gate_up;  /* fp8 only: [n][2I] row scales; NULL for bf16 */
-  const float *s_down;     /* fp8 only: [n][H] row scales; NULL for bf16 */
+  const float *s_gate_up;  /* fp8: [n][2I] row scales; MXFP4: E8M0 block scale bytes (cast); NULL for bf16 */
+  const float *s_down;     /* fp8: [n][H] row scales; MXFP4: E8M0 block scale bytes (cast); NULL for bf16 */
 } moe_bank;
 
 /* One MoE layer.  veloGB10 README, "The model". */

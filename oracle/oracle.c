@@ -51,8 +51,9 @@
  *            cores' own (E8M0) scale format.  Each dot product is the exact sum of
  *            decoded codes times decoded weights, multiplied by the weight's
  *            row scale and the activation row's scale.
- *   R-mx4    wtype 3 (MXFP4, OCP Microscaling Formats v1.0, the pages' 4-bit
- *            routed experts in the gfx950-native form): weight (row, col) is
+ *   R-mx4    wtype 3 (MXFP4, OCP Microscaling Formats v1.0; 4-bit routed experts
+ *            with 16-bit activations as in Qwen3.8 Flash-Next . GB10 UltraFast,
+ *            "Target precision", in the gfx950-native form): weight (row, col) is
  *            the E2M1 code in nibble col & 1 (low nibble first) of byte
  *            col / 2 of the row, times 2^(X - 127) for the E8M0 byte X of
  *            block col / 32 of the row; no other scale.

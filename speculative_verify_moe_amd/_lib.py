@@ -19,7 +19,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(6)
-MOE_W_BF16, MOE_W_FP8_E4M3, MOE_W_FP8_E4M3_A8 = 0, 1, 2
+MOE_W_BF16, MOE_W_FP8_E4M3, MOE_W_FP8_E4M3_A8, MOE_W_MXFP4 = 0, 1, 2, 3
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -95,22 +95,32 @@ def _workspace(nbytes, device):
 class Bank:
     """A bank of n experts: w_gate_up [n][2I][H], w_down [n][H][I] (bf16, or uint8 fp8 codes
     with fp32 row scales s_gate_up [n][2I], s_down [n][H]).  ``act8`` (fp8 banks only): the
-    prefill path quantises the activations too (MOE_W_FP8_E4M3_A8).  Holds the tensors alive."""
+    prefill path quantises the activations too (MOE_W_FP8_E4M3_A8).  ``mxfp4``: uint8 code bytes
+    w_gate_up [n][2I][H/2], w_down [n][H][I/2] with uint8 E8M0 block scales s_gate_up
+    [n][2I][H/32], s_down [n][H][I/32] (MOE_W_MXFP4).  Holds the tensors alive."""
 
-    def __init__(self, w_gate_up, w_down, s_gate_up=None, s_down=None, act8=False):
+    def __init__(self, w_gate_up, w_down, s_gate_up=None, s_down=None, act8=False, mxfp4=False):
         self.w_gate_up, self.w_down, self.s_gate_up, self.s_down = w_gate_up, w_down, s_gate_up, s_down
-        fp8 = w_gate_up.dtype == torch.uint8
+        fp8 = w_gate_up.dtype == torch.uint8 and not mxfp4
         if act8 and not fp8:
             raise ValueError("act8 needs fp8 (uint8) weights")
-        self.wtype = (MOE_W_FP8_E4M3_A8 if act8 else MOE_W_FP8_E4M3) if fp8 else MOE_W_BF16
+        if mxfp4:
+            self.wtype = MOE_W_MXFP4
+        else:
+            self.wtype = (MOE_W_FP8_E4M3_A8 if act8 else MOE_W_FP8_E4M3) if fp8 else MOE_W_BF16
         gu = w_gate_up if w_gate_up.dim() == 3 else w_gate_up.unsqueeze(0)
         self.num_experts, two_i, self.hidden = gu.shape
+        if mxfp4:
+            self.hidden *= 2
         self.inter = two_i // 2
-        _dev(w_gate_up, torch.uint8 if fp8 else torch.bfloat16, "w_gate_up")
+        _dev(w_gate_up, torch.uint8 if (fp8 or mxfp4) else torch.bfloat16, "w_gate_up")
         _dev(w_down, w_gate_up.dtype, "w_down")
         if fp8:
             _dev(s_gate_up, torch.float32, "s_gate_up")
             _dev(s_down, torch.float32, "s_down")
+        if mxfp4:
+            _dev(s_gate_up, torch.uint8, "s_gate_up")
+            _dev(s_down, torch.uint8, "s_down")
 
     def struct(self):
         return _Bank(self.wtype, self.num_experts, self.hidden, self.inter, _ptr(self.w_gate_up), _ptr(self.w_down),
@@ -149,11 +159,12 @@ class Layer:
             return None if a is None else torch.from_numpy(a).to(device)
 
         act8 = L.get("wtype") == "fp8a8"
-        routed = Bank(wt(L["w_gate_up"]), wt(L["w_down"]), f32(L.get("s_gate_up")), f32(L.get("s_down")), act8)
+        mx = L.get("wtype") == "mxfp4"
+        routed = Bank(wt(L["w_gate_up"]), wt(L["w_down"]), f32(L.get("s_gate_up")), f32(L.get("s_down")), act8, mx)
         shared = None
         if L.get("I_s", 0) > 0:
             shared = Bank(wt(L["shared_w_gate_up"]), wt(L["shared_w_down"]), f32(L.get("shared_s_gate_up")),
-                          f32(L.get("shared_s_down")), act8)
+                          f32(L.get("shared_s_down")), act8, mx)
         return cls(f32(L["router_w"]), f32(L.get("router_b")), routed, L["k"], shared,
                    f32(L.get("shared_gate_w")), L.get("renormalize", True))
 

@@ -94,8 +94,10 @@ moe_status launched(hipError_t e, const char *what) {
 
 // ---------------------------------------------------------------- bank validation
 moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, int n_expected) {
-  if (b->wtype != MOE_W_BF16 && b->wtype != MOE_W_FP8_E4M3 && b->wtype != MOE_W_FP8_E4M3_A8)
-    return fail(MOE_ERR_INVALID_ARG, "%s.wtype = %d: must be MOE_W_BF16 (0), MOE_W_FP8_E4M3 (1) or MOE_W_FP8_E4M3_A8 (2)",
+  if (b->wtype != MOE_W_BF16 && b->wtype != MOE_W_FP8_E4M3 && b->wtype != MOE_W_FP8_E4M3_A8 &&
+      b->wtype != MOE_W_MXFP4)
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s.wtype = %d: must be MOE_W_BF16 (0), MOE_W_FP8_E4M3 (1), MOE_W_FP8_E4M3_A8 (2) or MOE_W_MXFP4 (3)",
                 name, b->wtype);
   if (need_n && b->num_experts != n_expected)
     return fail(MOE_ERR_INVALID_ARG, "%s.num_experts = %d: expected %d", name, b->num_experts, n_expected);
@@ -106,7 +108,10 @@ moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, i
     return fail(MOE_ERR_INVALID_ARG, "%s: w_gate_up and w_down are required", name);
   if (!aligned16(b->w_gate_up) || !aligned16(b->w_down))
     return fail(MOE_ERR_MISALIGNED, "%s: weight pointers must be 16-byte aligned", name);
-  if (b->wtype != MOE_W_BF16) {
+  if (b->wtype == MOE_W_MXFP4) {
+    if (b->s_gate_up == nullptr || b->s_down == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "%s: MXFP4 weights need s_gate_up and s_down block scales", name);
+  } else if (b->wtype != MOE_W_BF16) {
     if (b->s_gate_up == nullptr || b->s_down == nullptr)
       return fail(MOE_ERR_INVALID_ARG, "%s: fp8 weights need s_gate_up and s_down row scales", name);
     if (!aligned4(b->s_gate_up) || !aligned4(b->s_down))
@@ -213,6 +218,9 @@ moe_status validate_layer(int T, const moe_layer *L) {
     if (!aligned16(L->shared_gate_w)) return fail(MOE_ERR_MISALIGNED, "shared_gate_w must be 16-byte aligned");
   }
   if (T > 0 && !is_decode(T, L->top_k)) {
+    if (L->routed.wtype == MOE_W_MXFP4)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP4 experts run on the decode path only (T <= %d and T*k <= %d; T = %d)",
+                  kDecodeMaxT, kSmallSlots, T);
     if (L->hidden % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", L->hidden);
     // fp8 activations: 128 codes of K per stage in both expert GEMMs
@@ -367,6 +375,8 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
   if (!decode) {
     if (BM != 64 && BM != 128) return fail(MOE_ERR_UNSUPPORTED, "the prefill path needs BM = 64 or 128 (got %d)", BM);
     if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "prefill path needs hidden %% 128 == 0 (hidden = %d)", H);
+    if (routed->wtype == MOE_W_MXFP4)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP4 experts run on the decode path only (T <= %d; T = %d)", kDecodeMaxT, T);
     if (routed->wtype == MOE_W_FP8_E4M3_A8 && routed->inter % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "fp8 activations on the prefill path need inter %% 128 == 0 (inter = %d)",
                   routed->inter);
@@ -453,7 +463,7 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
   const LayerPlan p = plan_layer(T, L);
   const int E = L->num_experts, k = L->top_k;
   const bool shared = L->shared.num_experts > 0;
-  if (p.path == PATH_DECODE && g_opt_fused != 0 &&
+  if (p.path == PATH_DECODE && g_opt_fused != 0 && L->routed.wtype != MOE_W_MXFP4 &&
       fused_decode_fits(T, L->hidden, E, k, L->routed.inter, shared ? L->shared.inter : 0,
                         decode_wtype(L->routed.wtype))) {
     snprintf(g_plan, sizeof(g_plan),
@@ -513,7 +523,8 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
               (int32_t *)(base + p.off_offsets), (int32_t *)(base + p.off_np)};
   Stager sg;
 
-  const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 &&
+  // (MXFP4 experts run on the GEMV kernels: the fused kernel streams bf16 and fp8 codes)
+  const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 && L->routed.wtype != MOE_W_MXFP4 &&
                      fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0,
                                        decode_wtype(L->routed.wtype));
   if (fused) {

@@ -63,13 +63,38 @@ __device__ __forceinline__ void copy_to_lds(uint4 *dst, const uint4 *src, int n,
   for (int i = threadIdx.x; i < n; i += nthreads) dst[i] = src[i];
 }
 
+// MXFP4: 32 E2M1 codes of one scale block (byte b holds values 2b in its low nibble and
+// 2b + 1 in its high nibble) against 32 bf16 activations x[0..3]; v_cvt_scalef32_pk_bf16_fp4
+// widens two codes exactly (scale 1), the block scale multiplies the finished block sum.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+__device__ __forceinline__ float dot32_fp4_bf16(const uint4 &w, const uint4 *x) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint4 xv = x[d];
+    acc = dot2_bf16(fp4x2_to_bf16x2<0>(wd[d]), xv.x, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<1>(wd[d]), xv.y, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<2>(wd[d]), xv.z, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<3>(wd[d]), xv.w, acc);
+  }
+  return acc;
+}
+// E8M0 scale byte -> 2^(X - 127) (0xFF: NaN)
+__device__ __forceinline__ float e8m0_scale(uint32_t X) {
+  return X == 0xFFu ? __builtin_nanf("") : ldexpf(1.0f, (int)X - 127);
+}
+
 // ============================================================ gate/up
-// ESZ: bytes per weight (2 bf16, 1 fp8 codes).  CG: 16-byte groups per lane per row.
-template <int ESZ, int CG, bool XLDS>
+// VPG: weights per 16-byte group (8 bf16, 16 fp8 codes, 32 MXFP4 codes, which are also one
+// scale block).  CG: 16-byte groups per lane per row.
+template <int VPG, int CG, bool XLDS>
 __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NT = kGuNW * kWave;
-  constexpr int VPG = 16 / ESZ;  // weights per 16-byte group
   const int lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
   const int r0 = blockIdx.x * 2;
   const bool do_routed = r0 < a.I;
@@ -80,33 +105,39 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
   const int G = H / VPG;       // groups per weight row
   const int G8 = H / 8;        // 16-byte groups per token row
 
-  // weight row of this lane for entry `ent` (expert id known)
-  auto row_of = [&](int ent, int e) -> const uint4 * {
-    const uint8_t *bank;
+  // weight row of this lane for entry `ent` (expert id known), and its MXFP4 block scales
+  auto row_of = [&](int ent, int e, const uint8_t *&srow) -> const uint4 * {
+    const uint8_t *bank, *sbank;
     int Iw;
     if (ent < nr) {
-      bank = (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
+      bank = (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * G * 16;
+      sbank = (const uint8_t *)a.s_gu + (size_t)e * 2 * a.I * G;
       Iw = a.I;
     } else {
       bank = (const uint8_t *)a.ws_gu;
+      sbank = (const uint8_t *)a.ss_gu;
       Iw = a.I_s;
     }
     const int row = rg < 2 ? r0 + rg : Iw + r0 + (rg - 2);
-    return reinterpret_cast<const uint4 *>(bank + (size_t)row * H * ESZ);
+    srow = VPG == 32 ? sbank + (size_t)row * G : nullptr;
+    return reinterpret_cast<const uint4 *>(bank + (size_t)row * G * 16);
   };
   uint4 wa[CG], wb[CG];
-  auto load = [&](uint4(&w)[CG], int ent, int e) {
-    const uint4 *p = row_of(ent, e);
+  uint32_t xa[VPG == 32 ? CG : 1], xb[VPG == 32 ? CG : 1];  // MXFP4: scale byte of each group
+  auto load = [&](uint4(&w)[CG], uint32_t(&xs)[VPG == 32 ? CG : 1], int ent, int e) {
+    const uint8_t *srow;
+    const uint4 *p = row_of(ent, e, srow);
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       const int g = l16 + 16 * c;
       w[c] = g < G ? ld_stream(p + g) : make_uint4(0, 0, 0, 0);
+      if (VPG == 32) xs[c] = g < G ? srow[g] : 127u;
     }
   };
 
   // first entry's rows go out before the staging below
   int ent = wave;
-  if (ent < NE) load(wa, ent, ent < nr ? a.tl_e[ent] : 0);
+  if (ent < NE) load(wa, xa, ent, ent < nr ? a.tl_e[ent] : 0);
 
   int32_t *lbase = reinterpret_cast<int32_t *>(smem);
   const ListLds lst = stage_list(a, nr, lbase, NT);
@@ -120,13 +151,16 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
   }
   __syncthreads();
 
-  auto compute = [&](const uint4(&w)[CG], int ent) {
+  auto compute = [&](const uint4(&w)[CG], const uint32_t(&ws)[VPG == 32 ? CG : 1], int ent) {
     const bool routed = ent < nr;
     const int e = routed ? lst.e[ent] : 0;
     const int q0 = routed ? lst.start[ent] : 0;
     const int q1 = routed ? lst.start[ent + 1] : a.T;
+    float bsc[VPG == 32 ? CG : 1];  // MXFP4 block scales of the lane's groups
+#pragma unroll
+    for (int c = 0; c < (VPG == 32 ? CG : 1); ++c) bsc[c] = VPG == 32 ? e8m0_scale(ws[c]) : 1.0f;
     float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
-    if (ESZ == 1) {
+    if (VPG == 16) {
       const float *sc = routed ? a.s_gu + (size_t)e * 2 * a.I : a.ss_gu;
       const int Iw = routed ? a.I : a.I_s;
       sg0 = sc[r0];
@@ -143,8 +177,10 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
       for (int c = 0; c < CG; ++c) {
         const int g = l16 + 16 * c;
         if (g < G) {
-          if (ESZ == 2) {
+          if (VPG == 8) {
             acc = dot8_bf16(w[c], xr[g], acc);
+          } else if (VPG == 32) {
+            acc = fmaf(dot32_fp4_bf16(w[c], xr + 4 * g), bsc[c], acc);
           } else {
             const uint4 x0 = xr[2 * g], x1 = xr[2 * g + 1];
             acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[c].x), x0.x, acc);
@@ -171,12 +207,12 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
 
   while (ent < NE) {
     const int e2 = ent + kGuNW;
-    if (e2 < NE) load(wb, e2, e2 < nr ? lst.e[e2] : 0);
-    compute(wa, ent);
+    if (e2 < NE) load(wb, xb, e2, e2 < nr ? lst.e[e2] : 0);
+    compute(wa, xa, ent);
     if (e2 >= NE) break;
     const int e3 = e2 + kGuNW;
-    if (e3 < NE) load(wa, e3, e3 < nr ? lst.e[e3] : 0);
-    compute(wb, e2);
+    if (e3 < NE) load(wa, xa, e3, e3 < nr ? lst.e[e3] : 0);
+    compute(wb, xb, e2);
     ent = e3;
   }
 }
@@ -184,39 +220,39 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
 // ============================================================ down + combine
 // CG: 16-byte groups per lane per weight row; each lane holds two rows (o0 + rg and
 // o0 + 4 + rg).
-template <int ESZ, int CG, bool HLDS>
+template <int VPG, int CG, bool HLDS>
 __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NT = kDnNW * kWave;
-  constexpr int VPG = 16 / ESZ;
+  constexpr int NS = VPG == 32 ? CG : 1;  // MXFP4 scale bytes per lane and row
   const int lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
   const int o0 = blockIdx.x * kDnRows;
   const int nr = a.tl_n[0];
   const int NE = nr + (a.has_shared ? 1 : 0);
   const int n_slots = a.T * a.k;
 
-  auto rows_of = [&](int ent, int e) -> const uint8_t * {
-    if (ent < nr) return (const uint8_t *)a.w_d + (size_t)e * a.H * a.I * ESZ;
-    return (const uint8_t *)a.ws_d;
-  };
   uint4 wa[2][CG], wb[2][CG];
-  auto load = [&](uint4(&w)[2][CG], int ent, int e) {
-    const uint8_t *bank = rows_of(ent, e);
+  uint32_t xa[2][NS], xb[2][NS];  // MXFP4: scale byte of each group
+  auto load = [&](uint4(&w)[2][CG], uint32_t(&xs)[2][NS], int ent, int e) {
     const int K = ent < nr ? a.I : a.I_s;
     const int G = K / VPG;
+    const uint8_t *bank = ent < nr ? (const uint8_t *)a.w_d + (size_t)e * a.H * G * 16 : (const uint8_t *)a.ws_d;
+    const uint8_t *sbank = ent < nr ? (const uint8_t *)a.s_d + (size_t)e * a.H * G : (const uint8_t *)a.ss_d;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(bank + (size_t)(o0 + 4 * s + rg) * K * ESZ);
+      const int row = o0 + 4 * s + rg;
+      const uint4 *p = reinterpret_cast<const uint4 *>(bank + (size_t)row * G * 16);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
         const int g = l16 + 16 * c;
         w[s][c] = g < G ? ld_stream(p + g) : make_uint4(0, 0, 0, 0);
+        if (VPG == 32) xs[s][c] = g < G ? sbank[(size_t)row * G + g] : 127u;
       }
     }
   };
 
   int ent = wave;
-  if (ent < NE) load(wa, ent, ent < nr ? a.tl_e[ent] : 0);
+  if (ent < NE) load(wa, xa, ent, ent < nr ? a.tl_e[ent] : 0);
 
   // LDS: list, y [T*k][8] fp32, y_s [T][8] fp32, then h [T*k][I] and h_s [T][I_s] bf16
   int32_t *lbase = reinterpret_cast<int32_t *>(smem);
@@ -238,15 +274,20 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
   }
   __syncthreads();
 
-  auto compute = [&](const uint4(&w)[2][CG], int ent) {
+  auto compute = [&](const uint4(&w)[2][CG], const uint32_t(&ws)[2][NS], int ent) {
     const bool routed = ent < nr;
     const int e = routed ? lst.e[ent] : 0;
     const int K = routed ? a.I : a.I_s;
     const int G = K / VPG;
     const int q0 = routed ? lst.start[ent] : 0;
     const int q1 = routed ? lst.start[ent + 1] : a.T;
+    float bsc[2][NS];  // MXFP4 block scales
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c = 0; c < NS; ++c) bsc[s][c] = VPG == 32 ? e8m0_scale(ws[s][c]) : 1.0f;
     float sc0 = 1.f, sc1 = 1.f;
-    if (ESZ == 1) {
+    if (VPG == 16) {
       const float *sc = routed ? a.s_d + (size_t)e * a.H : a.ss_d;
       sc0 = sc[o0 + rg];
       sc1 = sc[o0 + 4 + rg];
@@ -259,10 +300,13 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
       for (int c = 0; c < CG; ++c) {
         const int g = l16 + 16 * c;
         if (g < G) {
-          if (ESZ == 2) {
+          if (VPG == 8) {
             const uint4 hv = hr[g];
             acc0 = dot8_bf16(w[0][c], hv, acc0);
             acc1 = dot8_bf16(w[1][c], hv, acc1);
+          } else if (VPG == 32) {
+            acc0 = fmaf(dot32_fp4_bf16(w[0][c], hr + 4 * g), bsc[0][c], acc0);
+            acc1 = fmaf(dot32_fp4_bf16(w[1][c], hr + 4 * g), bsc[1][c], acc1);
           } else {
             const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
 #pragma unroll
@@ -294,12 +338,12 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
 
   while (ent < NE) {
     const int e2 = ent + kDnNW;
-    if (e2 < NE) load(wb, e2, e2 < nr ? lst.e[e2] : 0);
-    compute(wa, ent);
+    if (e2 < NE) load(wb, xb, e2, e2 < nr ? lst.e[e2] : 0);
+    compute(wa, xa, ent);
     if (e2 >= NE) break;
     const int e3 = e2 + kDnNW;
-    if (e3 < NE) load(wa, e3, e3 < nr ? lst.e[e3] : 0);
-    compute(wb, e2);
+    if (e3 < NE) load(wa, xa, e3, e3 < nr ? lst.e[e3] : 0);
+    compute(wb, xb, e2);
     ent = e3;
   }
   __syncthreads();
@@ -344,15 +388,15 @@ static hipError_t set_lds(const void *kernel, size_t bytes) {
   return hipSuccess;
 }
 
-template <int ESZ, int CG>
+template <int VPG, int CG>
 static hipError_t launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, bool xlds, size_t lds) {
   if (xlds) {
-    auto k = gemv_gate_up_kernel<ESZ, CG, true>;
+    auto k = gemv_gate_up_kernel<VPG, CG, true>;
     hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
   } else {
-    auto k = gemv_gate_up_kernel<ESZ, CG, false>;
+    auto k = gemv_gate_up_kernel<VPG, CG, false>;
     launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
   }
   return hipGetLastError();
@@ -365,32 +409,38 @@ hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, siz
   const size_t xbytes = (size_t)a.T * a.H * 2;
   const bool xlds = lb + xbytes <= kLdsMax;
   const size_t lds = lb + (xlds ? xbytes : 0);
-  const int esz = a.wtype == 0 ? 2 : 1;
-  const int groups = a.H * esz / 16;          // 16-byte groups per weight row
+  const int vpg = a.wtype == 0 ? 8 : a.wtype == 3 ? 32 : 16;
+  const int groups = a.H / vpg;               // 16-byte groups per weight row
   const int cg = (groups + 15) / 16;
-  if (desc) snprintf(desc, desc_len, "gemv_gate_up<esz=%d,CG=%d,XLDS=%d> grid=%u block=%d lds=%zu", esz, cg, (int)xlds, grid.x, kGuNW * kWave, lds);
-  if (esz == 2) {
-    if (cg <= 4) return launch_gu<2, 4>(a, s, grid, xlds, lds);
-    if (cg <= 8) return launch_gu<2, 8>(a, s, grid, xlds, lds);
-    if (cg <= 16) return launch_gu<2, 16>(a, s, grid, xlds, lds);
-    if (cg <= 32) return launch_gu<2, 32>(a, s, grid, xlds, lds);
+  if (desc) snprintf(desc, desc_len, "gemv_gate_up<vpg=%d,CG=%d,XLDS=%d> grid=%u block=%d lds=%zu", vpg, cg, (int)xlds, grid.x, kGuNW * kWave, lds);
+  if (vpg == 8) {
+    if (cg <= 4) return launch_gu<8, 4>(a, s, grid, xlds, lds);
+    if (cg <= 8) return launch_gu<8, 8>(a, s, grid, xlds, lds);
+    if (cg <= 16) return launch_gu<8, 16>(a, s, grid, xlds, lds);
+    if (cg <= 32) return launch_gu<8, 32>(a, s, grid, xlds, lds);
+  } else if (vpg == 16) {
+    if (cg <= 4) return launch_gu<16, 4>(a, s, grid, xlds, lds);
+    if (cg <= 8) return launch_gu<16, 8>(a, s, grid, xlds, lds);
+    if (cg <= 16) return launch_gu<16, 16>(a, s, grid, xlds, lds);
   } else {
-    if (cg <= 4) return launch_gu<1, 4>(a, s, grid, xlds, lds);
-    if (cg <= 8) return launch_gu<1, 8>(a, s, grid, xlds, lds);
-    if (cg <= 16) return launch_gu<1, 16>(a, s, grid, xlds, lds);
+    if (cg <= 1) return launch_gu<32, 1>(a, s, grid, xlds, lds);
+    if (cg <= 2) return launch_gu<32, 2>(a, s, grid, xlds, lds);
+    if (cg <= 4) return launch_gu<32, 4>(a, s, grid, xlds, lds);
+    if (cg <= 8) return launch_gu<32, 8>(a, s, grid, xlds, lds);
+    if (cg <= 16) return launch_gu<32, 16>(a, s, grid, xlds, lds);
   }
   return hipErrorInvalidValue;
 }
 
-template <int ESZ, int CG>
+template <int VPG, int CG>
 static hipError_t launch_dn(const GemvArgs &a, hipStream_t s, dim3 grid, bool hlds, size_t lds) {
   if (hlds) {
-    auto k = gemv_down_kernel<ESZ, CG, true>;
+    auto k = gemv_down_kernel<VPG, CG, true>;
     hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
   } else {
-    auto k = gemv_down_kernel<ESZ, CG, false>;
+    auto k = gemv_down_kernel<VPG, CG, false>;
     hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
@@ -406,18 +456,22 @@ hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t
   const size_t hbytes = n_slots * a.I * 2 + (a.has_shared ? (size_t)a.T * a.I_s * 2 : 0);
   const bool hlds = base + hbytes <= kLdsMax;
   const size_t lds = base + (hlds ? hbytes : 0);
-  const int esz = a.wtype == 0 ? 2 : 1;
+  const int vpg = a.wtype == 0 ? 8 : a.wtype == 3 ? 32 : 16;
   const int kmax = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
-  const int groups = kmax * esz / 16;
+  const int groups = kmax / vpg;
   const int cg = (groups + 15) / 16;
-  if (desc) snprintf(desc, desc_len, "gemv_down_combine<esz=%d,CG=%d,HLDS=%d> grid=%u block=%d lds=%zu", esz, cg, (int)hlds, grid.x, kDnNW * kWave, lds);
-  if (esz == 2) {
-    if (cg <= 2) return launch_dn<2, 2>(a, s, grid, hlds, lds);
-    if (cg <= 4) return launch_dn<2, 4>(a, s, grid, hlds, lds);
-    if (cg <= 8) return launch_dn<2, 8>(a, s, grid, hlds, lds);
+  if (desc) snprintf(desc, desc_len, "gemv_down_combine<vpg=%d,CG=%d,HLDS=%d> grid=%u block=%d lds=%zu", vpg, cg, (int)hlds, grid.x, kDnNW * kWave, lds);
+  if (vpg == 8) {
+    if (cg <= 2) return launch_dn<8, 2>(a, s, grid, hlds, lds);
+    if (cg <= 4) return launch_dn<8, 4>(a, s, grid, hlds, lds);
+    if (cg <= 8) return launch_dn<8, 8>(a, s, grid, hlds, lds);
+  } else if (vpg == 16) {
+    if (cg <= 2) return launch_dn<16, 2>(a, s, grid, hlds, lds);
+    if (cg <= 4) return launch_dn<16, 4>(a, s, grid, hlds, lds);
   } else {
-    if (cg <= 2) return launch_dn<1, 2>(a, s, grid, hlds, lds);
-    if (cg <= 4) return launch_dn<1, 4>(a, s, grid, hlds, lds);
+    if (cg <= 1) return launch_dn<32, 1>(a, s, grid, hlds, lds);
+    if (cg <= 2) return launch_dn<32, 2>(a, s, grid, hlds, lds);
+    if (cg <= 4) return launch_dn<32, 4>(a, s, grid, hlds, lds);
   }
   return hipErrorInvalidValue;
 }

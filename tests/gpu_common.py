@@ -8,13 +8,13 @@ import torch
 import oracle
 from synth import configs
 
-TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3}
+TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3, "mxfp4": 5e-3}
 # max-abs bars, as a fraction of max |ref|.  fp8 activations on the prefill path: the device's
 # h (fp32 sums rounded to bf16) can differ from the oracle's (fp64 sums) by one bf16 step,
 # which now and then moves an h code by one e4m3 step (at most 1/8 of that element) or a row's
 # scale (every code of the row by at most one step); one slot's output then moves by a few
 # percent of max |ref|.  The relL2 bar still binds the whole output.
-MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 5e-2}
+MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 5e-2, "mxfp4": 1e-2}
 
 
 def runs_decode_path(T, k):

@@ -145,6 +145,9 @@ LAYER_CASES = [
     ("prefill_T200", "prefill", 200, [0, 64, 127, 128, 199]),
     ("prefill_fp8_T4096", "prefill_fp8", 4096, [0, 1, 63, 64, 777, 2048, 3001, 4095]),
     ("prefill_fp8_T200", "prefill_fp8", 200, [0, 64, 127, 128, 199]),
+    ("qwen36_mxfp4_T1", "qwen36_a3b_mxfp4", 1, None),
+    ("qwen36_mxfp4_T8", "qwen36_a3b_mxfp4", 8, None),
+    ("qwen36_mxfp4_T32", "qwen36_a3b_mxfp4", 32, None),
     ("prefill_fp8a8_T4096", "prefill_fp8a8", 4096, [0, 1, 63, 64, 777, 2048, 3001, 4095]),
     ("prefill_fp8a8_T200", "prefill_fp8a8", 200, [0, 64, 127, 128, 199]),
 ]
@@ -225,6 +228,25 @@ def test_fp8a8_prefill_tiny_shapes():
                 _check_act8_is_quantised(L, x, rep)
 
 
+def test_mxfp4_tiny_shapes():
+    """MXFP4 experts at the tiny size: one token to a full decode block, with and without a
+    shared expert, k = 1, and H not a multiple of 512; a prefill chunk is refused."""
+    from speculative_verify_moe_amd import MoeError, moe_layer_forward
+    for v in (dict(wtype="mxfp4"), dict(wtype="mxfp4", I_s=64, bias="normal"), dict(wtype="mxfp4", k=1),
+              dict(wtype="mxfp4", H=192, I=64, I_s=128)):
+        for T in (1, 4, 64):
+            cfg = configs.with_shape(configs.CONFIGS["tiny"], **v)
+            _say(f"[mxfp4] {v} T={T}")
+            L = configs.make_layer(cfg, seed=6)
+            rep = {}
+            G.check_layer(L, configs.make_tokens(cfg, T, seed=6), report=rep)
+            _say(f"[mxfp4] relL2={rep['rel_l2']:.3e}")
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="mxfp4")
+    D = G.device_layer(configs.make_layer(cfg, seed=6))
+    with pytest.raises(MoeError, match="decode path only"):
+        moe_layer_forward(G.to_dev_bf16(configs.make_tokens(cfg, 100, seed=6)), D)
+
+
 def test_fp8a8_needs_inter_multiple_of_128_on_the_prefill_path():
     from speculative_verify_moe_amd import MoeError, moe_layer_forward
     cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="fp8a8", I=64)
@@ -259,6 +281,7 @@ def _digest(bits):
 
 
 @pytest.mark.parametrize("recipe,T,runs", [("qwen36_a3b", 8, 20), ("flash_next_fp8", 6, 10), ("prefill", 4096, 5),
+                                           ("qwen36_a3b_mxfp4", 8, 10),
                                            ("prefill_fp8a8", 4096, 3),
                                            ("prefill_fp8", 4096, 3)])
 def test_bitwise_deterministic(recipe, T, runs):
@@ -275,10 +298,11 @@ def test_bitwise_deterministic(recipe, T, runs):
     assert len(digests) == 1
 
 
-def test_verify_block_rows_equal_single_token_calls():
+@pytest.mark.parametrize("recipe", ["qwen36_a3b", "qwen36_a3b_mxfp4"])
+def test_verify_block_rows_equal_single_token_calls(recipe):
     """Row t of a T=8 verify-block call is bitwise the T=1 call on token t (decode path)."""
     from speculative_verify_moe_amd import moe_layer_forward
-    cfg = configs.CONFIGS["qwen36_a3b"]
+    cfg = configs.CONFIGS[recipe]
     D = G.device_layer(G.host_layer(cfg))
     xb = configs.make_tokens(cfg, 8)
     x = G.to_dev_bf16(xb)
@@ -292,7 +316,7 @@ def test_verify_block_rows_equal_single_token_calls():
 
 @pytest.mark.parametrize("recipe,T,BM", [("tiny", 4, 16), ("qwen36_a3b", 8, 16), ("tiny", 300, 64),
                                          ("prefill", 4096, 64), ("tiny", 130, 128), ("prefill_fp8", 4096, 64),
-                                         ("prefill_fp8a8", 4096, 64)])
+                                         ("prefill_fp8a8", 4096, 64), ("qwen36_a3b_mxfp4", 8, 16)])
 def test_experts_forward_parity(recipe, T, BM):
     from speculative_verify_moe_amd import moe_align, moe_experts_forward, moe_route_topk
     _say(f"[experts] {recipe} T={T} BM={BM}")
