@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--four-kernel", action="store_true", help="run decode blocks as four kernels, not the fused one")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eager calls instead of replays of one captured HIP graph per replica")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times) for the HBM counter calibration")
     return p.parse_args()
@@ -212,16 +214,47 @@ def main():
 
     flops_layer = 2 * T * k * 3 * H * I + (2 * T * 3 * H * I_s if I_s else 0)
 
-    # ---- warmup
-    for i in range(args.warmup):
-        r = i % L_rep
-        moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
+    # ---- HIP graphs: one of the L replicas' calls in a row (steps i .. i+L-1 for i a multiple
+    # of L), and one of the first K mod L of them, so that K steps are K // L replays of the
+    # first and one of the second; the timed steps carry no per-call host overhead (the layer
+    # call allocates nothing and captures as is)
+    K = args.steps
+    graphs = {}
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        for n in sorted({L_rep, K % L_rep} - {0}):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for r in range(n):
+                    moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
+            graphs[n] = g
+        torch.cuda.synchronize()
+
+    def run_steps(n_steps):
+        if graphs:
+            for _ in range(n_steps // L_rep):
+                graphs[L_rep].replay()
+            if n_steps % L_rep:
+                graphs[n_steps % L_rep].replay()
+        else:
+            for i in range(n_steps):
+                r = i % L_rep
+                moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
+
+    # ---- warmup (whole rounds of the replicas)
+    run_steps(-(-args.warmup // L_rep) * L_rep)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events on every stage's kernels (launch stream)
-    K = args.steps
+    # ---- timed region: exactly K steps
+    t_start = time.perf_counter()
+    run_steps(K)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    # ---- kernel durations: the same K steps once more as eager calls, with HIP events on every
+    # stage's kernels (attached to the kernel dispatches by the library, on the launch stream).
     # stage s of step i: events[i][2s] at its first kernel's start, events[i][2s+1] at its last
-    # kernel's end (attached to the kernel dispatches by the library)
+    # kernel's end
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(K)]
     stream = torch.cuda.current_stream()
     for evs in events:
@@ -229,14 +262,12 @@ def main():
             ev.record(stream)
     handles = [moe.stage_event_handles(evs) for evs in events]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for i in range(K):
         r = i % L_rep
         moe.moe_set_stage_events(handles[i])
         moe.moe_layer_forward(xs[r], layers[r], out=outs[r], ws=wss[r])
     moe.moe_set_stage_events(None)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
 
     stage_ms = np.zeros((K, nst))
     for i in range(K):
@@ -328,6 +359,8 @@ def main():
                    "path": plan.split()[0].split("=")[1]},
         "roofline": roofline, "layer": layer, "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1), "device": torch.cuda.get_device_name(0),
+        "timing": ("HIP graph replays (one graph per round of the replicas)" if graphs else "eager calls")
+                  + "; kernel durations from HIP events on a second pass of the same steps",
     }
     print(json.dumps(line), flush=True)
 
