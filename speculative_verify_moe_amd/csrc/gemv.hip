@@ -135,8 +135,12 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
     }
   };
 
+  // blocks (b, y) for y < gridDim.y share row pair b and split the entries: wavefront w of
+  // block y takes entries y*NW + w, then every NW*gridDim.y-th (more of a small weight
+  // format in flight per row pair)
+  const int NWS = kGuNW * gridDim.y;
   // first entry's rows go out before the staging below
-  int ent = wave;
+  int ent = blockIdx.y * kGuNW + wave;
   if (ent < NE) load(wa, xa, ent, ent < nr ? a.tl_e[ent] : 0);
 
   int32_t *lbase = reinterpret_cast<int32_t *>(smem);
@@ -206,11 +210,11 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
   };
 
   while (ent < NE) {
-    const int e2 = ent + kGuNW;
+    const int e2 = ent + NWS;
     if (e2 < NE) load(wb, xb, e2, e2 < nr ? lst.e[e2] : 0);
     compute(wa, xa, ent);
     if (e2 >= NE) break;
-    const int e3 = e2 + kGuNW;
+    const int e3 = e2 + NWS;
     if (e3 < NE) load(wa, xa, e3, e3 < nr ? lst.e[e3] : 0);
     compute(wb, xb, e2);
     ent = e3;
@@ -410,6 +414,7 @@ hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, siz
   const bool xlds = lb + xbytes <= kLdsMax;
   const size_t lds = lb + (xlds ? xbytes : 0);
   const int vpg = a.wtype == 0 ? 8 : a.wtype == 3 ? 32 : 16;
+  if (vpg == 32) grid.y = 2;                  // 4-bit rows are short: two blocks per row pair
   const int groups = a.H / vpg;               // 16-byte groups per weight row
   const int cg = (groups + 15) / 16;
   if (desc) snprintf(desc, desc_len, "gemv_gate_up<vpg=%d,CG=%d,XLDS=%d> grid=%u block=%d lds=%zu", vpg, cg, (int)xlds, grid.x, kGuNW * kWave, lds);
