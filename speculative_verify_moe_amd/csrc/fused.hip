@@ -90,11 +90,16 @@ __device__ __forceinline__ void consume(const uint4 (&w)[N]) {
 
 // flags[kMaxBlocks]: per-block arrival words, then the release word and a timeout count.
 // Every wavefront that wrote data the other blocks will read calls wait_stores() first.
-__device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
-  const unsigned nb = gridDim.x;
-  unsigned *rel = flags + kMaxBlocks;
+// The barrier is split in two: grid_arrive stores the block's arrival word once every
+// wavefront got there; grid_wait polls for the release.  Work issued between the two
+// (loads only) overlaps the wait without delaying the arrival.
+__device__ __forceinline__ void grid_arrive(unsigned *flags, unsigned token) {
   __syncthreads();
   if (threadIdx.x == 0) st_agent(&flags[blockIdx.x], token);
+}
+__device__ __forceinline__ void grid_wait(unsigned *flags, unsigned token) {
+  const unsigned nb = gridDim.x;
+  unsigned *rel = flags + kMaxBlocks;
   if (blockIdx.x == 0 && threadIdx.x < kWave) {
     unsigned spins = 0;
     while (true) {
@@ -131,6 +136,10 @@ __device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
   }
   asm volatile("" ::: "memory");
   __syncthreads();
+}
+__device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
+  grid_arrive(flags, token);
+  grid_wait(flags, token);
 }
 
 // Block barrier for LDS data only: waits for this wavefront's LDS operations but not for
@@ -557,20 +566,22 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return __builtin_amdgcn_readfirstlane(v);
   };
   wait_stores();  // this wavefront's h stores
-  // Four entries in flight per wavefront.  Wavefronts 1..7 issue the first two before the
-  // barrier (wavefront 0 polls it and keeps its load queue empty), so the barrier wait
-  // streams weights.  After the barrier the h loads go first and the other two entries'
-  // weights right behind them: loads return in issue order, so h is not held up by them,
-  // and the weight stream continues while h is staged.
+  // Four entries in flight per wavefront.  Wavefronts 1..7 issue the first two between the
+  // block's arrival and the wait for the release (wavefront 0 polls and keeps its load
+  // queue empty), so the barrier wait streams weights and the arrival waits for none of
+  // them.  After the barrier the h loads go first and the other two entries' weights
+  // right behind them: loads return in issue order, so h is not held up by them, and the
+  // weight stream continues while h is staged.
   int qb1 = 0, qb2 = 0, qb3 = 0, qb4 = 0;
   const bool early = wave != 0;
+  grid_arrive(a.bar, tok0 + 2u);
   if (early) {
     qb1 = grab_b();
     qb2 = grab_b();
     dn_load(da, qb1);
     dn_load(db, qb2);
   }
-  grid_barrier(a.bar, tok0 + 2u);
+  grid_wait(a.bar, tok0 + 2u);
   // (after the barrier the tokens are dead: y and h take the data region)
   float *s_y = reinterpret_cast<float *>(data);  // [T*k][8]
   float *s_ys = s_y + (size_t)n_slots * kOct;   // [T][8]
