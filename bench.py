@@ -71,8 +71,8 @@ def parse():
 # sources each dominant kernel is built from: a counter summary is valid only for this text
 CSRC = "speculative_verify_moe_amd/csrc/"
 KERNEL_SOURCES = {
-    "moe_decode_fused": [CSRC + "fused.hip", CSRC + "topk.h", CSRC + "device.h"],
-    "gemv_gate_up": [CSRC + "gemv.hip", CSRC + "device.h"],
+    "moe_decode_fused": [CSRC + "fused.hip", CSRC + "topk.h", CSRC + "device.h", CSRC + "mxfp4.h"],
+    "gemv_gate_up": [CSRC + "gemv.hip", CSRC + "device.h", CSRC + "mxfp4.h"],
     "gemm_gate_up_mfma": [CSRC + "gemm.hip", CSRC + "device.h"],
 }
 

@@ -463,7 +463,7 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
   const LayerPlan p = plan_layer(T, L);
   const int E = L->num_experts, k = L->top_k;
   const bool shared = L->shared.num_experts > 0;
-  if (p.path == PATH_DECODE && g_opt_fused != 0 && L->routed.wtype != MOE_W_MXFP4 &&
+  if (p.path == PATH_DECODE && g_opt_fused != 0 &&
       fused_decode_fits(T, L->hidden, E, k, L->routed.inter, shared ? L->shared.inter : 0,
                         decode_wtype(L->routed.wtype))) {
     snprintf(g_plan, sizeof(g_plan),
@@ -523,8 +523,7 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
               (int32_t *)(base + p.off_offsets), (int32_t *)(base + p.off_np)};
   Stager sg;
 
-  // (MXFP4 experts run on the GEMV kernels: the fused kernel streams bf16 and fp8 codes)
-  const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 && L->routed.wtype != MOE_W_MXFP4 &&
+  const bool fused = p.path == PATH_DECODE && g_opt_fused != 0 &&
                      fused_decode_fits(T, H, E, k, L->routed.inter, shared ? L->shared.inter : 0,
                                        decode_wtype(L->routed.wtype));
   if (fused) {

@@ -40,6 +40,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "mxfp4.h"
 #include "topk.h"
 
 namespace moe {
@@ -150,12 +151,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int ESZ, int CGU, int CGD, int CR>
+// VPG: weights per 16-byte column group -- 8 bf16, 16 fp8 codes, or 32 MXFP4 codes (which
+// are also one scale block).  CGU / CGD: column groups per lane and weight row in phase A /
+// phase B; CR: float4 router groups per lane.
+template <int VPG, int CGU, int CGD, int CR>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void moe_decode_fused_kernel(FusedArgs a) {
-  static_assert(16 * CGU * (16 / ESZ) == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
-  static_assert(16 * CGD * (16 / ESZ) == kHW, "lanes must span an h row");
+  static_assert(16 * CGU * VPG == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
+  static_assert(16 * CGD * VPG == kHW, "lanes must span an h row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int VPG = 16 / ESZ;
+  constexpr bool kFp4 = VPG == 32;
+  constexpr int NSU = kFp4 ? CGU : 1, NSD = kFp4 ? CGD : 1;  // MXFP4 scale bytes per lane and row
+  // bytes of n weights (n even)
+  auto nbytes = [](auto n) { return kFp4 ? n / 2 : n * (16 / VPG); };
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), rg = lane >> 4, l16 = lane & 15;
   const int NB = gridDim.x;
   const int T = a.T, H = a.H, E = a.E, k = a.k;
@@ -212,6 +219,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
   const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
   uint4 wa[CGU], wb[CGU];
+  uint32_t xa[NSU], xb[NSU];  // MXFP4: the E8M0 scale byte of each of the lane's groups
   // Weight rows are streamed with raw buffer loads: the expert's matrix is the buffer (base
   // in scalar registers), the lane's row and column offset one VGPR, the column group a
   // uniform scalar offset.  Exactly CGU (CGD per row set) load instructions, all in range:
@@ -223,24 +231,32 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto as_u4 = [](i4_t v) { return make_uint4(v.x, v.y, v.z, v.w); };
   // the lane's byte offset in an expert's gate/up matrix for row pair p (gate rows 2p, 2p+1,
   // up rows Iw+2p, Iw+2p+1): fixed for the whole phase, computed once
-  auto gu_voff = [&](int Iw, int p) {
-    const int row = rg < 2 ? 2 * p + rg : Iw + 2 * p + (rg - 2);
-    return row * H * ESZ + l16 * 16;
-  };
+  auto gu_row = [&](int Iw, int p) { return rg < 2 ? 2 * p + rg : Iw + 2 * p + (rg - 2); };
+  auto gu_voff = [&](int Iw, int p) { return nbytes(gu_row(Iw, p) * H) + l16 * 16; };
+  // MXFP4: the lane's byte offset in the matching scale matrix (one byte per group)
+  auto gu_soff = [&](int Iw, int p) { return gu_row(Iw, p) * (H / VPG) + l16; };
   // valid == false: an empty descriptor, so the loads return zeros without reading memory
   // (they still issue, which keeps every wait count the same on all paths)
-  auto gu_load = [&](uint4(&w)[CGU], bool valid, bool shared, int e, int voff) {
+  auto gu_load = [&](uint4(&w)[CGU], uint32_t(&xs)[NSU], bool valid, bool shared, int e, int voff, int soff) {
     e = __builtin_amdgcn_readfirstlane(e);  // uniform (read from LDS): the descriptor stays scalar
     const int Iw = shared ? a.I_s : a.I;
-    const uint8_t *bank = shared ? (const uint8_t *)a.ws_gu : (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * H * ESZ;
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_gu : (const uint8_t *)a.w_gu + nbytes((size_t)e * 2 * a.I * H);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
-                                                                        valid ? 2 * Iw * H * ESZ : 0, 0x00020000);
+                                                                        valid ? nbytes(2 * Iw * H) : 0, 0x00020000);
     const int last = H / VPG / 16 - 1;
 #pragma unroll
     for (int c = 0; c < CGU; ++c) w[c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff, 256 * min(c, last), kNt));
-    // the offset stays allocated past the loads, so no load lands in its register (a later
-    // write of that register would have to wait for the load)
-    asm volatile("" ::"v"(voff));
+    if (kFp4) {
+      const uint8_t *sbank = shared ? (const uint8_t *)a.ss_gu : (const uint8_t *)a.s_gu + (size_t)e * 2 * a.I * (H / VPG);
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t *>(sbank), 0, valid ? 2 * Iw * (H / VPG) : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < NSU; ++c) xs[c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, soff, 16 * min(c, last), kNt);
+    }
+    // the offsets stay allocated past the loads, so no load lands in their registers (a
+    // later write of those registers would have to wait for the load)
+    if (kFp4) asm volatile("" ::"v"(voff), "v"(soff));
+    else asm volatile("" ::"v"(voff));
   };
 
   // per lane: the column groups in order, four products each, one accumulation chain;
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool shA = a.has_shared && 2 * pA < a.I_s;
   const int NEA = pA < NPair ? (2 * pA < a.I ? nr : 0) + (shA ? 1 : 0) : 0;
   {
-    auto compute = [&](uint4(&w)[CGU], int q) {
+    auto compute = [&](uint4(&w)[CGU], const uint32_t(&xsc)[NSU], int q) {
       consume(w);
       // column groups past the row (whole groups) hold a repeated load: zero them in place
 #pragma unroll
@@ -432,8 +448,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int q0 = shared ? 0 : s_start[ri];
       const int q1 = shared ? T : s_start[ri + 1];
       const int p = pA;
+      float bsc[NSU];  // MXFP4 block scales of the lane's groups
+#pragma unroll
+      for (int c = 0; c < NSU; ++c) bsc[c] = kFp4 ? e8m0_scale(xsc[c]) : 1.0f;
       float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
-      if (ESZ == 1) {
+      if (VPG == 16) {
         const float *sc = shared ? a.ss_gu : a.s_gu + (size_t)e * 2 * a.I;
         const int Iw = shared ? a.I_s : a.I;
         sg0 = sc[2 * p];
@@ -449,15 +468,19 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // the token's LDS reads in groups of 4, the next group issued before the current one
         // is used (scheduling barriers keep at most two groups in registers); one
         // accumulation chain in lane-loop order
-        constexpr int kGrp = 4, NG = CGU / kGrp, XPG = 3 - ESZ;  // uint4 of x per column group
+        constexpr int kGrp = 4, NG = CGU / kGrp, XPG = VPG / 8;  // uint4 of x per column group
         static_assert(CGU % kGrp == 0, "column groups come in fours");
         uint4 xv[2][kGrp * XPG];
         auto read_group = [&](uint4(&dst)[kGrp * XPG], int gi) {
 #pragma unroll
           for (int u = 0; u < kGrp; ++u) {
             const int gu = min(l16 + 16 * (gi * kGrp + u), H / VPG);  // H / VPG: the zero pad
-            if (ESZ == 2) {
+            if (VPG == 8) {
               dst[u] = xr[gu];
+            } else if (kFp4) {  // four uint4 a group: a group past the row rereads the last one
+              const int gv = min(gu, H / VPG - 1);
+#pragma unroll
+              for (int d = 0; d < 4; ++d) dst[4 * u + d] = xr[4 * gv + d];
             } else {
               dst[2 * u] = xr[2 * gu];
               dst[2 * u + 1] = xr[2 * gu + 1];
@@ -473,8 +496,10 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int u = 0; u < kGrp; ++u) {
             const int c = gi * kGrp + u;
             const uint4 wc = w[c];
-            if (ESZ == 2) {
+            if (VPG == 8) {
               acc = dot8_bf16(wc, xv[gi & 1][u], acc);
+            } else if (kFp4) {
+              acc = fmaf(dot32_fp4_bf16(wc, &xv[gi & 1][4 * u]), bsc[c], acc);
             } else {
               const uint4 x0 = xv[gi & 1][2 * u], x1 = xv[gi & 1][2 * u + 1];
               acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.x), x0.x, acc);
@@ -501,9 +526,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
     const int voff_r = gu_voff(a.I, pA), voff_s = gu_voff(a.I_s, pA);
-    auto load = [&](uint4(&w)[CGU], int q) {  // q >= NEA: nothing to load (an empty descriptor)
+    const int soff_r = gu_soff(a.I, pA), soff_s = gu_soff(a.I_s, pA);
+    auto load = [&](uint4(&w)[CGU], uint32_t(&xs)[NSU], int q) {  // q >= NEA: an empty descriptor
       const bool valid = q < NEA, shared = shA && q == 0;
-      gu_load(w, valid, shared, (valid && !shared) ? s_e[q - (shA ? 1 : 0)] : 0, shared ? voff_s : voff_r);
+      gu_load(w, xs, valid, shared, (valid && !shared) ? s_e[q - (shA ? 1 : 0)] : 0, shared ? voff_s : voff_r,
+              shared ? soff_s : soff_r);
     };
     auto grab = [&]() -> int {
       int v = 0;
@@ -514,16 +541,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // counts are the same on every path and no prefetch is waited for early
     int q = grab();
     int q2 = grab();
-    load(wa, q);
-    load(wb, q2);
+    load(wa, xa, q);
+    load(wb, xb, q2);
     while (q < NEA) {
-      compute(wa, q);
+      compute(wa, xa, q);
       const int q3 = grab();
-      load(wa, q3);
+      load(wa, xa, q3);
       if (q2 >= NEA) break;
-      compute(wb, q2);
+      compute(wb, xb, q2);
       const int q4 = grab();
-      load(wb, q4);
+      load(wb, xb, q4);
       q = q3;
       q2 = q4;
     }
@@ -538,19 +565,23 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int oB = blockIdx.x;
   const int NEB = oB < NOct ? nr + (a.has_shared ? 1 : 0) : 0;
   uint4 da[2][CGD], db[2][CGD], dc[2][CGD], dd[2][CGD];
+  uint32_t sa[2][NSD], sb[2][NSD], sc_[2][NSD], sd[2][NSD];  // MXFP4 scale bytes
   // the lane's byte offsets in a down matrix for output rows 8o+rg and 8o+4+rg (row length
   // I or I_s): fixed for the whole phase, computed once
-  const int dv_r0 = (kOct * oB + rg) * a.I * ESZ + l16 * 16, dv_r1 = dv_r0 + 4 * a.I * ESZ;
-  const int dv_s0 = (kOct * oB + rg) * a.I_s * ESZ + l16 * 16, dv_s1 = dv_s0 + 4 * a.I_s * ESZ;
-  auto dn_load = [&](uint4(&w)[2][CGD], int q) {  // q >= NEB: an empty descriptor (as gu_load)
+  const int dv_r0 = nbytes((kOct * oB + rg) * a.I) + l16 * 16, dv_r1 = dv_r0 + nbytes(4 * a.I);
+  const int dv_s0 = nbytes((kOct * oB + rg) * a.I_s) + l16 * 16, dv_s1 = dv_s0 + nbytes(4 * a.I_s);
+  // MXFP4: the lane's offsets in the scale matrix (one byte per group)
+  const int ds_r0 = (kOct * oB + rg) * (a.I / VPG) + l16, ds_r1 = ds_r0 + 4 * (a.I / VPG);
+  const int ds_s0 = (kOct * oB + rg) * (a.I_s / VPG) + l16, ds_s1 = ds_s0 + 4 * (a.I_s / VPG);
+  auto dn_load = [&](uint4(&w)[2][CGD], uint32_t(&xs)[2][NSD], int q) {  // q >= NEB: an empty descriptor
     const bool valid = q < NEB;
     const bool shared = a.has_shared && q == 0;
     const int ri = q - (a.has_shared ? 1 : 0);
     const int K = shared ? a.I_s : a.I;
     const int e = (shared || !valid) ? 0 : __builtin_amdgcn_readfirstlane(s_e[ri]);  // uniform: a scalar descriptor
-    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + (size_t)e * H * a.I * ESZ;
+    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + nbytes((size_t)e * H * a.I);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
-                                                                        valid ? H * K * ESZ : 0, 0x00020000);
+                                                                        valid ? nbytes(H * K) : 0, 0x00020000);
     const int last = K / VPG / 16 - 1;
     const int v0 = shared ? dv_s0 : dv_r0, v1 = shared ? dv_s1 : dv_r1;
 #pragma unroll
@@ -558,7 +589,19 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       w[0][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v0, 256 * min(c, last), kNt));  // zeroed at use
       w[1][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v1, 256 * min(c, last), kNt));
     }
-    asm volatile("" ::"v"(v0), "v"(v1));  // as in gu_load
+    const int s0 = shared ? ds_s0 : ds_r0, s1 = shared ? ds_s1 : ds_r1;
+    if (kFp4) {
+      const uint8_t *sbank = shared ? (const uint8_t *)a.ss_d : (const uint8_t *)a.s_d + (size_t)e * H * (a.I / VPG);
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sbank), 0,
+                                                                           valid ? H * (K / VPG) : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < NSD; ++c) {
+        xs[0][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s0, 16 * min(c, last), kNt);
+        xs[1][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s1, 16 * min(c, last), kNt);
+      }
+    }
+    if (kFp4) asm volatile("" ::"v"(v0), "v"(v1), "v"(s0), "v"(s1));  // as in gu_load
+    else asm volatile("" ::"v"(v0), "v"(v1));
   };
   auto grab_b = [&]() -> int {
     int v = 0;
@@ -578,8 +621,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (early) {
     qb1 = grab_b();
     qb2 = grab_b();
-    dn_load(da, qb1);
-    dn_load(db, qb2);
+    dn_load(da, sa, qb1);
+    dn_load(db, sb, qb2);
   }
   grid_wait(a.bar, tok0 + 2u);
   // (after the barrier the tokens are dead: y and h take the data region)
@@ -630,13 +673,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!early) {
       qb1 = grab_b();
       qb2 = grab_b();
-      dn_load(da, qb1);
-      dn_load(db, qb2);
+      dn_load(da, sa, qb1);
+      dn_load(db, sb, qb2);
     }
     qb3 = grab_b();
     qb4 = grab_b();
-    dn_load(dc, qb3);
-    dn_load(dd, qb4);
+    dn_load(dc, sc_, qb3);
+    dn_load(dd, sd, qb4);
     // while those loads are in flight: the padded counts and their block-wide scan for the
     // caller's alignment (LDS only, so bare barriers)
     {
@@ -675,7 +718,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lds_barrier();  // h staged; the weight loads stay in flight
   {
     // ---- entries from the LDS counter, four in flight per wavefront
-    auto compute = [&](uint4(&w)[2][CGD], int q) {
+    auto compute = [&](uint4(&w)[2][CGD], const uint32_t(&xsc)[2][NSD], int q) {
       const bool shared = a.has_shared && q == 0;
       const int ri = q - (a.has_shared ? 1 : 0);
       const int e = shared ? 0 : s_e[ri];
@@ -689,8 +732,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int c = 0; c < CGD; ++c)
         if (16 * c >= Kv) w[0][c] = w[1][c] = make_uint4(0, 0, 0, 0);
       const int o = oB;
+      float bsc[2][NSD];  // MXFP4 block scales
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c = 0; c < NSD; ++c) bsc[s][c] = kFp4 ? e8m0_scale(xsc[s][c]) : 1.0f;
       float sc0 = 1.f, sc1 = 1.f;
-      if (ESZ == 1) {
+      if (VPG == 16) {
         const float *sc = shared ? a.ss_d : a.s_d + (size_t)e * H;
         sc0 = sc[kOct * o + rg];
         sc1 = sc[kOct * o + 4 + rg];
@@ -703,10 +751,14 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int c = 0; c < CGD; ++c) {
           const int g = min(l16 + 16 * c, Kv);  // Kv: the zero pad
           const uint4 w0 = w[0][c], w1 = w[1][c];
-          if (ESZ == 2) {
+          if (VPG == 8) {
             const uint4 hv = hr[g];
             acc0 = dot8_bf16(w0, hv, acc0);
             acc1 = dot8_bf16(w1, hv, acc1);
+          } else if (kFp4) {  // four uint4 a group: a group past the row rereads the last one
+            const uint4 *hg4 = hr + 4 * min(g, Kv - 1);
+            acc0 = fmaf(dot32_fp4_bf16(w0, hg4), bsc[0][c], acc0);
+            acc1 = fmaf(dot32_fp4_bf16(w1, hg4), bsc[1][c], acc1);
           } else {
             const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
 #pragma unroll
@@ -738,21 +790,21 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // entries are grabbed in increasing order, so the first one past the end ends the loop
     int q1 = qb1, q2 = qb2, q3 = qb3, q4 = qb4;
     while (q1 < NEB) {
-      compute(da, q1);
+      compute(da, sa, q1);
       q1 = grab_b();
-      dn_load(da, q1);
+      dn_load(da, sa, q1);
       if (q2 >= NEB) break;
-      compute(db, q2);
+      compute(db, sb, q2);
       q2 = grab_b();
-      dn_load(db, q2);
+      dn_load(db, sb, q2);
       if (q3 >= NEB) break;
-      compute(dc, q3);
+      compute(dc, sc_, q3);
       q3 = grab_b();
-      dn_load(dc, q3);
+      dn_load(dc, sc_, q3);
       if (q4 >= NEB) break;
-      compute(dd, q4);
+      compute(dd, sd, q4);
       q4 = grab_b();
-      dn_load(dd, q4);
+      dn_load(dd, sd, q4);
     }
   }
   __syncthreads();
@@ -838,7 +890,8 @@ int device_cus() {
 bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype) {
   if (T < 1 || T > kDecodeMaxT || T * k > kSmallSlots || E > kMaxExperts) return false;
   if (H > kXW || I > kHW || I_s > kHW) return false;
-  const int grp = 16 * (wtype == 0 ? 8 : 16);  // elements in 16 column groups of 16 bytes
+  // elements in 16 column groups of 16 bytes (MXFP4: no partial lane groups at all)
+  const int grp = 16 * (wtype == 0 ? 8 : wtype == 3 ? 32 : 16);
   if (H % grp != 0 || I % grp != 0 || I_s % grp != 0) return false;
   const int nb = std::min(device_cus(), kMaxBlocks);
   if ((I_s > I ? I_s : I) / 2 > nb || H / kOct > nb) return false;
@@ -853,9 +906,9 @@ struct FusedLaunchInfo {
   int cus = 0, per_cu = 0;
 };
 
-template <int ESZ, int CGU, int CGD, int CR>
+template <int VPG, int CGU, int CGD, int CR>
 static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *nb_out) {
-  auto kern = moe_decode_fused_kernel<ESZ, CGU, CGD, CR>;
+  auto kern = moe_decode_fused_kernel<VPG, CGU, CGD, CR>;
   static std::mutex mu;
   static FusedLaunchInfo info[64];
   int dev = 0;
@@ -903,9 +956,12 @@ hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t de
   a.lds_route = route_bytes(a.T, a.k, a.E);
   int nb = 0;
   hipError_t e;
-  if (a.wtype == 0) e = launch_fused_t<2, 16, 4, 8>(a, lds, s, &nb);
-  else e = launch_fused_t<1, 8, 2, 8>(a, lds, s, &nb);
-  if (desc) snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu", a.wtype == 0 ? "bf16" : "fp8", nb, kNT, lds);
+  if (a.wtype == 0) e = launch_fused_t<8, 16, 4, 8>(a, lds, s, &nb);
+  else if (a.wtype == 3) e = launch_fused_t<32, 4, 1, 8>(a, lds, s, &nb);
+  else e = launch_fused_t<16, 8, 2, 8>(a, lds, s, &nb);
+  if (desc)
+    snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu",
+             a.wtype == 0 ? "bf16" : a.wtype == 3 ? "mxfp4" : "fp8", nb, kNT, lds);
   return e;
 }
 

@@ -343,20 +343,31 @@ def test_experts_forward_parity(recipe, T, BM):
 
 # ---------------------------------------------------------------- the two decode paths
 
-@pytest.mark.parametrize("recipe,T", [("tiny", 4), ("tiny", 64), ("qwen36_a3b", 8), ("qwen36_a3b", 1),
-                                      ("qwen36_a3b", 32), ("flash_next_fp8", 6)])
-def test_four_kernel_decode_path_matches_oracle_and_fused(recipe, T):
+# (recipe, shape overrides, T, whether the fused kernel takes it): the fused kernel keeps the
+# tokens and h in LDS (up to ~16 tokens at these widths) and, for MXFP4, whole 512-element
+# lane groups; a 4-bit H of 512 or 1536 leaves lane groups past the row
+_FOUR_KERNEL_CASES = [("tiny", {}, 4, True), ("tiny", {}, 64, True), ("qwen36_a3b", {}, 8, True),
+                      ("qwen36_a3b", {}, 1, True), ("qwen36_a3b", {}, 32, False), ("flash_next_fp8", {}, 6, True),
+                      ("qwen36_a3b_mxfp4", {}, 8, True), ("qwen36_a3b_mxfp4", {}, 1, True),
+                      ("tiny", dict(wtype="mxfp4"), 4, False),
+                      ("tiny", dict(wtype="mxfp4", H=512, I=512, I_s=512, bias="normal"), 8, True),
+                      ("tiny", dict(wtype="mxfp4", H=1536, I=512, I_s=512, k=4), 5, True),
+                      ("tiny", dict(wtype="mxfp4", H=1024, I=512, I_s=0), 3, True)]
+
+
+@pytest.mark.parametrize("recipe,shape,T,expect_fused", _FOUR_KERNEL_CASES)
+def test_four_kernel_decode_path_matches_oracle_and_fused(recipe, shape, T, expect_fused):
     """MOE_OPT_DECODE_FUSED = 0 runs the decode block as four kernels; it must pass the same
     bars and give bitwise the same output and routing as the fused cooperative kernel."""
     import speculative_verify_moe_amd as moe
-    _say(f"[four-kernel] {recipe} T={T}")
-    cfg = configs.CONFIGS[recipe]
-    L = G.host_layer(cfg)
+    _say(f"[four-kernel] {recipe} {shape} T={T}")
+    cfg = configs.with_shape(configs.CONFIGS[recipe], **shape) if shape else configs.CONFIGS[recipe]
+    L = G.host_layer(cfg) if not shape else configs.make_layer(cfg, seed=9)
     x = configs.make_tokens(cfg, T)
     D = G.device_layer(L)
-    # the fused kernel keeps the tokens and h in LDS: up to ~16 tokens at these widths
-    expect_fused = not (recipe == "qwen36_a3b" and T == 32)
     assert ("decode-fused" in moe.moe_describe_plan(T, D)) == expect_fused
+    if expect_fused:
+        G.check_layer(L, x)
     fused = G.run_layer(L, x)
     moe.moe_set_option(moe.MOE_OPT_DECODE_FUSED, 0)
     try:
