@@ -6,8 +6,8 @@
 // over all CUs.
 // Top-k: Qwen3.8 Flash-Next . GB10 UltraFast, "How it works" (a sort-free
 // verify-path top-k): one wavefront per token holds the token's E logits in
-// registers as 64-bit (rank code, ~expert) keys; each of the k rounds is a local
-// max plus a 6-step xor-butterfly max, and the winner's key is cleared.  No sort.
+// registers as order-preserving 32-bit codes; each of the k rounds is a wavefront
+// maximum with ties to the lower expert index, and the winner is retired (topk.h).
 // Alignment: Qwen3.8 Flash-Next . GB10 UltraFast, first bullet (moe_align_block_size
 // with an arrival-order shim): counts come from integer LDS atomics (their final
 // value does not depend on arrival order) and each slot's place inside its expert's
@@ -20,11 +20,15 @@
 namespace moe {
 
 // ============================================================ router (decode)
-// One wavefront per router row n (n < E: expert rows, n == E: the shared gate row),
-// all T tokens.  The wavefront's fp32 row is loaded into registers first (lane l owns
-// float4 groups g = l + 64c), the block stages the tokens into LDS while those loads
-// are in flight, then each token is one register dot product and one DPP reduction.
+// One wavefront per router row n (n < E: expert rows, n == E: the shared gate row) and
+// block row y per chunk of kRouterTB tokens, so that a 32-token block fills the chip
+// (blockIdx.y splits the tokens; a router row is read once per chunk, from L2 after the
+// first).  The wavefront's fp32 row is loaded into registers first (lane l owns float4
+// groups g = l + 64c), the block stages its tokens into LDS while those loads are in
+// flight (kStage loads per thread in flight together), then each token is one register
+// dot product and one DPP reduction.
 constexpr int kRouterLds = 64 * 1024;
+constexpr int kRouterTB = 8;
 
 template <int C>
 __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__restrict__ x, int T, int H,
@@ -54,14 +58,23 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__rest
     }
   }
   const float bias = (active && n < E && b_r != nullptr) ? b_r[n] : 0.0f;
-  const int TP = kRouterLds / (H * 2);
+  const int TP = min(kRouterLds / (H * 2), kRouterTB);
   const int G8 = H / 8;
   const uint2 *sx2 = reinterpret_cast<const uint2 *>(s_x);
-  for (int t0 = 0; t0 < T; t0 += TP) {
-    const int nt = T - t0 < TP ? T - t0 : TP;
-    __syncthreads();
+  const int tb0 = blockIdx.y * TP, tb1 = min(T, tb0 + TP);
+  for (int t0 = tb0; t0 < tb1; t0 += TP) {
+    const int nt = tb1 - t0;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t0 * H);
-    for (int i = threadIdx.x; i < nt * G8; i += 256) s_x[i] = src[i];
+    constexpr int kStage = 8;
+    for (int i0 = threadIdx.x; i0 < nt * G8; i0 += 256 * kStage) {
+      uint4 v[kStage];
+#pragma unroll
+      for (int j = 0; j < kStage; ++j)
+        if (i0 + 256 * j < nt * G8) v[j] = src[i0 + 256 * j];
+#pragma unroll
+      for (int j = 0; j < kStage; ++j)
+        if (i0 + 256 * j < nt * G8) s_x[i0 + 256 * j] = v[j];
+    }
     __syncthreads();
     if (!active) continue;
     for (int i = 0; i < nt; i += 4) {
@@ -102,8 +115,8 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__rest
 hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r, const float *b_r, int E,
                               const float *w_sg, float *logits, float *gate_logit, hipStream_t s) {
   const int NR = E + (w_sg != nullptr ? 1 : 0);
-  dim3 grid((NR + 3) / 4), block(256);
-  const int TP = kRouterLds / (H * 2);
+  const int TP = std::min(kRouterLds / (H * 2), kRouterTB);
+  dim3 grid((NR + 3) / 4, (T + TP - 1) / TP), block(256);
   const size_t lds = (size_t)(T < TP ? T : TP) * H * 2;
   const int C = (H / 4 + kWave - 1) / kWave;
   if (C <= 2) launch_k(router_rows_kernel<2>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
