@@ -272,46 +272,113 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
       sc0 = sc[o0 + rg];
       sc1 = sc[o0 + 4 + rg];
     }
-    for (int q = q0; q < q1; ++q) {
-      const int slot = routed ? lst.slots[q] : q;
-      const uint4 *hr = routed ? hs + (size_t)slot * (a.I / 8) : hss + (size_t)q * (a.I_s / 8);
-      float acc0 = 0.f, acc1 = 0.f;
+    if constexpr (HLDS) {
+      for (int q = q0; q < q1; ++q) {
+        const int slot = routed ? lst.slots[q] : q;
+        const uint4 *hr = routed ? hs + (size_t)slot * (a.I / 8) : hss + (size_t)q * (a.I_s / 8);
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        const int g = l16 + 16 * c;
-        if (g < G) {
-          if (VPG == 8) {
-            const uint4 hv = hr[g];
-            acc0 = dot8_bf16(w[0][c], hv, acc0);
-            acc1 = dot8_bf16(w[1][c], hv, acc1);
-          } else if (VPG == 32) {
-            acc0 = fmaf(dot32_fp4_bf16(w[0][c], hr + 4 * g), bsc[0][c], acc0);
-            acc1 = fmaf(dot32_fp4_bf16(w[1][c], hr + 4 * g), bsc[1][c], acc1);
-          } else {
-            const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
+        for (int c = 0; c < CG; ++c) {
+          const int g = l16 + 16 * c;
+          if (g < G) {
+            if (VPG == 8) {
+              const uint4 hv = hr[g];
+              acc0 = dot8_bf16(w[0][c], hv, acc0);
+              acc1 = dot8_bf16(w[1][c], hv, acc1);
+            } else if (VPG == 32) {
+              acc0 = fmaf(dot32_fp4_bf16(w[0][c], hr + 4 * g), bsc[0][c], acc0);
+              acc1 = fmaf(dot32_fp4_bf16(w[1][c], hr + 4 * g), bsc[1][c], acc1);
+            } else {
+              const uint4 h0 = hr[2 * g], h1 = hr[2 * g + 1];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              float acc = s == 0 ? acc0 : acc1;
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].x), h0.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].x), h0.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].y), h0.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].y), h0.w, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].z), h1.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].z), h1.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].w), h1.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].w), h1.w, acc);
-              if (s == 0) acc0 = acc;
-              else acc1 = acc;
+              for (int s = 0; s < 2; ++s) {
+                float acc = s == 0 ? acc0 : acc1;
+                acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].x), h0.x, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].x), h0.y, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].y), h0.z, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].y), h0.w, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].z), h1.x, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].z), h1.y, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s][c].w), h1.z, acc);
+                acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s][c].w), h1.w, acc);
+                if (s == 0) acc0 = acc;
+                else acc1 = acc;
+              }
             }
           }
         }
+        acc0 = row16_sum(acc0);
+        acc1 = row16_sum(acc1);
+        if (l16 == 0) {
+          float *dst = routed ? s_y + (size_t)slot * kDnRows : s_ys + (size_t)q * kDnRows;
+          dst[rg] = round_bf16(acc0 * sc0);
+          dst[4 + rg] = round_bf16(acc1 * sc1);
+        }
       }
-      acc0 = row16_sum(acc0);
-      acc1 = row16_sum(acc1);
-      if (l16 == 0) {
-        float *dst = routed ? s_y + (size_t)slot * kDnRows : s_ys + (size_t)q * kDnRows;
-        dst[rg] = round_bf16(acc0 * sc0);
-        dst[4 + rg] = round_bf16(acc1 * sc1);
+
+    } else {
+      // h from global memory (too large for LDS): the h of kPS slots (as many as the
+      // registers hold without spilling) is loaded together, then used, so the slots' load
+      // latencies overlap; each slot's sums are unchanged
+      constexpr int XPG = VPG / 8, NH = CG * XPG, kPS = NH <= 4 ? 4 : NH <= 8 ? 2 : 1;
+      for (int q = q0; q < q1; q += kPS) {
+        uint4 hb[kPS][NH];
+#pragma unroll
+        for (int u = 0; u < kPS; ++u) {
+          if (q + u < q1) {
+            const int slot = routed ? lst.slots[q + u] : q + u;
+            const uint4 *hr = routed ? hs + (size_t)slot * (a.I / 8) : hss + (size_t)(q + u) * (a.I_s / 8);
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const int g = l16 + 16 * c;
+#pragma unroll
+              for (int d = 0; d < XPG; ++d) hb[u][c * XPG + d] = g < G ? hr[XPG * g + d] : make_uint4(0, 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kPS; ++u) {
+          if (q + u < q1) {
+            const int slot = routed ? lst.slots[q + u] : q + u;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const int g = l16 + 16 * c;
+              if (g < G) {
+                if (VPG == 8) {
+                  acc0 = dot8_bf16(w[0][c], hb[u][c], acc0);
+                  acc1 = dot8_bf16(w[1][c], hb[u][c], acc1);
+                } else if (VPG == 32) {
+                  acc0 = fmaf(dot32_fp4_bf16(w[0][c], &hb[u][4 * c]), bsc[0][c], acc0);
+                  acc1 = fmaf(dot32_fp4_bf16(w[1][c], &hb[u][4 * c]), bsc[1][c], acc1);
+                } else {
+                  const uint4 h0 = hb[u][2 * c], h1 = hb[u][2 * c + 1];
+#pragma unroll
+                  for (int s2 = 0; s2 < 2; ++s2) {
+                    float acc = s2 == 0 ? acc0 : acc1;
+                    acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s2][c].x), h0.x, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s2][c].x), h0.y, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s2][c].y), h0.z, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s2][c].y), h0.w, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s2][c].z), h1.x, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s2][c].z), h1.y, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[s2][c].w), h1.z, acc);
+                    acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[s2][c].w), h1.w, acc);
+                    if (s2 == 0) acc0 = acc;
+                    else acc1 = acc;
+                  }
+                }
+              }
+            }
+            acc0 = row16_sum(acc0);
+            acc1 = row16_sum(acc1);
+            if (l16 == 0) {
+              float *dst = routed ? s_y + (size_t)slot * kDnRows : s_ys + (size_t)(q + u) * kDnRows;
+              dst[rg] = round_bf16(acc0 * sc0);
+              dst[4 + rg] = round_bf16(acc1 * sc1);
+            }
+          }
+        }
       }
     }
   };
