@@ -223,16 +223,17 @@ __device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, 
 }
 
 __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t *__restrict__ ids, int n, int E, int BM,
-                                                           int cap, AlignOut al) {
+                                                           int cap, AlignOut al, Touched tl) {
   __shared__ int32_t s_ids[kSmallSlots];
   __shared__ AlignLds L;
   if (threadIdx.x < n) s_ids[threadIdx.x] = ids[threadIdx.x];
   __syncthreads();
-  align_block(s_ids, n, E, BM, cap, L, al, Touched{nullptr, nullptr, nullptr, nullptr});
+  align_block(s_ids, n, E, BM, cap, L, al, tl);
 }
 
 hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s) {
-  launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, BM, (int)cap, al);
+  launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, BM, (int)cap, al,
+           Touched{nullptr, nullptr, nullptr, nullptr});
   return hipGetLastError();
 }
 
@@ -256,6 +257,14 @@ __global__ __launch_bounds__(1024) void topk_align_small_kernel(const float *__r
 hipError_t launch_topk_align_small(const float *logits, const float *gate_logit, int T, int E, int k, int renorm,
                                    int BM, int64_t cap, int32_t *ids, float *w, float *gamma, AlignOut al,
                                    Touched tl, hipStream_t s) {
+  // more tokens than the block's 16 wavefronts: the top-k spread over the chip first (one
+  // wavefront per token, the same arithmetic), then the alignment in one block
+  if (T > 1024 / kWave) {
+    hipError_t e = launch_topk(logits, T, E, k, renorm, ids, w, gate_logit, gamma, s);
+    if (e != hipSuccess) return e;
+    launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, BM, (int)cap, al, tl);
+    return hipGetLastError();
+  }
   const int epl = (E + kWave - 1) / kWave;
   dim3 grid(1), block(1024);
   const int c = (int)cap;
