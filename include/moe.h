@@ -73,8 +73,9 @@ typedef enum {
  *     (s_gate_up, s_down); bf16 activations.
  *   MOE_W_FP8_E4M3_A8: the same weight storage.  On the prefill path the activations
  *     entering each expert matrix are quantised too -- every token row, and every
- *     slot's bf16 h row, to E4M3FN codes with one fp32 scale per row (amax / 448, the
- *     nearest code, ties to an even mantissa) -- and the expert GEMMs run on the fp8
+ *     slot's bf16 h row, to E4M3FN codes with one scale per row (the least power of two
+ *     s with amax <= 448 s; code = the nearest E4M3FN code of a / s, ties to an even
+ *     mantissa) -- and the expert GEMMs run on the fp8
  *     matrix cores (Qwen3.8 Flash-Next . GB10 UltraFast and veloGB10 README, FP8
  *     layers; gfx950 fp8 MFMA).  The decode path (T <= 64) streams the same weights
  *     with bf16 activations, exactly as MOE_W_FP8_E4M3.
