@@ -347,6 +347,8 @@ def test_experts_forward_parity(recipe, T, BM):
 # tokens and h in LDS (up to ~16 tokens at these widths) and, for MXFP4, whole 512-element
 # lane groups; a 4-bit H of 512 or 1536 leaves lane groups past the row
 _FOUR_KERNEL_CASES = [("tiny", {}, 4, True), ("tiny", {}, 64, True), ("qwen36_a3b", {}, 8, True),
+                      # 16 tokens: top-k and alignment in one block; 17: top-k over the chip first
+                      ("tiny", {}, 16, True), ("tiny", {}, 17, True), ("qwen36_a3b", {}, 17, False),
                       ("qwen36_a3b", {}, 1, True), ("qwen36_a3b", {}, 32, False), ("flash_next_fp8", {}, 6, True),
                       ("qwen36_a3b_mxfp4", {}, 8, True), ("qwen36_a3b_mxfp4", {}, 1, True),
                       ("tiny", dict(wtype="mxfp4"), 4, False),
