@@ -72,11 +72,6 @@ __device__ __forceinline__ void st_agent(unsigned *p, unsigned v) {
 // issue order, so this also waits for earlier loads); the clobber keeps the compiler from
 // moving memory operations across it.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N vector memory operations of this wavefront are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Mark a register buffer as consumed here: the compiler waits for its loads at this point,
 // so no later reuse of those registers waits on the loads issued after them.
@@ -192,7 +187,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // only once every block has arrived, and a block's arrival depends on this load
   const unsigned tok0 = ld_agent(a.bar + kMaxBlocks);
 
-  // ---------------- phase 0: router rows, shared-expert prefetch, tokens to LDS
+  // ---------------- phase 0: router rows, tokens to LDS
   const int NR = E + (a.w_sg != nullptr ? 1 : 0);
   // Router row n runs on block n % NB; every wavefront of the block holds the row (the
   // block's 8 loads of it share the CU's caches) and takes the tokens wave, wave + 8, ...,
@@ -224,8 +219,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // in scalar registers), the lane's row and column offset one VGPR, the column group a
   // uniform scalar offset.  Exactly CGU (CGD per row set) load instructions, all in range:
   // groups past the row (whole groups: H, I, I_s are multiples of 16 groups) reload the
-  // last group and are zeroed where they are used, so nothing waits for a load here;
-  // phase A counts on that number when it waits for its h stores.
+  // last group and are zeroed where they are used, so nothing waits for a load here.
   typedef int i4_t __attribute__((ext_vector_type(4)));
   constexpr int kNt = 2;  // cache policy: non-temporal (weights are read once)
   auto as_u4 = [](i4_t v) { return make_uint4(v.x, v.y, v.z, v.w); };
