@@ -123,7 +123,7 @@ def calibrate_copy(mib):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
