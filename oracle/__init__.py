@@ -56,6 +56,9 @@ def _load():
         lib.oracle_moe_layer.restype = None
         lib.oracle_moe_layer.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                          _I, _P, _P, _P, _P, _P, _I, _P, _I, _P]
+        lib.oracle_moe_layer_mt.restype = _I
+        lib.oracle_moe_layer_mt.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                            _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I]
         lib.oracle_expert.restype = None
         lib.oracle_expert.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _I, _P]
         _lib = lib
@@ -74,6 +77,16 @@ def _c(a, dtype):
 
 def lib_path():
     return _LIB_PATH
+
+
+def default_threads():
+    """Host threads the layer oracle uses by default: the CPUs this process may run on, at
+    most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 # ---------------------------------------------------------------- number formats
@@ -210,7 +223,7 @@ def _bank_arrays(layer, prefix):
     return wtype, gu, dn, sgu, sd
 
 
-def moe_layer(x, layer, ids, w, tokens=None, rounding=True):
+def moe_layer(x, layer, ids, w, tokens=None, rounding=True, threads=None, stats=None):
     """Layer output [n_tok][H] float64 for the given routing (ids [T][k], w [T][k]).
 
     ``layer`` is a dict with H, E, k, I, I_s, wtype ('bf16' | 'fp8' | 'fp8a8': fp8 weights with
@@ -219,6 +232,9 @@ def moe_layer(x, layer, ids, w, tokens=None, rounding=True):
     shared_w_gate_up, shared_w_down, shared_s_*, shared_gate_w when I_s > 0).
     ``tokens`` selects which tokens to compute (default: all).  With ``rounding`` the
     outputs are bf16-representable values (bf16 at h, at each expert output and at the end).
+    ``threads`` splits the tokens over that many host threads (default: default_threads());
+    every token is computed by the same code, so the result does not depend on it.  A dict
+    passed as ``stats`` receives the number of threads used.
     """
     lib = _load()
     x = _c(x, np.uint16)
@@ -237,9 +253,17 @@ def moe_layer(x, layer, ids, w, tokens=None, rounding=True):
         tokens = np.arange(T, dtype=np.int32)
     tokens = _c(tokens, np.int32)
     out = np.empty((len(tokens), H), dtype=np.float64)
-    lib.oracle_moe_layer(T, H, E, k, I, wtype, _ptr(x), _ptr(gu), _ptr(dn), _ptr(sgu), _ptr(sd), _ptr(ids), _ptr(w),
-                         I_s, _ptr(sgu_w), _ptr(sdn_w), _ptr(ssgu), _ptr(ssd), _ptr(wsg), len(tokens), _ptr(tokens),
-                         1 if rounding else 0, _ptr(out))
+    nth = default_threads() if threads is None else int(threads)
+    args = (T, H, E, k, I, wtype, _ptr(x), _ptr(gu), _ptr(dn), _ptr(sgu), _ptr(sd), _ptr(ids), _ptr(w),
+            I_s, _ptr(sgu_w), _ptr(sdn_w), _ptr(ssgu), _ptr(ssd), _ptr(wsg), len(tokens), _ptr(tokens),
+            1 if rounding else 0, _ptr(out))
+    if nth <= 1:
+        lib.oracle_moe_layer(*args)
+        used = 1
+    else:
+        used = lib.oracle_moe_layer_mt(*args, nth)
+    if stats is not None:
+        stats["threads"] = used
     return out
 
 

@@ -9,7 +9,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 def build(src=None, out=None, extra=()):
     src = src or os.path.join(HERE, "oracle.c")
     out = out or LIB
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-fno-fast-math",
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-fno-fast-math", "-pthread",
            *extra, src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out

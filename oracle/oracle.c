@@ -64,6 +64,7 @@
  */
 #include <fenv.h>
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -399,4 +400,75 @@ void oracle_expert(int H, int I, int wtype, const uint16_t *x, const void *w_gu,
   double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
   expert_ffn(H, I, wtype, x, w_gu, w_d, s_gu, s_d, rounding, hbuf, y);
   free(hbuf);
+}
+
+/* ------------------------------------------------------------------------ */
+/* the layer over several host threads                                       */
+
+typedef struct {
+  int T, H, E, k, I, wtype;
+  const uint16_t *x;
+  const void *w_gu, *w_d, *s_gu, *s_d;
+  const int32_t *ids;
+  const double *w;
+  int I_s;
+  const void *ws_gu, *ws_d, *ss_gu, *ss_d;
+  const float *w_sg;
+  const int32_t *tokens;
+  int rounding;
+  double *out;
+  int first, count; /* this thread's range of the token list */
+} layer_job;
+
+static void *layer_worker(void *p) {
+  const layer_job *j = (const layer_job *)p;
+  if (j->count > 0)
+    oracle_moe_layer(j->T, j->H, j->E, j->k, j->I, j->wtype, j->x, j->w_gu, j->w_d, j->s_gu, j->s_d, j->ids, j->w,
+                     j->I_s, j->ws_gu, j->ws_d, j->ss_gu, j->ss_d, j->w_sg, j->count, j->tokens + j->first,
+                     j->rounding, j->out + (size_t)j->first * j->H);
+  return NULL;
+}
+
+/* oracle_moe_layer with the token list split into nthreads contiguous ranges, one host
+ * thread each.  Every token is computed by exactly the code above, on its own buffers, so
+ * the output is bitwise that of oracle_moe_layer for any thread count.  Returns the number
+ * of threads used (1 when nthreads <= 1 or a thread cannot be started). */
+int oracle_moe_layer_mt(int T, int H, int E, int k, int I, int wtype, const uint16_t *x, const void *w_gu,
+                        const void *w_d, const void *s_gu, const void *s_d, const int32_t *ids, const double *w,
+                        int I_s, const void *ws_gu, const void *ws_d, const void *ss_gu, const void *ss_d,
+                        const float *w_sg, int n_tok, const int32_t *tokens, int rounding, double *out,
+                        int nthreads) {
+  if (nthreads > n_tok) nthreads = n_tok;
+  if (nthreads < 1) nthreads = 1;
+  layer_job *jobs = (layer_job *)calloc((size_t)nthreads, sizeof(layer_job));
+  pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    layer_job *j = &jobs[i];
+    j->T = T; j->H = H; j->E = E; j->k = k; j->I = I; j->wtype = wtype;
+    j->x = x; j->w_gu = w_gu; j->w_d = w_d; j->s_gu = s_gu; j->s_d = s_d;
+    j->ids = ids; j->w = w; j->I_s = I_s;
+    j->ws_gu = ws_gu; j->ws_d = ws_d; j->ss_gu = ss_gu; j->ss_d = ss_d; j->w_sg = w_sg;
+    j->tokens = tokens; j->rounding = rounding; j->out = out;
+    j->first = (int)((int64_t)n_tok * i / nthreads);
+    j->count = (int)((int64_t)n_tok * (i + 1) / nthreads) - j->first;
+  }
+  /* thread 0's range runs on the calling thread; a range whose thread cannot be started
+   * runs here too */
+  int used = 1;
+  char *live = (char *)calloc((size_t)nthreads, 1);
+  for (int i = 1; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, layer_worker, &jobs[i]) == 0) {
+      live[i] = 1;
+      ++used;
+    } else {
+      layer_worker(&jobs[i]);
+    }
+  }
+  layer_worker(&jobs[0]);
+  for (int i = 1; i < nthreads; ++i)
+    if (live[i]) pthread_join(th[i], NULL);
+  free(live);
+  free(jobs);
+  free(th);
+  return used;
 }

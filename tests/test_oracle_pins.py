@@ -576,6 +576,25 @@ def test_layer_with_shared_equals_dense_masked_gates(rounding):
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("wtype", ["bf16", "fp8a8", "mxfp4"])
+@pytest.mark.parametrize("rounding", [False, True])
+def test_threaded_layer_is_bitwise_the_single_threaded_one(wtype, rounding):
+    """The token list split over host threads gives bitwise the one-thread result, for any
+    thread count (more threads than tokens included) and any order of the token list."""
+    cfg = configs.with_shape(configs.CONFIGS["tiny"], I_s=64, k=3, bias="normal", wtype=wtype)
+    L = configs.make_layer(cfg, seed=7)
+    x = configs.make_tokens(cfg, 29, seed=7)
+    ids, w = routed(x, L, cfg.k)
+    tokens = np.random.default_rng(7).permutation(29)[:23].astype(np.int32)
+    tokens = np.concatenate([tokens, tokens[:4]])  # repeated tokens too
+    one = oracle.moe_layer(x, L, ids, w, tokens=tokens, rounding=rounding, threads=1)
+    for n in (2, 3, 8, 27, 40):
+        st = {}
+        got = oracle.moe_layer(x, L, ids, w, tokens=tokens, rounding=rounding, threads=n, stats=st)
+        assert st["threads"] == min(n, len(tokens))
+        assert np.array_equal(got.view(np.uint64), one.view(np.uint64)), f"{n} threads"
+
+
 def test_layer_k_equals_E_is_dense_soft_moe():
     cfg = configs.with_shape(configs.CONFIGS["tiny"], E=6, k=6)
     L = configs.make_layer(cfg, seed=4)
