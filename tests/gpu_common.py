@@ -8,13 +8,16 @@ import torch
 import oracle
 from synth import configs
 
-TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3, "mxfp4": 5e-3}
-# max-abs bars, as a fraction of max |ref|.  fp8 activations on the prefill path: the device's
-# h (fp32 sums rounded to bf16) can differ from the oracle's (fp64 sums) by one bf16 step,
-# which now and then moves an h code by one e4m3 step (at most 1/8 of that element) or a row's
-# scale (every code of the row by at most one step); one slot's output then moves by a few
-# percent of max |ref|.  The relL2 bar still binds the whole output.
-MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 5e-2, "mxfp4": 1e-2}
+# relL2 bars.  MXFP4 weights decode exactly on both sides (E2M1 codes times a power of two),
+# which leaves the error sources of bf16 -- fp32 against fp64 sums and the three bf16
+# roundings -- so it takes the bf16 bar.  fp8 weights keep the 5e-3 their type is allowed;
+# fp8 activations add one e4m3 rounding per activation (measured worst case 1.79e-3).
+TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3, "mxfp4": 1e-3}
+# max-abs bars, as a fraction of max |ref|: 1e-2 for every type.  fp8 activations come
+# closest (measured worst case 8.2e-3 over the 4096-token chunk): the device's h (fp32 sums
+# rounded to bf16) can differ from the oracle's by one bf16 step, which now and then moves an
+# h code by one e4m3 step or a row's scale by one binade.
+MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 1e-2, "mxfp4": 1e-2}
 
 
 def runs_decode_path(T, k):
@@ -89,6 +92,15 @@ def run_layer(L, x_bits):
     return bf16_bits(out), logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
 
 
+def say_margin(name, rep):
+    """One line per compared case: the measured relL2 and max-abs (as a fraction of max |ref|)
+    beside their bars."""
+    wt = rep.get("wtype")
+    frac = rep["max_abs"] / max(rep["max_ref"], 1e-300)
+    print(f"[margin] {name} wtype={wt} relL2={rep['rel_l2']:.3e} bar={TOL[wt]:.0e} "
+          f"maxabs/max|ref|={frac:.3e} bar={MAX_ABS[wt]:.0e}", flush=True)
+
+
 def check_layer(L, x_bits, tokens=None, report=None):
     """Compare one layer call with the oracle.  Routing: bit-exact ids from the device logits,
     weights within 1e-6; logits within 1e-5 (1 + |L|) of fp64; output relL2 / max-abs bars."""
@@ -114,7 +126,7 @@ def check_layer(L, x_bits, tokens=None, report=None):
     tol = TOL[Lref["wtype"]]
     if report is not None:
         report.update(rel_l2=rel, max_abs=mx, max_ref=np.max(np.abs(ref)), ref=ref, got=got, ids=ids_ref, w=w_ref,
-                      tokens=tokens)
+                      tokens=tokens, wtype=Lref["wtype"])
     assert rel <= tol, f"relL2 {rel:.3e} > {tol}"
     mtol = MAX_ABS[Lref["wtype"]]
     assert mx <= mtol * np.max(np.abs(ref)), f"max-abs {mx:.3e} > {mtol} * {np.max(np.abs(ref)):.3e}"
