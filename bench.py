@@ -54,11 +54,13 @@ PREFILL_A8_STAGES = ["router_gemm_mfma", "topk", "align", "quant_tokens", "gemm_
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=2400)
+    p.add_argument("--warmup", type=int, default=320)
     p.add_argument("--workload", default="qwen36_T8", choices=sorted(WORKLOADS))
     p.add_argument("--replicas", type=int, default=0, help="layer replicas in HBM (0: 16 decode, 2 prefill)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--rounds", type=int, default=3, help="the K timed steps are split into this many rounds")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target wall time of each leg of the oracle baseline (one thread, all threads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--four-kernel", action="store_true", help="run decode blocks as four kernels, not the fused one")
     p.add_argument("--no-graph", action="store_true",
@@ -219,10 +221,12 @@ def main():
     # first and one of the second; the timed steps carry no per-call host overhead (the layer
     # call allocates nothing and captures as is)
     K = args.steps
+    n_rounds = max(1, min(args.rounds, K))
+    round_steps = [K * (i + 1) // n_rounds - K * i // n_rounds for i in range(n_rounds)]
     graphs = {}
     if not args.no_graph:
         cap = torch.cuda.Stream()
-        for n in sorted({L_rep, K % L_rep} - {0}):
+        for n in sorted(({L_rep} | {m % L_rep for m in round_steps}) - {0}):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 for r in range(n):
@@ -245,11 +249,33 @@ def main():
     run_steps(-(-args.warmup // L_rep) * L_rep)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps
-    t_start = time.perf_counter()
-    run_steps(K)
+    # ---- timed region: exactly K steps, in rounds, each bracketed by a device synchronisation
+    round_s = []
+    for m in round_steps:
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        run_steps(m)
+        torch.cuda.synchronize()
+        round_s.append(time.perf_counter() - t_start)
+    elapsed = float(sum(round_s))
+    round_rate = np.array([T * m / t for m, t in zip(round_steps, round_s)])
+    cv = float(round_rate.std() / round_rate.mean()) if n_rounds > 1 else 0.0
+
+    # ---- cold single call: a 1 GiB scratch write first (caches hold other data), then one
+    # eager call on replica 0, its kernels timed by the stage events and the host clock
+    scratch = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    cold_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
+    cold_h = moe.stage_event_handles(cold_ev)
+    scratch.fill_(1)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    moe.moe_set_stage_events(cold_h)
+    t_c0 = time.perf_counter()
+    moe.moe_layer_forward(xs[0], layers[0], out=outs[0], ws=wss[0])
+    torch.cuda.synchronize()
+    cold_wall_us = (time.perf_counter() - t_c0) * 1e6
+    moe.moe_set_stage_events(None)
+    cold_gpu_us = sum(cold_ev[2 * j].elapsed_time(cold_ev[2 * j + 1]) for j in range(nst)) * 1e3
+    del scratch
 
     # ---- kernel durations: the same K steps once more as eager calls, with HIP events on every
     # stage's kernels (attached to the kernel dispatches by the library, on the launch stream).
@@ -319,35 +345,50 @@ def main():
              "touched_experts_mean": round(float(nt_steps.mean()), 2),
              "stage_us": {s: round(float(stage_ms[:, j].mean()) * 1e3, 2) for j, s in enumerate(stages)}}
 
-    # ---- CPU baseline: the fp64 oracle, as it stands, on a bounded sample of the same workload
+    # ---- CPU baseline: the fp64 oracle, as it stands, on a bounded sample of the same workload:
+    # whole layer calls (router, top-k, experts, shared, combine) on the replicas in turn, first
+    # on one thread, then on all the host threads the process may use (one call per thread at
+    # a time; the oracle's C calls run outside Python's lock)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        hl = dict(host)
-        if prefill:
-            sample_T = 16
-        else:
-            sample_T = T
-        n_calls = 0
-        t_c = time.perf_counter()
-        while True:
-            r = n_calls % L_rep
-            hr = host_routers[r]
+        from concurrent.futures import ThreadPoolExecutor
+        sample_T = 16 if prefill else T
+
+        def oracle_call(r):
+            hr = host_routers[r % L_rep]
+            hl = dict(host)
             hl["router_w"], hl["router_b"] = hr["router_w"], hr["router_b"]
             if I_s:
                 hl["shared_gate_w"] = hr["shared_gate_w"]
-            xb = host_x[r][:sample_T]
+            xb = host_x[r % L_rep][:sample_T]
             lg = oracle.router_logits(xb, hr["router_w"], hr["router_b"]).astype(np.float32)
             ids, w = oracle.route_topk(lg, k, cfg.renormalize)
-            oracle.moe_layer(xb, hl, ids, w, rounding=True)
-            n_calls += 1
-            if time.perf_counter() - t_c >= args.cpu_seconds:
-                break
-        cpu_s = time.perf_counter() - t_c
-        cpu = {"value": round(n_calls * sample_T / cpu_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_calls} oracle layer calls of {sample_T} tokens each (router, top-k, experts, shared, "
-                         f"combine; fp64) on replicas cycled like the GPU steps, {cpu_s:.1f} s single-threaded",
-               "cpu": _cpu_model()}
+            oracle.moe_layer(xb, hl, ids, w, rounding=True, threads=1)
+
+        def leg(n_threads):
+            n_calls, t_c = 0, time.perf_counter()
+            if n_threads == 1:
+                while time.perf_counter() - t_c < args.cpu_seconds:
+                    oracle_call(n_calls)
+                    n_calls += 1
+            else:
+                with ThreadPoolExecutor(max_workers=n_threads) as pool:
+                    while time.perf_counter() - t_c < args.cpu_seconds:
+                        list(pool.map(oracle_call, range(n_calls, n_calls + n_threads)))
+                        n_calls += n_threads
+            return n_calls, time.perf_counter() - t_c
+
+        n1, s1 = leg(1)
+        nth = oracle.default_threads()
+        nn, sn = leg(nth) if nth > 1 else (n1, s1)
+        what = (f"oracle layer calls of {sample_T} tokens each (router, top-k, experts, shared, combine; fp64) "
+                f"on the replicas in turn")
+        cpu = {"value": round(nn * sample_T / sn, 3), "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"{nn} {what}, {sn:.1f} s on {nth} host threads (one call per thread)",
+               "cpu": _cpu_model(),
+               "single_thread": {"value": round(n1 * sample_T / s1, 3), "unit": "tokens/s", "cores": 1,
+                                 "sample": f"{n1} {what}, {s1:.1f} s on one thread"}}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -362,9 +403,17 @@ def main():
                    "shared_inter": I_s, "weights": cfg.wtype, "replicas": L_rep,
                    "path": plan.split()[0].split("=")[1]},
         "roofline": roofline, "layer": layer, "cpu_baseline": cpu,
+        "rounds": [round(float(v), 1) for v in round_rate], "round_steps": round_steps,
+        "median_round_value": round(float(np.median(round_rate)), 1), "cv": round(cv, 4),
+        "valid": cv <= 0.03,
+        "cold": {"us_kernels": round(cold_gpu_us, 2), "us_wall": round(cold_wall_us, 2),
+                 "after": "a 1 GiB device write; one eager call on replica 0"},
         "setup_s": round(setup_s, 1), "device": torch.cuda.get_device_name(0),
-        "timing": ("HIP graph replays (one graph per round of the replicas)" if graphs else "eager calls")
-                  + "; kernel durations from HIP events on a second pass of the same steps",
+        "timing": (f"{n_rounds} rounds of " + ("HIP graph replays (one graph per round of the replicas)"
+                                                  if graphs else "eager calls")
+                   + "; value = all K steps over the summed round times; the line is invalid when the rounds' "
+                     "coefficient of variation exceeds 3%; kernel durations from HIP events on a second pass "
+                     "of the same steps"),
     }
     print(json.dumps(line), flush=True)
 
