@@ -13,11 +13,13 @@ from synth import configs
 # roundings -- so it takes the bf16 bar.  fp8 weights keep the 5e-3 their type is allowed;
 # fp8 activations add one e4m3 rounding per activation (measured worst case 1.79e-3).
 TOL = {"bf16": 1e-3, "fp8": 5e-3, "fp8a8": 5e-3, "mxfp4": 1e-3}
-# max-abs bars, as a fraction of max |ref|: 1e-2 for every type.  fp8 activations come
-# closest (measured worst case 8.2e-3 over the 4096-token chunk): the device's h (fp32 sums
-# rounded to bf16) can differ from the oracle's by one bf16 step, which now and then moves an
-# h code by one e4m3 step or a row's scale by one binade.
-MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 1e-2, "mxfp4": 1e-2}
+# max-abs bars, as a fraction of max |ref|: 1e-2, except fp8 activations, whose h codes can
+# differ from the oracle's: the device's h (fp32 sums rounded to bf16) can differ from the
+# oracle's by one bf16 step, which now and then moves an h code by one e4m3 step or a row's
+# scale by one binade, and one slot's output then moves by a percent or two of max |ref|
+# (measured worst cases: 8.2e-3 over the 4096-token chunk, 1.41e-2 for a 600-token chunk of the
+# tiny layer, whose 128-wide h rows give a single code more weight).
+MAX_ABS = {"bf16": 1e-2, "fp8": 1e-2, "fp8a8": 3e-2, "mxfp4": 1e-2}
 
 
 def runs_decode_path(T, k):

@@ -180,7 +180,9 @@ def test_layer_tiny_variants():
             _say(f"[layer-variant] {v} T={T}")
             L = configs.make_layer(cfg, seed=11)
             x = configs.make_tokens(cfg, T, seed=11)
-            G.check_layer(L, x)
+            rep = {}
+            G.check_layer(L, x, report=rep)
+            G.say_margin(f"tiny{v}_T{T}", rep)
 
 
 def test_fp8_prefill_tiny_shapes():
@@ -192,7 +194,9 @@ def test_fp8_prefill_tiny_shapes():
             _say(f"[fp8-prefill] {v} T={T}")
             L = configs.make_layer(cfg, seed=5)
             x = configs.make_tokens(cfg, T, seed=5)
-            G.check_layer(L, x)
+            rep = {}
+            G.check_layer(L, x, report=rep)
+            G.say_margin(f"tiny{v}_T{T}", rep)
 
 
 def _check_act8_is_quantised(L, x, rep):
@@ -227,6 +231,7 @@ def test_fp8a8_prefill_tiny_shapes():
             x = configs.make_tokens(cfg, T, seed=5)
             rep = {}
             G.check_layer(L, x, report=rep)
+            G.say_margin(f"tiny{v}_T{T}", rep)
             if not G.runs_decode_path(T, cfg.k):
                 _check_act8_is_quantised(L, x, rep)
 
@@ -243,7 +248,7 @@ def test_mxfp4_tiny_shapes():
             L = configs.make_layer(cfg, seed=6)
             rep = {}
             G.check_layer(L, configs.make_tokens(cfg, T, seed=6), report=rep)
-            _say(f"[mxfp4] relL2={rep['rel_l2']:.3e}")
+            G.say_margin(f"tiny{v}_T{T}", rep)
     cfg = configs.with_shape(configs.CONFIGS["tiny"], wtype="mxfp4")
     D = G.device_layer(configs.make_layer(cfg, seed=6))
     with pytest.raises(MoeError, match="decode path only"):
@@ -464,3 +469,48 @@ def test_graph_replays_equal_eager(recipe, T):
         eager = G.bf16_bits(moe_layer_forward(xb, D, ws=ws))
         torch.cuda.synchronize()
         assert np.array_equal(eager, ref_b), f"{recipe} T={T} eager call after replay {i}"
+
+
+# ---------------------------------------------------------------- the fused kernel's waits
+
+@pytest.mark.parametrize("recipe,T", [("qwen36_a3b", 8), ("qwen36_a3b", 1), ("flash_next_fp8", 6),
+                                      ("qwen36_a3b_mxfp4", 8), ("tiny", 64), ("tiny", 3)])
+def test_fused_waits_never_give_up(recipe, T):
+    """Normal use of the fused decode kernel: over many calls on one workspace no wait gives up
+    (the workspace's status word stays 0) and every output is finite and the same."""
+    import speculative_verify_moe_amd as moe
+    _say(f"[status] {recipe} T={T}")
+    cfg = configs.CONFIGS[recipe]
+    D = G.device_layer(G.host_layer(cfg))
+    assert "decode-fused" in moe.moe_describe_plan(T, D)
+    x = G.to_dev_bf16(configs.make_tokens(cfg, T))
+    ws = torch.zeros((moe.moe_layer_workspace_size(T, D),), dtype=torch.uint8, device="cuda")
+    outs = [moe.moe_layer_forward(x, D, ws=ws) for _ in range(40)]
+    torch.cuda.synchronize()
+    assert moe.moe_workspace_status(ws) == 0
+    first = G.bf16_bits(outs[0])
+    assert np.all(np.isfinite(G.bf16_values(first)))
+    for o in outs[1:]:
+        assert np.array_equal(G.bf16_bits(o), first)
+
+
+def test_one_workspace_serves_calls_of_every_size():
+    """Fused decode blocks, four-kernel decode blocks and prefill chunks take turns on one
+    zeroed workspace: every call equals the same call on a workspace of its own, bitwise, and
+    no fused wait gives up."""
+    import speculative_verify_moe_amd as moe
+    cfg = configs.CONFIGS["qwen36_a3b"]
+    D = G.device_layer(G.host_layer(cfg))
+    sizes = (8, 32, 100, 3, 64, 1)
+    xs = {T: G.to_dev_bf16(configs.make_tokens(cfg, T, replica=T)) for T in sizes}
+    refs = {}
+    for T in sizes:
+        ws_own = torch.zeros((moe.moe_layer_workspace_size(T, D),), dtype=torch.uint8, device="cuda")
+        refs[T] = G.bf16_bits(moe.moe_layer_forward(xs[T], D, ws=ws_own))
+    ws = torch.zeros((max(moe.moe_layer_workspace_size(T, D) for T in sizes),), dtype=torch.uint8, device="cuda")
+    for rnd in range(3):
+        for T in sizes:
+            _say(f"[shared-workspace] round {rnd} T={T}: {moe.moe_describe_plan(T, D).split()[0]}")
+            got = G.bf16_bits(moe.moe_layer_forward(xs[T], D, ws=ws))
+            assert np.array_equal(got, refs[T]), f"round {rnd} T={T}"
+    assert moe.moe_workspace_status(ws) == 0
