@@ -81,10 +81,9 @@ typedef enum {
  *     with bf16 activations, exactly as MOE_W_FP8_E4M3.
  *   MOE_W_MXFP4: OCP MX (Microscaling) FP4 -- E2M1 codes, two per byte with the
  *     even-indexed weight in the low nibble, w_gate_up [n][2I][H/2] and w_down
- *     [n][H][I/2] bytes; s_gate_up [n][2I][H/32] and s_down [n][H][I/32] hold one
- *     E8M0 scale byte (2^(X-127)) per block of 32 consecutive weights of a row (the
- *     scale pointers are then byte arrays, no alignment needed).  4-bit routed experts
- *     with 16-bit activations (Qwen3.8 Flash-Next . GB10 UltraFast, "Target
+ *     [n][H][I/2] bytes, and one E8M0 scale byte (2^(X-127)) per block of 32 consecutive
+ *     weights of a row in mx_gate_up [n][2I][H/32] and mx_down [n][H][I/32].  4-bit routed
+ *     experts with 16-bit activations (Qwen3.8 Flash-Next . GB10 UltraFast, "Target
  *     precision"; Qwen3.6-35B-A3B for NInfer, "Artifact"; veloGB10 README, NVFP4 packs),
  *     in the format gfx950 converts natively.  Decode path only (T <= 64): a prefill
  *     chunk returns MOE_ERR_UNSUPPORTED. */
@@ -93,14 +92,16 @@ typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1, MOE_W_FP8_E4M3_A8 = 2, MOE_W_
 /* A bank of experts of one form (routed: n = E experts; shared: n = 1).
  * Qwen3.6-35B-A3B for NInfer, "Artifact" (gate/up and down per expert). */
 typedef struct {
-  int32_t wtype;           /* moe_wtype */
-  int32_t num_experts;     /* n; a shared bank with n == 0 means "no shared expert" */
-  int32_t hidden;          /* H, multiple of 64, at most 8192 */
-  int32_t inter;           /* I, multiple of 64 */
-  const void *w_gate_up;   /* [n][2I][H]: rows [0,I) gate, rows [I,2I) up */
-  const void *w_down;      /* [n][H][I] */
-  const float *s_gate_up;  /* fp8: [n][2I] row scales; MXFP4: E8M0 block scale bytes (cast); NULL for bf16 */
-  const float *s_down;     /* fp8: [n][H] row scales; MXFP4: E8M0 block scale bytes (cast); NULL for bf16 */
+  int32_t wtype;              /* moe_wtype */
+  int32_t num_experts;        /* n; a shared bank with n == 0 means "no shared expert" */
+  int32_t hidden;             /* H, multiple of 64, at most 8192 */
+  int32_t inter;              /* I, multiple of 64 */
+  const void *w_gate_up;      /* [n][2I][H]: rows [0,I) gate, rows [I,2I) up (MXFP4: [n][2I][H/2] bytes) */
+  const void *w_down;         /* [n][H][I] (MXFP4: [n][H][I/2] bytes) */
+  const float *s_gate_up;     /* fp8 types: [n][2I] fp32 row scales, 4-byte aligned; ignored otherwise */
+  const float *s_down;        /* fp8 types: [n][H] fp32 row scales, 4-byte aligned; ignored otherwise */
+  const uint8_t *mx_gate_up;  /* MXFP4: [n][2I][H/32] E8M0 block-scale bytes; ignored otherwise */
+  const uint8_t *mx_down;     /* MXFP4: [n][H][I/32] E8M0 block-scale bytes; ignored otherwise */
 } moe_bank;
 
 /* One MoE layer.  veloGB10 README, "The model". */
@@ -169,22 +170,39 @@ moe_status moe_experts_forward(const uint16_t *x, int32_t T, const moe_bank *rou
                                const int32_t *expert_counts, const int32_t *expert_offsets, int32_t BM,
                                int64_t cap, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes moe_layer_forward needs for T tokens.  The workspace is scratch for
- * one call at a time; a decode/verify block on the fused kernel also keeps its grid
- * barrier words there (each call writes a fresh 31-bit token, so no reset is needed;
- * zeroing a new workspace once rules out a stale word that happens to equal a token). */
+/* Workspace bytes moe_layer_forward needs for T tokens.  The workspace is scratch for one
+ * call at a time on one device; calls of any T may take turns on it.  Its first bytes hold
+ * the synchronisation words of the fused decode kernel (an arrival count that carries over
+ * from call to call, so no call needs a reset or a memset; a status word; per-entry
+ * readiness counts), laid out the same in every plan: zero a new workspace once, before its
+ * first call, and do not write into it between calls. */
 size_t moe_layer_workspace_size(int32_t T, const moe_layer *L);
 
 /* The whole layer: router, top-k, alignment, routed experts, shared expert and
- * combine.  Sources as above.
+ * combine -- the routed MoE FFN block of veloGB10 README, "The model" (top-k routed
+ * experts plus one always-on shared expert), with the routing folded into the expert
+ * kernels (same README, "Kernel work") and the deterministic alignment and combine of
+ * Qwen3.8 Flash-Next . GB10 UltraFast, first bullet.
  *   x [T][H] bf16 (in); out [T][H] bf16 (out).
  *   logits_out [T][E] fp32, ids_out [T][k] int32, w_out [T][k] fp32: optional
  *   (NULL to skip) copies of the routing the layer used.
  * Decode/verify blocks (T <= 64) use BM = 16 and the GEMV path; prefill chunks
  * use BM = 64 and the MFMA path (bf16 or fp8 weights; fp8 activations as well
- * for MOE_W_FP8_E4M3_A8, which then needs inter % 128 == 0). */
+ * for MOE_W_FP8_E4M3_A8, which then needs inter % 128 == 0).
+ * Residency: a decode block that fits the fused kernel runs one block per CU and needs
+ * all of them resident together (its blocks wait for one another).  Kernels of other
+ * streams or processes that hold CUs can delay some of its blocks; every wait is bounded,
+ * and a wait that gives up adds one to the workspace's status word
+ * (moe_workspace_status_offset) and makes the call write NaN for the output rows that
+ * depended on it -- a wrong result is never silent and no call hangs.  Run the fused path
+ * on a GPU it does not share, or read the status word after a batch of calls. */
 moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                              int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Byte offset, inside every moe_layer_forward workspace, of a uint32 count of the fused
+ * decode kernel's waits that gave up (0 in normal use; see moe_layer_forward).  The count
+ * only grows; zeroing the workspace clears it.  Pure host function. */
+size_t moe_workspace_status_offset(void);
 
 /* Detail of the last non-OK status on the calling thread (empty if none). */
 const char *moe_last_error(void);

@@ -28,7 +28,8 @@ _SZ = ctypes.c_size_t
 
 class _Bank(ctypes.Structure):
     _fields_ = [("wtype", _I32), ("num_experts", _I32), ("hidden", _I32), ("inter", _I32),
-                ("w_gate_up", _P), ("w_down", _P), ("s_gate_up", _P), ("s_down", _P)]
+                ("w_gate_up", _P), ("w_down", _P), ("s_gate_up", _P), ("s_down", _P), ("mx_gate_up", _P),
+                ("mx_down", _P)]
 
 
 class _Layer(ctypes.Structure):
@@ -47,6 +48,7 @@ EXPORTS = {
     "moe_layer_workspace_size": (_SZ, [_I32, ctypes.POINTER(_Layer)]),
     "moe_layer_forward": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_Layer), _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
+    "moe_workspace_status_offset": (_SZ, []),
     "moe_describe_plan": (ctypes.c_char_p, [_I32, ctypes.POINTER(_Layer)]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(_P), _I32]),
     "moe_set_option": (ctypes.c_int, [_I32, _I32]),
@@ -123,8 +125,10 @@ class Bank:
             _dev(s_down, torch.uint8, "s_down")
 
     def struct(self):
+        mx = self.wtype == MOE_W_MXFP4
         return _Bank(self.wtype, self.num_experts, self.hidden, self.inter, _ptr(self.w_gate_up), _ptr(self.w_down),
-                     _ptr(self.s_gate_up), _ptr(self.s_down))
+                     None if mx else _ptr(self.s_gate_up), None if mx else _ptr(self.s_down),
+                     _ptr(self.s_gate_up) if mx else None, _ptr(self.s_down) if mx else None)
 
 
 class Layer:
@@ -139,7 +143,8 @@ class Layer:
         self.hidden, self.num_experts = routed.hidden, routed.num_experts
         self._s = _Layer(self.hidden, self.num_experts, self.top_k, 1 if self.renormalize else 0, _ptr(self.router_w),
                          _ptr(self.router_b), routed.struct(),
-                         shared.struct() if shared is not None else _Bank(0, 0, self.hidden, 0, None, None, None, None),
+                         shared.struct() if shared is not None else _Bank(0, 0, self.hidden, 0, None, None, None, None,
+                                                                           None, None),
                          _ptr(self.shared_gate_w))
 
     @property
@@ -190,6 +195,13 @@ def moe_layer_workspace_size(T, layer):
 
 def moe_last_error():
     return _lib.moe_last_error().decode()
+
+
+def moe_workspace_status(ws):
+    """The workspace's count of fused-kernel waits that gave up (0 in normal use); reads the
+    word on the device (synchronises with the current stream)."""
+    off = int(_lib.moe_workspace_status_offset())
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 def moe_describe_plan(T, layer):
@@ -297,3 +309,4 @@ def moe_layer_forward(x, layer, out=None, logits_out=None, ids_out=None, w_out=N
     _check(_lib.moe_layer_forward(_ptr(x), T, ctypes.byref(layer.struct), _ptr(out), _ptr(logits_out), _ptr(ids_out),
                                   _ptr(w_out), _ptr(ws), ws.numel(), _stream()))
     return out
+

@@ -109,8 +109,8 @@ moe_status check_bank(const moe_bank *b, const char *name, int H, bool need_n, i
   if (!aligned16(b->w_gate_up) || !aligned16(b->w_down))
     return fail(MOE_ERR_MISALIGNED, "%s: weight pointers must be 16-byte aligned", name);
   if (b->wtype == MOE_W_MXFP4) {
-    if (b->s_gate_up == nullptr || b->s_down == nullptr)
-      return fail(MOE_ERR_INVALID_ARG, "%s: MXFP4 weights need s_gate_up and s_down block scales", name);
+    if (b->mx_gate_up == nullptr || b->mx_down == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "%s: MXFP4 weights need the mx_gate_up and mx_down block scales", name);
   } else if (b->wtype != MOE_W_BF16) {
     if (b->s_gate_up == nullptr || b->s_down == nullptr)
       return fail(MOE_ERR_INVALID_ARG, "%s: fp8 weights need s_gate_up and s_down row scales", name);
@@ -164,6 +164,9 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     o = align_up(o + bytes, 256);
     return r;
   };
+  // the fused kernel's synchronisation words first, in every plan: calls of any size may
+  // share one workspace without another buffer overwriting them
+  p.off_bar = take((size_t)kBarrierWords * 4);
   p.off_logits = take((size_t)T * E * 4);
   p.off_gate = take((size_t)T * 4);
   p.off_ids = take((size_t)n * 4);
@@ -178,7 +181,6 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     p.off_h = take((size_t)n * I * 2);
     p.off_hs = take((size_t)T * I_s * 2);
     p.off_tl = take(touched_ints(E, n) * 4);
-    p.off_bar = take((size_t)kBarrierWords * 4);
     p.off_hist = p.off_y = p.off_ys = 0;
   } else {
     p.off_hist = take(align_hist_ints(n, E) * 4);
@@ -186,7 +188,7 @@ LayerPlan plan_layer(int T, const moe_layer *L) {
     p.off_hs = take((size_t)T * I_s * 2);
     p.off_y = take((size_t)n * H * 2);
     p.off_ys = take((size_t)T * H * 2);
-    p.off_tl = p.off_bar = 0;
+    p.off_tl = 0;
     if (L->routed.wtype == MOE_W_FP8_E4M3_A8) {
       p.off_x8 = take((size_t)T * H);
       p.off_sx = take((size_t)T * 4);
@@ -249,6 +251,8 @@ void fill_gemv(GemvArgs &g, const uint16_t *x, int T, int H, int k, const moe_ba
   g.s_gu = routed->s_gate_up;
   g.w_d = routed->w_down;
   g.s_d = routed->s_down;
+  g.x_gu = routed->mx_gate_up;
+  g.x_d = routed->mx_down;
 }
 
 }  // namespace
@@ -269,6 +273,8 @@ size_t moe_align_workspace_size(int32_t T, int32_t k, int32_t E) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_status_offset(void) { return (size_t)kBarStatus * 4; }
 
 moe_status moe_set_option(int32_t key, int32_t value) {
   if (key == MOE_OPT_DECODE_FUSED) {
@@ -547,11 +553,15 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     f.s_gu = L->routed.s_gate_up;
     f.w_d = L->routed.w_down;
     f.s_d = L->routed.s_down;
+    f.x_gu = L->routed.mx_gate_up;
+    f.x_d = L->routed.mx_down;
     if (shared) {
       f.ws_gu = L->shared.w_gate_up;
       f.ss_gu = L->shared.s_gate_up;
       f.ws_d = L->shared.w_down;
       f.ss_d = L->shared.s_down;
+      f.xs_gu = L->shared.mx_gate_up;
+      f.xs_d = L->shared.mx_down;
     }
     f.logits = logits;
     f.gate_logit = gate;
@@ -595,6 +605,8 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
       g.ss_gu = L->shared.s_gate_up;
       g.ws_d = L->shared.w_down;
       g.ss_d = L->shared.s_down;
+      g.xs_gu = L->shared.mx_gate_up;
+      g.xs_d = L->shared.mx_down;
       g.gamma = gamma;
     }
     g.h = (uint16_t *)(base + p.off_h);

@@ -7,31 +7,40 @@
 // in slot order and a combine without float atomics.
 //
 // One block per CU (8 wavefronts); the grid never exceeds what the device holds resident
-// at once, so every block runs concurrently and the grid-wide barriers complete.  Four
-// phases separated by two barriers:
-//   0  tokens staged in LDS; router row n runs on block n % NB, its tokens spread over
-//      the block's wavefronts.                                           -- grid sync
-//   1  every block routes all T tokens itself from the logits (top-k per wavefront,
-//      histogram, scans, stable slot lists in LDS): no launch, no second sync.  Block 0
-//      also writes the routing and the padded alignment to global memory.
-//   A  gate/up stream: block b owns gate/up row pair b (2b, 2b+1 and I+2b, I+2b+1) of
-//      every touched expert and of the shared expert; h goes to global memory.
-//                                                                        -- grid sync
-//      Each wavefront then issues its first phase-B weight rows while h is staged.
-//   B  down stream: h staged in LDS, block b owns output rows 8b..8b+7 of every touched
-//      expert and the shared one, y kept in LDS, combine in slot order in fp32.
-// Lane mapping as in gemv.hip: four 16-lane DPP rows per wavefront, one weight row each,
-// 16-byte column groups per lane, one 4-step DPP sum per dot product set.
+// at once.  Phases:
+//   0  router row n on block n % NB, tokens staged in LDS; every wavefront also loads the
+//      shared expert's gate/up rows of its block's row pair (they do not depend on the
+//      routing, so they stream while the head of the kernel is latency-bound).
+//                                                                  -- grid barrier
+//   1  every block routes all T tokens itself from the logits (top-k per wavefront, token
+//      masks per expert, entry lists): no exchange, no second launch.
+//   A  wavefronts 0..6: gate/up row pair b (2b, 2b+1 and I+2b, I+2b+1) of the shared expert
+//      (entry 0, its rows already in registers) and of every touched expert; each entry's
+//      h values go to an LDS outbox.  Wavefront 7, the stager, stores the outbox to global
+//      memory entry by entry and publishes how many entries the block has finished; one
+//      wavefront of block 0 publishes the minimum over the blocks; the stagers copy the h
+//      rows of every entry that all blocks have finished into LDS with direct-to-LDS
+//      loads, while the gate/up stream goes on.
+//   B  wavefronts 0..6, each as soon as it runs out of gate/up entries: down rows
+//      8b..8b+7 of the shared expert and of every touched expert, weights prefetched four
+//      entries deep; an entry is computed once the stager has staged its h rows.  y stays
+//      in LDS, the combine sums in slot order in fp32.
+// There is no grid barrier between the two expert phases: an entry's down projection waits
+// only for that entry's h, so the down stream starts while slower blocks finish gate/up.
+// The compute wavefronts never wait for a store: all stores that other blocks read come
+// from the stager, whose memory queue holds nothing else.
 //
-// Grid barrier: each block stores this call's token into its own flag word, one
-// wavefront of block 0 polls all flags with one coalesced load per round and then
-// stores the token into a release word that every block polls; spins are bounded, so a
-// misuse can give wrong results but never a hang.  Wavefront 0 does the polling and never
-// has weight prefetches in flight at a barrier: vector loads return in issue order, so a
-// poll queued behind 16 KiB of prefetch would see the flags microseconds late.  Data that crosses a barrier (logits,
-// gate logits, h) is written and read with agent-scope atomic accesses (sc1: coherent
-// across the XCDs' L2s), so the barrier needs no cache write-back or invalidate --
-// every wavefront waits for its own stores to complete before its block arrives.
+// Lane mapping: four 16-lane DPP rows per wavefront, one weight row each, 16-byte column
+// groups per lane, one 4-step DPP sum per dot product.
+//
+// Synchronisation through global memory uses agent-scope atomic loads and stores (sc1:
+// coherent across the XCDs' L2s) for every word that crosses blocks (logits, gate logits,
+// h, flags, progress counts), and each word has one writer -- no read-modify-write on a
+// shared word, which the memory side would serialise.  A flag or count is stored only after
+// the data it announces has completed (vmcnt), so no cache write-back or invalidate is
+// needed.  Every wait is bounded: a wait that gives up adds one to the workspace's status
+// word and the affected blocks write NaN for their output rows, so a misuse (a block that
+// never became resident) is visible and never hangs.
 
 #include <algorithm>
 #include <atomic>
@@ -48,13 +57,17 @@ namespace moe {
 namespace {
 constexpr int kNW = 8;
 constexpr int kNT = kNW * kWave;
-constexpr int kOct = 8;  // output rows per block in phase B
+constexpr int kStager = kNW - 1;  // the wavefront that publishes and stages h
+constexpr int kAggr = kNW - 2;    // in block 0: the wavefront that publishes the blocks' minimum
+constexpr unsigned kTokMask = 0x7FFFFFFFu, kBarErr = 0x80000000u, kNoFlag = 0xFFFFFFFFu;
+constexpr int kOct = 8;           // output rows per block in phase B
 // Widths (elements) the lanes' column groups span: H <= kXW, I and I_s <= kHW.  The LDS
 // rows of the tokens and of h end in two zero uint4; a lane's column index beyond the row
 // is clamped onto them (its weights are zero too), so the dot-product loops have no
 // bounds tests and no branch.
 constexpr int kXW = 2048;
 constexpr int kHW = 512;
+typedef __attribute__((address_space(3))) void lds_void;
 }  // namespace
 
 __host__ __device__ __forceinline__ size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -67,10 +80,13 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned *p) {
 __device__ __forceinline__ void st_agent(unsigned *p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void add_agent(unsigned *p, unsigned v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Wait until this wavefront's stores have completed (vmcnt counts loads and stores in
-// issue order, so this also waits for earlier loads); the clobber keeps the compiler from
-// moving memory operations across it.
+// Wait until this wavefront's earlier vector memory operations have completed (vmcnt
+// counts loads and stores in issue order); the clobber keeps the compiler from moving
+// memory operations across it.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Mark a register buffer as consumed here: the compiler waits for its loads at this point,
@@ -81,69 +97,12 @@ __device__ __forceinline__ void consume(const uint4 (&w)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" ::"v"(w[i].x), "v"(w[i].y), "v"(w[i].z), "v"(w[i].w));
 }
 
-// Barrier words (kBarrierWords in the workspace): arrival flags [kMaxBlocks], the release
-// word, the timeout count.
-
-// flags[kMaxBlocks]: per-block arrival words, then the release word and a timeout count.
-// Every wavefront that wrote data the other blocks will read calls wait_stores() first.
-// The barrier is split in two: grid_arrive stores the block's arrival word once every
-// wavefront got there; grid_wait polls for the release.  Work issued between the two
-// (loads only) overlaps the wait without delaying the arrival.
-__device__ __forceinline__ void grid_arrive(unsigned *flags, unsigned token) {
-  __syncthreads();
-  if (threadIdx.x == 0) st_agent(&flags[blockIdx.x], token);
-}
-__device__ __forceinline__ void grid_wait(unsigned *flags, unsigned token) {
-  const unsigned nb = gridDim.x;
-  unsigned *rel = flags + kMaxBlocks;
-  if (blockIdx.x == 0 && threadIdx.x < kWave) {
-    unsigned spins = 0;
-    while (true) {
-      // every flag of a round loaded at once (no short-circuit chain of loads)
-      constexpr int kPer = kMaxBlocks / kWave;
-      unsigned v[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const unsigned i = threadIdx.x + kWave * j;
-        if (kWave * j < nb) v[j] = ld_agent(&flags[i < nb ? i : nb - 1]);
-      }
-      bool ok = true;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (kWave * j < nb) ok &= v[j] == token;
-      if (__all(ok)) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        if (threadIdx.x == 0) atomicAdd(rel + 1, 1u);
-        break;
-      }
-    }
-    if (threadIdx.x == 0) st_agent(rel, token);
-  }
-  if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    while (ld_agent(rel) != token) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        atomicAdd(rel + 1, 1u);
-        break;
-      }
-    }
-  }
-  asm volatile("" ::: "memory");
-  __syncthreads();
-}
-__device__ __forceinline__ void grid_barrier(unsigned *flags, unsigned token) {
-  grid_arrive(flags, token);
-  grid_wait(flags, token);
-}
-
-// Block barrier for LDS data only: waits for this wavefront's LDS operations but not for
-// its vector memory operations, so loads stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// A wait that gave up: count it in the workspace (the caller reads the count; the only
+// read-modify-write on a global word, and only on this path) and mark the block, which then
+// writes NaN for its output rows.
+__device__ __forceinline__ void note_timeout(unsigned *bar, int *s_err) {
+  add_agent(bar + kBarStatus, 1u);
+  __hip_atomic_store(s_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // VPG: weights per 16-byte column group -- 8 bf16, 16 fp8 codes, or 32 MXFP4 codes (which
@@ -166,7 +125,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int xg = G8 + 2;                                                // uint4 per LDS token row
   const int hg = ((a.has_shared && a.I_s > a.I) ? a.I_s : a.I) / 8 + 2;  // uint4 per LDS h row
 
-  // ---------------- LDS: routing region, then the data region (x, later h and y)
+  // ---------------- LDS: routing region, tokens, expert outputs y, h rows
   int *s_ids = reinterpret_cast<int *>(smem);         // [T*k]
   float *s_topw = reinterpret_cast<float *>(s_ids + n_slots);
   int *s_slots = reinterpret_cast<int *>(s_topw + n_slots);      // [T*k] grouped by expert
@@ -181,19 +140,31 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   unsigned *s_mhi = s_mlo + E;                                    // [E] tokens 32..63
   __shared__ int s_nt;
   __shared__ int s_qa, s_qb;  // phase A / phase B entry counters
-  __shared__ uint32_t s_wsum[2 * kNW];
-  char *data = smem + a.lds_route;
-  // this call's barrier tokens follow the workspace's last release word: block 0 rewrites it
-  // only once every block has arrived, and a block's arrival depends on this load
-  const unsigned tok0 = ld_agent(a.bar + kMaxBlocks);
+  __shared__ int s_hready;    // phase-B entries whose h rows are staged (shared expert first)
+  __shared__ int s_err;       // a wait of this block gave up
+  __shared__ unsigned s_tok;  // this call's barrier token
+  // entries whose gate/up rows of this block are in the outbox (or that have none here)
+  __shared__ unsigned long long s_done[(kMaxExperts + 1 + 63) / 64];
+  uint4 *sx = reinterpret_cast<uint4 *>(smem + a.lds_route);            // [T][xg]
+  float *s_y = reinterpret_cast<float *>(sx + (size_t)T * xg);          // [T*k][8]
+  float *s_ys = s_y + (size_t)n_slots * kOct;                           // [T][8]
+  // h values of this block's row pair, one packed pair per slot position (then T shared)
+  uint32_t *s_out = reinterpret_cast<uint32_t *>(s_ys + (size_t)T * kOct);  // [T*k + T]
+  uint4 *hl = reinterpret_cast<uint4 *>(smem + a.lds_route + al16((size_t)T * xg * 16) +
+                                        al16((size_t)(n_slots + T) * (kOct + 1) * 4));  // [T*k + T][hg]
+  // this call's barrier token follows the release word the previous call left: block 0
+  // rewrites that word only after every block has arrived, so every block reads the same
+  // value here (the token lives in bits 0..30, never 0, so it differs from a cleared flag)
+  unsigned rel0 = 0;
+  if (tid == 0) rel0 = ld_agent(a.bar + kBarRelease);
 
-  // ---------------- phase 0: router rows, tokens to LDS
+  // ---------------- phase 0: router rows, tokens to LDS, the shared expert's gate/up
   const int NR = E + (a.w_sg != nullptr ? 1 : 0);
   // Router row n runs on block n % NB; every wavefront of the block holds the row (the
   // block's 8 loads of it share the CU's caches) and takes the tokens wave, wave + 8, ...,
   // so each token's dot product is one short chain.  The block's first kRR rows and their
   // biases are loaded first of all.
-  constexpr int kRR = 3;
+  constexpr int kRR = 2;
   float4 wr[kRR][CR];
   float bias[kRR];
   auto load_router_row = [&](float4(&w)[CR], float &b, int n) {
@@ -211,17 +182,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // phase-A weight buffers; the prefetch wavefront's first entry is the shared expert
-  const int NPair = (a.has_shared && a.I_s > a.I ? a.I_s : a.I) / 2;
   uint4 wa[CGU], wb[CGU];
   uint32_t xa[NSU], xb[NSU];  // MXFP4: the E8M0 scale byte of each of the lane's groups
   // Weight rows are streamed with raw buffer loads: the expert's matrix is the buffer (base
   // in scalar registers), the lane's row and column offset one VGPR, the column group a
-  // uniform scalar offset.  Exactly CGU (CGD per row set) load instructions, all in range:
-  // groups past the row (whole groups: H, I, I_s are multiples of 16 groups) reload the
-  // last group and are zeroed where they are used, so nothing waits for a load here.
+  // uniform scalar offset.  Exactly kGuLoads load instructions, all in range: groups past
+  // the row (whole groups: H, I, I_s are multiples of 16 groups) reload the last group and
+  // are zeroed where they are used, so nothing waits for a load here.
   typedef int i4_t __attribute__((ext_vector_type(4)));
-  constexpr int kNt = 2;  // cache policy: non-temporal (weights are read once)
+  constexpr int kNt = 2;    // cache policy: non-temporal (weights are read once)
+  constexpr int kSc1 = 16;  // cache policy: coherent across the XCDs (data other blocks wrote)
   auto as_u4 = [](i4_t v) { return make_uint4(v.x, v.y, v.z, v.w); };
   // the lane's byte offset in an expert's gate/up matrix for row pair p (gate rows 2p, 2p+1,
   // up rows Iw+2p, Iw+2p+1): fixed for the whole phase, computed once
@@ -241,7 +211,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int c = 0; c < CGU; ++c) w[c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff, 256 * min(c, last), kNt));
     if (kFp4) {
-      const uint8_t *sbank = shared ? (const uint8_t *)a.ss_gu : (const uint8_t *)a.s_gu + (size_t)e * 2 * a.I * (H / VPG);
+      const uint8_t *sbank = shared ? a.xs_gu : a.x_gu + (size_t)e * 2 * a.I * (H / VPG);
       const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t *>(sbank), 0, valid ? 2 * Iw * (H / VPG) : 0, 0x00020000);
 #pragma unroll
@@ -270,9 +240,82 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __hip_atomic_store(dst, n < E ? v + b : v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
+  // One token's gate/up partial sums for the wavefront's four rows (lane row group rg): the
+  // token's LDS reads in groups of 4, the next group issued before the current one is used
+  // (scheduling barriers keep at most two groups in registers); one accumulation chain in
+  // lane-loop order.  Column groups of w past the row must be zero.
+  auto gu_token = [&](const uint4(&w)[CGU], const float(&bsc)[NSU], int t) {
+    const uint4 *xr = sx + (size_t)t * xg;
+    float acc = 0.0f;
+    constexpr int kGrp = 4, NG = CGU / kGrp, XPG = VPG / 8;  // uint4 of x per column group
+    static_assert(CGU % kGrp == 0, "column groups come in fours");
+    uint4 xv[2][kGrp * XPG];
+    auto read_group = [&](uint4(&dst)[kGrp * XPG], int gi) {
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        const int gu = min(l16 + 16 * (gi * kGrp + u), H / VPG);  // H / VPG: the zero pad
+        if (VPG == 8) {
+          dst[u] = xr[gu];
+        } else if (kFp4) {  // four uint4 a group: a group past the row rereads the last one
+          const int gv = min(gu, H / VPG - 1);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) dst[4 * u + d] = xr[4 * gv + d];
+        } else {
+          dst[2 * u] = xr[2 * gu];
+          dst[2 * u + 1] = xr[2 * gu + 1];
+        }
+      }
+    };
+    read_group(xv[0], 0);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (gi + 1 < NG) read_group(xv[(gi + 1) & 1], gi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        const int c = gi * kGrp + u;
+        const uint4 wc = w[c];
+        if (VPG == 8) {
+          acc = dot8_bf16(wc, xv[gi & 1][u], acc);
+        } else if (kFp4) {
+          acc = fmaf(dot32_fp4_bf16(wc, &xv[gi & 1][4 * u]), bsc[c], acc);
+        } else {
+          const uint4 x0 = xv[gi & 1][2 * u], x1 = xv[gi & 1][2 * u + 1];
+          acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.x), x0.x, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.x), x0.y, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.y), x0.z, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.y), x0.w, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.z), x1.x, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.z), x1.y, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.w), x1.z, acc);
+          acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.w), x1.w, acc);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return row16_sum(acc);
+  };
+  // Prepare a gate/up weight buffer for use: wait for it, zero the column groups past the row
+  // (whole groups, holding a repeated load), decode the MXFP4 block scales.
+  auto gu_ready = [&](uint4(&w)[CGU], const uint32_t(&xsc)[NSU], float(&bsc)[NSU]) {
+    consume(w);
+#pragma unroll
+    for (int c = 0; c < CGU; ++c)
+      if (16 * c >= H / VPG) w[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < NSU; ++c) bsc[c] = kFp4 ? e8m0_scale(xsc[c]) : 1.0f;
+  };
+  // h values of one token for row pair pA: lane 0 puts silu(g) * u of rows 2pA and 2pA+1 (the
+  // row sums sit in lanes 0, 16 | 32, 48, scaled by the fp8 row scales) into outbox slot p
+  auto gu_out = [&](float acc, int p, float sg0, float sg1, float su0, float su1) {
+    const float g0 = lane_value(acc, 0) * sg0, g1 = lane_value(acc, 16) * sg1;
+    const float u0 = lane_value(acc, 32) * su0, u1 = lane_value(acc, 48) * su1;
+    if (lane == 0) s_out[p] = pack_bf16x2(g0 / (1.0f + expf(-g0)) * u0, g1 / (1.0f + expf(-g1)) * u1);
+  };
+
   // The router's critical path: the block's rows and each wavefront's first token (t = wave)
-  // straight into registers, before the token staging's loads (loads return in issue
-  // order); column groups past the row read the last group and are zeroed (zero weights).
+  // straight into registers, before the other loads (loads return in issue order); column
+  // groups past the row read the last group and are zeroed (zero weights).
 #pragma unroll
   for (int r = 0; r < kRR; ++r)
     if (blockIdx.x + r * NB < NR) load_router_row(wr[r], bias[r], blockIdx.x + r * NB);
@@ -286,10 +329,15 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (g >= H / 4) xt[c] = make_uint2(0, 0);
     }
   }
+  // the shared expert's gate/up rows of this block's row pair, in every wavefront: whichever
+  // wavefront takes entry 0 first in phase A has them (the block's 8 loads share the CU's
+  // caches); the bytes stream during the head
+  const int pA = blockIdx.x;
+  const bool shA = a.has_shared && 2 * pA < a.I_s;
+  gu_load(wa, xa, shA, true, 0, gu_voff(a.I_s, pA), gu_soff(a.I_s, pA));
 
   // tokens to LDS (for phase A and the router's later tokens), in rows of xg uint4 ending
   // in the zero pad; unguarded (clamped) loads, so they are in flight together
-  uint4 *sx = reinterpret_cast<uint4 *>(data);
   {
     constexpr int kStep = kNT, kB = 8;
     const uint4 *gx = reinterpret_cast<const uint4 *>(a.x);
@@ -320,16 +368,28 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       x_store(base);
     }
   }
-  const uint4 *xs = sx;
+  // LDS set-up: the token masks, the h rows (zero, so that the pads and any row tail no
+  // copy fills read as zeros), the counters; this call's readiness counts start at zero
   for (int e = tid; e < E; e += kNT) {
     s_mlo[e] = 0u;
     s_mhi[e] = 0u;
+  }
+  for (int i = tid; i < (n_slots + T) * hg; i += kNT) hl[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < (kMaxExperts + 1 + 63) / 64; i += kNT) s_done[i] = 0ull;
+  if (tid == 0) {
+    s_err = 0;
+    s_hready = 0;
+    const unsigned t = ((rel0 & kTokMask) + 1u) & kTokMask;
+    s_tok = t == 0 ? 1u : t;
+    // this call's progress counts start at zero (published before the barrier)
+    st_agent(a.bar + kBarProgress + blockIdx.x, 0u);
+    if (blockIdx.x == 0) st_agent(a.bar + kBarReady, 0u);
   }
   __syncthreads();
 
   // the wavefront's further tokens and the rows past the first kRR, from the staged tokens
   auto lds_token = [&](uint2(&xv)[CR], int t) {
-    const uint2 *x2 = reinterpret_cast<const uint2 *>(xs) + (size_t)t * (2 * xg);
+    const uint2 *x2 = reinterpret_cast<const uint2 *>(sx) + (size_t)t * (2 * xg);
 #pragma unroll
     for (int c = 0; c < CR; ++c) xv[c] = x2[min(lane + kWave * c, H / 4)];  // H / 4: the zero pad
   };
@@ -348,8 +408,62 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       router_dot(wr[0], bias[0], n, t, xv);
     }
   }
-  wait_stores();  // the router rows' logit stores
-  grid_barrier(a.bar, tok0 + 1u);
+  // grid barrier: every wavefront's logit and count stores have completed before the block
+  // stores its arrival flag; wavefront 0 of block 0 polls all flags (one batched load per
+  // lane and round) and stores the release word, which every block polls.  A wait that
+  // gives up sets bit 31 of the release word, so every block of the call knows; a block
+  // whose own wait gave up (it started after the release: its token is off by one) clears
+  // its flag, so that no later call takes the stale token for an arrival.
+  wait_stores();
+  __syncthreads();
+  {
+    const unsigned tok = s_tok;
+    unsigned *flags = a.bar, *rel = a.bar + kBarRelease;
+    if (tid == 0) st_agent(flags + blockIdx.x, tok);
+    if (blockIdx.x == 0 && wave == 0) {
+      constexpr int kPer = kMaxBlocks / kWave;
+      unsigned spins = 0;
+      bool gave_up = false;
+      while (true) {
+        unsigned v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = lane + kWave * j;
+          if (kWave * j < NB) v[j] = ld_agent(flags + (i < NB ? i : NB - 1));
+        }
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (kWave * j < NB) ok &= v[j] == tok;
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          gave_up = true;
+          break;
+        }
+      }
+      if (lane == 0) {
+        if (gave_up) note_timeout(a.bar, &s_err);
+        st_agent(rel, tok | (gave_up ? kBarErr : 0u));
+      }
+    }
+    if (tid == 0) {
+      unsigned spins = 0;
+      unsigned r;
+      while (((r = ld_agent(rel)) & kTokMask) != tok) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          note_timeout(a.bar, &s_err);
+          st_agent(flags + blockIdx.x, kNoFlag);
+          r = 0;
+          break;
+        }
+      }
+      if (r & kBarErr) __hip_atomic_store(&s_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  asm volatile("" ::: "memory");
+  __syncthreads();
 
   // ---------------- phase 1: routing in every block
   {
@@ -421,110 +535,192 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
   const int nr = s_nt;
+  const int sh = a.has_shared ? 1 : 0;  // phase-B entry 0 is the shared expert
+  const int NOct = H / kOct;
+  const int oB = blockIdx.x;
+  const int NEB = oB < NOct ? nr + sh : 0;
 
-  // ---------------- phase A: gate/up of row pair p = b (2b, 2b+1 and I+2b, I+2b+1) for
-  // every entry: entry 0 is the shared expert when this pair has one, then the touched
-  // experts in order of first use.  The wavefronts take entries from an LDS counter, two in
-  // flight each.
-  const int pA = blockIdx.x;
-  const bool shA = a.has_shared && 2 * pA < a.I_s;
-  const int NEA = pA < NPair ? (2 * pA < a.I ? nr : 0) + (shA ? 1 : 0) : 0;
-  {
-    auto compute = [&](uint4(&w)[CGU], const uint32_t(&xsc)[NSU], int q) {
-      consume(w);
-      // column groups past the row (whole groups) hold a repeated load: zero them in place
-#pragma unroll
-      for (int c = 0; c < CGU; ++c)
-        if (16 * c >= H / VPG) w[c] = make_uint4(0, 0, 0, 0);
-      const bool shared = shA && q == 0;
-      const int ri = q - (shA ? 1 : 0);
-      const int e = shared ? 0 : s_e[ri];
-      const int q0 = shared ? 0 : s_start[ri];
-      const int q1 = shared ? T : s_start[ri + 1];
-      const int p = pA;
-      float bsc[NSU];  // MXFP4 block scales of the lane's groups
-#pragma unroll
-      for (int c = 0; c < NSU; ++c) bsc[c] = kFp4 ? e8m0_scale(xsc[c]) : 1.0f;
-      float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
-      if (VPG == 16) {
-        const float *sc = shared ? a.ss_gu : a.s_gu + (size_t)e * 2 * a.I;
-        const int Iw = shared ? a.I_s : a.I;
-        sg0 = sc[2 * p];
-        sg1 = sc[2 * p + 1];
-        su0 = sc[Iw + 2 * p];
-        su1 = sc[Iw + 2 * p + 1];
+  const int total = nr + sh;                     // phase-B entries (and gate/up entries)
+  const bool ownR = 2 * pA < a.I;                // this block has a gate/up row pair of the routed experts
+  if (wave == kStager) {
+    // ---------------- the stager.  (1) Stores the outbox of every entry the compute
+    // wavefronts have finished, in entry order, then -- once the stores have completed --
+    // publishes the count in the block's progress word.  (2) Copies the h rows of every
+    // entry all blocks have finished (block 0's published minimum) into LDS, in phase-B entry
+    // order: row r < T*k of hl is position r of the slots grouped by entry, row T*k + t the
+    // shared expert's token t; one direct-to-LDS load per row (64 lanes x 16 bytes = 1 KiB,
+    // the row of I = 512); consecutive entries have consecutive rows.  Coherent (sc1) loads:
+    // h was written by other blocks.
+    // entries with no gate/up rows in this block are done from the start
+    if (lane == 0) {
+      if (sh && !shA) s_done[0] |= 1ull;
+      if (!ownR)
+        for (int q = sh; q < total; ++q) s_done[q >> 6] |= 1ull << (q & 63);
+    }
+    const int rbytes = a.I * 2, srbytes = a.I_s * 2;
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(a.h, 0, NEB > 0 ? n_slots * rbytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rhs =
+        __builtin_amdgcn_make_buffer_rsrc(a.h_s, 0, (NEB > 0 && sh) ? T * srbytes : 0, 0x00020000);
+    // the first entry at or after q that this block has not finished
+    auto done_upto = [&](int q) {
+      while (q < total) {
+        const unsigned long long m =
+            __hip_atomic_load(&s_done[q >> 6], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >> (q & 63);
+        const int run = m == ~0ull >> (q & 63) ? 64 - (q & 63) : (int)__builtin_ctzll(~m);
+        q += run;
+        if (run < 64 - ((q - run) & 63)) break;
       }
-      for (int qq = q0; qq < q1; ++qq) {
-        const int slot = shared ? qq : s_slots[qq];
-        const int t = shared ? qq : s_stok[qq];
-        const uint4 *xr = xs + (size_t)t * xg;
-        float acc = 0.0f;
-        // the token's LDS reads in groups of 4, the next group issued before the current one
-        // is used (scheduling barriers keep at most two groups in registers); one
-        // accumulation chain in lane-loop order
-        constexpr int kGrp = 4, NG = CGU / kGrp, XPG = VPG / 8;  // uint4 of x per column group
-        static_assert(CGU % kGrp == 0, "column groups come in fours");
-        uint4 xv[2][kGrp * XPG];
-        auto read_group = [&](uint4(&dst)[kGrp * XPG], int gi) {
-#pragma unroll
-          for (int u = 0; u < kGrp; ++u) {
-            const int gu = min(l16 + 16 * (gi * kGrp + u), H / VPG);  // H / VPG: the zero pad
-            if (VPG == 8) {
-              dst[u] = xr[gu];
-            } else if (kFp4) {  // four uint4 a group: a group past the row rereads the last one
-              const int gv = min(gu, H / VPG - 1);
-#pragma unroll
-              for (int d = 0; d < 4; ++d) dst[4 * u + d] = xr[4 * gv + d];
-            } else {
-              dst[2 * u] = xr[2 * gu];
-              dst[2 * u + 1] = xr[2 * gu + 1];
-            }
-          }
-        };
-        read_group(xv[0], 0);
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          if (gi + 1 < NG) read_group(xv[(gi + 1) & 1], gi + 1);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int u = 0; u < kGrp; ++u) {
-            const int c = gi * kGrp + u;
-            const uint4 wc = w[c];
-            if (VPG == 8) {
-              acc = dot8_bf16(wc, xv[gi & 1][u], acc);
-            } else if (kFp4) {
-              acc = fmaf(dot32_fp4_bf16(wc, &xv[gi & 1][4 * u]), bsc[c], acc);
-            } else {
-              const uint4 x0 = xv[gi & 1][2 * u], x1 = xv[gi & 1][2 * u + 1];
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.x), x0.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.x), x0.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.y), x0.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.y), x0.w, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.z), x1.x, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.z), x1.y, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<false>(wc.w), x1.z, acc);
-              acc = dot2_bf16(fp8x2_to_bf16x2<true>(wc.w), x1.w, acc);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        acc = row16_sum(acc);
-        const float g0 = lane_value(acc, 0) * sg0, g1 = lane_value(acc, 16) * sg1;
-        const float u0 = lane_value(acc, 32) * su0, u1 = lane_value(acc, 48) * su1;
-        if (lane == 0) {
-          uint16_t *dst = shared ? a.h_s + (size_t)t * a.I_s + 2 * p : a.h + (size_t)slot * a.I + 2 * p;
-          __hip_atomic_store(reinterpret_cast<uint32_t *>(dst),
-                             pack_bf16x2(g0 / (1.0f + expf(-g0)) * u0, g1 / (1.0f + expf(-g1)) * u1),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      return min(q, total);
     };
-    const int voff_r = gu_voff(a.I, pA), voff_s = gu_voff(a.I_s, pA);
-    const int soff_r = gu_soff(a.I, pA), soff_s = gu_soff(a.I_s, pA);
-    auto load = [&](uint4(&w)[CGU], uint32_t(&xs)[NSU], int q) {  // q >= NEA: an empty descriptor
-      const bool valid = q < NEA, shared = shA && q == 0;
-      gu_load(w, xs, valid, shared, (valid && !shared) ? s_e[q - (shA ? 1 : 0)] : 0, shared ? voff_s : voff_r,
-              shared ? soff_s : soff_r);
+    int pub = 0, staged = 0;
+    unsigned spins = 0;
+    while (pub < total || (NEB > 0 && staged < total)) {
+      bool moved = false;
+      const int m = done_upto(pub);
+      asm volatile("" ::: "memory");
+      if (m > pub) {
+        // (1) the outbox of entries [pub, m), then the progress word
+        if (sh && pub == 0 && shA)
+          for (int t = lane; t < T; t += kWave)
+            st_agent(reinterpret_cast<unsigned *>(a.h_s + (size_t)t * a.I_s + 2 * pA), s_out[n_slots + t]);
+        if (ownR) {
+          const int p0 = s_start[max(pub - sh, 0)], p1 = s_start[m - sh];
+          for (int p = p0 + lane; p < p1; p += kWave)
+            st_agent(reinterpret_cast<unsigned *>(a.h + (size_t)s_slots[p] * a.I + 2 * pA), s_out[p]);
+        }
+        wait_stores();
+        if (lane == 0) st_agent(a.bar + kBarProgress + blockIdx.x, (unsigned)m);
+        pub = m;
+        moved = true;
+      }
+      if (NEB > 0 && staged < total) {
+        // (2) entries every block has finished: h rows into LDS
+        const unsigned g = __builtin_amdgcn_readfirstlane(ld_agent(a.bar + kBarReady));
+        const int gr = min((int)(g & kTokMask), total);
+        if (g & kBarErr) {  // block 0 gave up waiting for some block: stage what there is
+          if (lane == 0) __hip_atomic_store(&s_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        const int upto = (g & kBarErr) ? total : gr;
+        if (upto > staged) {
+          if (sh && staged == 0)
+            for (int t = 0; t < T; ++t)
+              if (lane * 16 < srbytes)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rhs, (lds_void *)(hl + (size_t)(n_slots + t) * hg), 16,
+                                                         lane * 16, t * srbytes, 0, kSc1);
+          if (upto > sh) {
+            const int r0 = s_start[max(staged - sh, 0)], r1 = s_start[upto - sh];
+            for (int r = r0; r < r1; ++r)
+              if (lane * 16 < rbytes)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void *)(hl + (size_t)r * hg), 16, lane * 16,
+                                                         s_slots[r] * rbytes, 0, kSc1);
+          }
+          wait_stores();  // the copies have landed in LDS
+          staged = upto;
+          if (lane == 0) __hip_atomic_store(&s_hready, staged, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          moved = true;
+        }
+      }
+      if (moved) {
+        spins = 0;
+      } else {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {  // let the compute wavefronts finish (their rows become NaN)
+          if (lane == 0) {
+            note_timeout(a.bar, &s_err);
+            __hip_atomic_store(&s_hready, total, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          break;
+        }
+      }
+    }
+    // the padded counts and their scan for the caller's alignment (one wavefront, 64 experts
+    // a step)
+    {
+      const int BM = a.BM;
+      int run = 0;
+      for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        const int c = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : 0;
+        const uint32_t pc = (uint32_t)((c + BM - 1) / BM * BM);
+        const uint32_t incl = wave_incl_scan_u32(pc);
+        if (e < E) {
+          s_cnt[e] = c;
+          s_off[e] = run + (int)(incl - pc);
+        }
+        run += __builtin_amdgcn_readlane((int)incl, kWave - 1);
+      }
+      if (lane == 0) s_off[E] = run;
+    }
+  } else if (blockIdx.x == 0 && wave == kAggr) {
+    // ---------------- block 0's aggregator: the minimum of all blocks' progress counts into the
+    // ready word the stagers poll (one batched load per lane and round)
+    constexpr int kPer = kMaxBlocks / kWave;
+    unsigned last = 0, spins = 0;
+    while ((int)last < total) {
+      unsigned v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = lane + kWave * j;
+        if (kWave * j < NB) v[j] = ld_agent(a.bar + kBarProgress + (i < NB ? i : NB - 1));
+      }
+      unsigned mn = ~0u;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (kWave * j < NB) mn = min(mn, v[j]);
+      mn = wave_min_u32(mn);
+      if (mn > last) {
+        last = mn;
+        if (lane == 0) st_agent(a.bar + kBarReady, last);
+        spins = 0;
+      } else {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {  // some block never finished: release the stagers, flagged
+          if (lane == 0) {
+            note_timeout(a.bar, &s_err);
+            st_agent(a.bar + kBarReady, (unsigned)total | kBarErr);
+          }
+          break;
+        }
+      }
+    }
+  } else {
+    // ---------------- phase A: gate/up of row pair pA for the shared expert (entry 0, with one)
+    // and every touched expert, taken from an LDS counter by the compute wavefronts, two
+    // entries in flight each; the h values go to the outbox
+    auto owned = [&](int q) { return (sh && q == 0) ? shA : ownR; };
+    auto compute_a = [&](uint4(&w)[CGU], const uint32_t(&xsc)[NSU], int q) {
+      float bsc[NSU];
+      gu_ready(w, xsc, bsc);
+      const bool shared = sh && q == 0;
+      if (owned(q)) {
+        const int ri = q - sh;
+        const int e = shared ? 0 : s_e[ri];
+        const int Iw = shared ? a.I_s : a.I;
+        const int q0 = shared ? 0 : s_start[ri], q1 = shared ? T : s_start[ri + 1];
+        float sg0 = 1.f, sg1 = 1.f, su0 = 1.f, su1 = 1.f;
+        if (VPG == 16) {
+          const float *sc = shared ? a.ss_gu : a.s_gu + (size_t)e * 2 * a.I;
+          sg0 = sc[2 * pA];
+          sg1 = sc[2 * pA + 1];
+          su0 = sc[Iw + 2 * pA];
+          su1 = sc[Iw + 2 * pA + 1];
+        }
+        for (int qq = q0; qq < q1; ++qq)
+          gu_out(gu_token(w, bsc, shared ? qq : s_stok[qq]), shared ? n_slots + qq : qq, sg0, sg1, su0, su1);
+      }
+      // the outbox writes of this wavefront precede the done bit (LDS operations of one
+      // wavefront complete in order)
+      asm volatile("" ::: "memory");
+      if (lane == 0)
+        __hip_atomic_fetch_or(&s_done[q >> 6], 1ull << (q & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    const int voff_r = gu_voff(a.I, pA), soff_r = gu_soff(a.I, pA);
+    auto load_a = [&](uint4(&w)[CGU], uint32_t(&xs)[NSU], int q) {  // q >= total or not owned: an empty descriptor
+      const bool shared = sh && q == 0;
+      const bool valid = q < total && owned(q);
+      gu_load(w, xs, valid, shared, (valid && !shared) ? s_e[q - sh] : 0, shared ? gu_voff(a.I_s, pA) : voff_r,
+              shared ? gu_soff(a.I_s, pA) : soff_r);
     };
     auto grab = [&]() -> int {
       int v = 0;
@@ -532,189 +728,79 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return __builtin_amdgcn_readfirstlane(v);
     };
     // every load is issued (past the last entry they read nothing), so the compiler's wait
-    // counts are the same on every path and no prefetch is waited for early
+    // counts are the same on every path and no prefetch is waited for early; entry 0 (the
+    // shared expert) is the first grab of one wavefront, whose rows from phase 0 are in wa
     int q = grab();
     int q2 = grab();
-    load(wa, xa, q);
-    load(wb, xb, q2);
-    while (q < NEA) {
-      compute(wa, xa, q);
+    if (!(sh && q == 0)) load_a(wa, xa, q);
+    load_a(wb, xb, q2);
+    while (q < total) {
+      compute_a(wa, xa, q);
       const int q3 = grab();
-      load(wa, xa, q3);
-      if (q2 >= NEA) break;
-      compute(wb, xb, q2);
+      load_a(wa, xa, q3);
+      if (q2 >= total) break;
+      compute_a(wb, xb, q2);
       const int q4 = grab();
-      load(wb, xb, q4);
+      load_a(wb, xb, q4);
       q = q3;
       q2 = q4;
     }
-  }
 
-  // ---------------- phase B: down + combine for output rows 8o .. 8o+7, o = b.  Entries:
-  // 0 the shared expert (with one), then the touched experts, taken from an LDS counter.
-  // Each wavefront except 0 takes its first two entries and starts their weight loads
-  // before the second grid barrier (wavefront 0 polls the barrier and keeps its load queue
-  // empty), so the barrier wait streams weights.
-  const int NOct = H / kOct;
-  const int oB = blockIdx.x;
-  const int NEB = oB < NOct ? nr + (a.has_shared ? 1 : 0) : 0;
-  uint4 da[2][CGD], db[2][CGD], dc[2][CGD], dd[2][CGD];
-  uint32_t sa[2][NSD], sb[2][NSD], sc_[2][NSD], sd[2][NSD];  // MXFP4 scale bytes
-  // the lane's byte offsets in a down matrix for output rows 8o+rg and 8o+4+rg (row length
-  // I or I_s): fixed for the whole phase, computed once
-  const int dv_r0 = nbytes((kOct * oB + rg) * a.I) + l16 * 16, dv_r1 = dv_r0 + nbytes(4 * a.I);
-  const int dv_s0 = nbytes((kOct * oB + rg) * a.I_s) + l16 * 16, dv_s1 = dv_s0 + nbytes(4 * a.I_s);
-  // MXFP4: the lane's offsets in the scale matrix (one byte per group)
-  const int ds_r0 = (kOct * oB + rg) * (a.I / VPG) + l16, ds_r1 = ds_r0 + 4 * (a.I / VPG);
-  const int ds_s0 = (kOct * oB + rg) * (a.I_s / VPG) + l16, ds_s1 = ds_s0 + 4 * (a.I_s / VPG);
-  auto dn_load = [&](uint4(&w)[2][CGD], uint32_t(&xs)[2][NSD], int q) {  // q >= NEB: an empty descriptor
-    const bool valid = q < NEB;
-    const bool shared = a.has_shared && q == 0;
-    const int ri = q - (a.has_shared ? 1 : 0);
-    const int K = shared ? a.I_s : a.I;
-    const int e = (shared || !valid) ? 0 : __builtin_amdgcn_readfirstlane(s_e[ri]);  // uniform: a scalar descriptor
-    const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + nbytes((size_t)e * H * a.I);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
-                                                                        valid ? nbytes(H * K) : 0, 0x00020000);
-    const int last = K / VPG / 16 - 1;
-    const int v0 = shared ? dv_s0 : dv_r0, v1 = shared ? dv_s1 : dv_r1;
+    // ---------------- phase B: down rows 8o .. 8o+7, o = b, for entry 0 (the shared expert,
+    // with one) and the touched experts, taken from an LDS counter; four entries in flight
+    // per wavefront; an entry waits only for its staged h rows
+    uint4 da[2][CGD], db[2][CGD], dc[2][CGD], dd[2][CGD];
+    uint32_t sa[2][NSD], sb[2][NSD], sc_[2][NSD], sd[2][NSD];  // MXFP4 scale bytes
+    // the lane's byte offsets in a down matrix for output rows 8o+rg and 8o+4+rg (row length
+    // I or I_s): fixed for the whole phase, computed once
+    const int dv_r0 = nbytes((kOct * oB + rg) * a.I) + l16 * 16, dv_r1 = dv_r0 + nbytes(4 * a.I);
+    const int dv_s0 = nbytes((kOct * oB + rg) * a.I_s) + l16 * 16, dv_s1 = dv_s0 + nbytes(4 * a.I_s);
+    // MXFP4: the lane's offsets in the scale matrix (one byte per group)
+    const int ds_r0 = (kOct * oB + rg) * (a.I / VPG) + l16, ds_r1 = ds_r0 + 4 * (a.I / VPG);
+    const int ds_s0 = (kOct * oB + rg) * (a.I_s / VPG) + l16, ds_s1 = ds_s0 + 4 * (a.I_s / VPG);
+    auto dn_load = [&](uint4(&w)[2][CGD], uint32_t(&xs)[2][NSD], int q) {  // q >= NEB: an empty descriptor
+      const bool valid = q < NEB;
+      const bool shared = sh && q == 0;
+      const int ri = q - sh;
+      const int K = shared ? a.I_s : a.I;
+      const int e = (shared || !valid) ? 0 : __builtin_amdgcn_readfirstlane(s_e[ri]);  // uniform: a scalar descriptor
+      const uint8_t *bank = shared ? (const uint8_t *)a.ws_d : (const uint8_t *)a.w_d + nbytes((size_t)e * H * a.I);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(bank), 0,
+                                                                          valid ? nbytes(H * K) : 0, 0x00020000);
+      const int last = K / VPG / 16 - 1;
+      const int v0 = shared ? dv_s0 : dv_r0, v1 = shared ? dv_s1 : dv_r1;
 #pragma unroll
-    for (int c = 0; c < CGD; ++c) {
-      w[0][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v0, 256 * min(c, last), kNt));  // zeroed at use
-      w[1][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v1, 256 * min(c, last), kNt));
-    }
-    const int s0 = shared ? ds_s0 : ds_r0, s1 = shared ? ds_s1 : ds_r1;
-    if (kFp4) {
-      const uint8_t *sbank = shared ? (const uint8_t *)a.ss_d : (const uint8_t *)a.s_d + (size_t)e * H * (a.I / VPG);
-      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sbank), 0,
-                                                                           valid ? H * (K / VPG) : 0, 0x00020000);
-#pragma unroll
-      for (int c = 0; c < NSD; ++c) {
-        xs[0][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s0, 16 * min(c, last), kNt);
-        xs[1][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s1, 16 * min(c, last), kNt);
+      for (int c = 0; c < CGD; ++c) {
+        w[0][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v0, 256 * min(c, last), kNt));  // zeroed at use
+        w[1][c] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rs, v1, 256 * min(c, last), kNt));
       }
-    }
-    if (kFp4) asm volatile("" ::"v"(v0), "v"(v1), "v"(s0), "v"(s1));  // as in gu_load
-    else asm volatile("" ::"v"(v0), "v"(v1));
-  };
-  auto grab_b = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&s_qb, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  wait_stores();  // this wavefront's h stores
-  // Four entries in flight per wavefront.  Wavefronts 1..7 issue the first two between the
-  // block's arrival and the wait for the release (wavefront 0 polls and keeps its load
-  // queue empty), so the barrier wait streams weights and the arrival waits for none of
-  // them.  After the barrier the h loads go first and the other two entries' weights
-  // right behind them: loads return in issue order, so h is not held up by them, and the
-  // weight stream continues while h is staged.
-  int qb1 = 0, qb2 = 0, qb3 = 0, qb4 = 0;
-  const bool early = wave != 0;
-  grid_arrive(a.bar, tok0 + 2u);
-  if (early) {
-    qb1 = grab_b();
-    qb2 = grab_b();
-    dn_load(da, sa, qb1);
-    dn_load(db, sb, qb2);
-  }
-  grid_wait(a.bar, tok0 + 2u);
-  // (after the barrier the tokens are dead: y and h take the data region)
-  float *s_y = reinterpret_cast<float *>(data);  // [T*k][8]
-  float *s_ys = s_y + (size_t)n_slots * kOct;   // [T][8]
-  // h rows in LDS, hg uint4 each ending in the zero pad: row r < T*k is position r of the
-  // slots grouped by expert, row T*k + t the shared expert's token t.  h crosses the barrier:
-  // 16-byte loads with the sc1 cache policy (coherent across the XCDs' L2s).  A block with
-  // no rows in this phase reads from empty descriptors (zeros, no traffic), so every
-  // wavefront issues the same loads.
-  uint4 *hl = reinterpret_cast<uint4 *>(data + al16((size_t)(n_slots + T) * kOct * 4));
-  {
-    constexpr int kSc1 = 16;
-    const int gr = a.I / 8, gs = a.I_s / 8;
-    const bool any = NEB > 0;
-    // one descriptor for h and h_s (h_s lies after h, checked by the launcher): a per-lane
-    // choice between two descriptors would become a loop over them
-    const int dsh = a.has_shared ? (int)((const char *)a.h_s - (const char *)a.h) : 0;
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        a.h, 0, any ? (a.has_shared ? dsh + T * gs * 16 : n_slots * gr * 16) : 0, 0x00020000);
-    const int sh0 = a.has_shared ? T : 0;
-    const int nrow = n_slots + sh0;
-    constexpr int kB = 12;  // 72 rows of 66 uint4 (T = 8) in one round
-    i4_t v[kB];
-    // offsets first (every slot-list read in flight together), then the loads; a lane past
-    // the rows reads past the buffer, which returns zeros
-    auto stage_load = [&](int base) {
-      int off[kB];
+      const int s0 = shared ? ds_s0 : ds_r0, s1 = shared ? ds_s1 : ds_r1;
+      if (kFp4) {
+        const uint8_t *sbank = shared ? a.xs_d : a.x_d + (size_t)e * H * (a.I / VPG);
+        const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sbank), 0,
+                                                                             valid ? H * (K / VPG) : 0, 0x00020000);
 #pragma unroll
-      for (int jj = 0; jj < kB; ++jj) {
-        const int idx = base + jj * kNT, r = idx / hg, g = idx - r * hg;
-        const bool shr = r >= n_slots;  // rows n_slots.. : the shared expert
-        const int sl = s_slots[min(r, n_slots - 1)];
-        const bool ok = idx < nrow * hg && g < (shr ? gs : gr);
-        off[jj] = ok ? (shr ? dsh + ((r - n_slots) * gs + g) * 16 : (sl * gr + g) * 16) : 0x7FFFFFF0;
-      }
-#pragma unroll
-      for (int jj = 0; jj < kB; ++jj) v[jj] = __builtin_amdgcn_raw_buffer_load_b128(rh, off[jj], 0, kSc1);
-    };
-    auto stage_store = [&](int base) {
-#pragma unroll
-      for (int jj = 0; jj < kB; ++jj) {
-        const int idx = base + jj * kNT;
-        if (idx < nrow * hg) hl[idx] = make_uint4(v[jj].x, v[jj].y, v[jj].z, v[jj].w);
-      }
-    };
-    stage_load(tid);
-    if (!early) {
-      qb1 = grab_b();
-      qb2 = grab_b();
-      dn_load(da, sa, qb1);
-      dn_load(db, sb, qb2);
-    }
-    qb3 = grab_b();
-    qb4 = grab_b();
-    dn_load(dc, sc_, qb3);
-    dn_load(dd, sd, qb4);
-    // while those loads are in flight: the padded counts and their block-wide scan for the
-    // caller's alignment (LDS only, so bare barriers)
-    {
-      const int BM = a.BM;
-      const int per = (E + kNT - 1) / kNT;
-      const int e0 = tid * per;
-      uint32_t vb = 0;
-      for (int u = 0; u < per; ++u) {
-        const int e = e0 + u;
-        if (e < E) {
-          const int c = __popc(s_mlo[e]) + __popc(s_mhi[e]);
-          s_cnt[e] = c;
-          vb += (uint32_t)((c + BM - 1) / BM * BM);
+        for (int c = 0; c < NSD; ++c) {
+          xs[0][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s0, 16 * min(c, last), kNt);
+          xs[1][c] = __builtin_amdgcn_raw_buffer_load_b8(rsc, s1, 16 * min(c, last), kNt);
         }
       }
-      const uint32_t ib = wave_incl_scan_u32(vb);
-      if (lane == kWave - 1) s_wsum[wave] = ib;
-      lds_barrier();
-      uint32_t rb = ib - vb;
-      for (int w = 0; w < wave; ++w) rb += s_wsum[w];
-      for (int u = 0; u < per; ++u) {
-        const int e = e0 + u;
-        if (e < E) {
-          s_off[e] = (int)rb;
-          rb += (uint32_t)((s_cnt[e] + BM - 1) / BM * BM);
-        }
-      }
-      if (tid == kNT - 1) s_off[E] = (int)rb;
-    }
-    stage_store(tid);
-    for (int base = tid + kB * kNT; base < nrow * hg; base += kB * kNT) {  // larger blocks
-      stage_load(base);
-      stage_store(base);
-    }
-  }
-  lds_barrier();  // h staged; the weight loads stay in flight
-  {
-    // ---- entries from the LDS counter, four in flight per wavefront
+      if (kFp4) asm volatile("" ::"v"(v0), "v"(v1), "v"(s0), "v"(s1));  // as in gu_load
+      else asm volatile("" ::"v"(v0), "v"(v1));
+    };
+    auto grab_b = [&]() -> int {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&s_qb, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    // entry q's h rows are in LDS once the stager has published a count above q
+    auto wait_staged = [&](int q) {
+      while (__hip_atomic_load(&s_hready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= q)
+        __builtin_amdgcn_s_sleep(1);
+    };
     auto compute = [&](uint4(&w)[2][CGD], const uint32_t(&xsc)[2][NSD], int q) {
-      const bool shared = a.has_shared && q == 0;
-      const int ri = q - (a.has_shared ? 1 : 0);
+      const bool shared = sh && q == 0;
+      const int ri = q - sh;
       const int e = shared ? 0 : s_e[ri];
       const int q0 = shared ? 0 : s_start[ri];
       const int q1 = shared ? T : s_start[ri + 1];
@@ -725,7 +811,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int c = 0; c < CGD; ++c)
         if (16 * c >= Kv) w[0][c] = w[1][c] = make_uint4(0, 0, 0, 0);
-      const int o = oB;
       float bsc[2][NSD];  // MXFP4 block scales
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -734,9 +819,10 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       float sc0 = 1.f, sc1 = 1.f;
       if (VPG == 16) {
         const float *sc = shared ? a.ss_d : a.s_d + (size_t)e * H;
-        sc0 = sc[kOct * o + rg];
-        sc1 = sc[kOct * o + 4 + rg];
+        sc0 = sc[kOct * oB + rg];
+        sc1 = sc[kOct * oB + 4 + rg];
       }
+      wait_staged(q);
       for (int qq = q0; qq < q1; ++qq) {
         const int slot = shared ? qq : s_slots[qq];
         const uint4 *hr = hl + (size_t)(shared ? n_slots + qq : qq) * hg;
@@ -781,16 +867,20 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     };
+    int q1 = grab_b(), q2b = grab_b(), q3 = grab_b(), q4 = grab_b();
+    dn_load(da, sa, q1);
+    dn_load(db, sb, q2b);
+    dn_load(dc, sc_, q3);
+    dn_load(dd, sd, q4);
     // entries are grabbed in increasing order, so the first one past the end ends the loop
-    int q1 = qb1, q2 = qb2, q3 = qb3, q4 = qb4;
     while (q1 < NEB) {
       compute(da, sa, q1);
       q1 = grab_b();
       dn_load(da, sa, q1);
-      if (q2 >= NEB) break;
-      compute(db, sb, q2);
-      q2 = grab_b();
-      dn_load(db, sb, q2);
+      if (q2b >= NEB) break;
+      compute(db, sb, q2b);
+      q2b = grab_b();
+      dn_load(db, sb, q2b);
       if (q3 >= NEB) break;
       compute(dc, sc_, q3);
       q3 = grab_b();
@@ -802,13 +892,14 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   __syncthreads();
+  const bool err = __hip_atomic_load(&s_err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
   if (oB < NOct) {
     for (int idx = tid; idx < T * kOct; idx += kNT) {
       const int t = idx / kOct, rr = idx % kOct;
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) acc = fmaf(s_topw[t * k + j], s_y[(size_t)(t * k + j) * kOct + rr], acc);
       if (a.has_shared) acc = fmaf(s_gamma[t], s_ys[t * kOct + rr], acc);
-      a.out[(size_t)t * H + kOct * oB + rr] = to_bf16(acc);
+      a.out[(size_t)t * H + kOct * oB + rr] = err ? (uint16_t)0x7FC0u : to_bf16(acc);
     }
   }
   // the routing and the padded alignment for the caller, spread over the blocks: any
@@ -852,15 +943,16 @@ size_t route_bytes(int T, int k, int E) {
 }
 }  // namespace
 
-// LDS of one block: the routing region, then the data region -- the tokens in phases 0
-// and A, then the expert outputs y of the block's rows and the h rows in phase B.
+// LDS of one block: the routing region, the tokens, the expert outputs y of the block's rows
+// and the outbox of its h values, and the h rows (all live together: the stager fills h while
+// the tokens are still in use).
 size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared) {
   const size_t rb = route_bytes(T, k, E);
   const size_t n = (size_t)T * k;
   const size_t xb = al16((size_t)T * (H / 8 + 2) * 16);
-  const size_t yb = al16((n + T) * kOct * 4);
-  const size_t hb = (n + (has_shared ? (size_t)T : 0)) * ((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16;
-  return rb + std::max(xb, yb + hb);
+  const size_t yb = al16((n + T) * (kOct + 1) * 4);  // y of the block's rows, then the h outbox
+  const size_t hb = (n + T) * ((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16;
+  return rb + xb + yb + hb;
 }
 
 namespace {
@@ -929,7 +1021,8 @@ static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *n
     cus = d.cus;
     per_cu = d.per_cu;
   }
-  // one block per CU; the whole grid must be resident at once for the barriers
+  // one block per CU; the whole grid must be resident at once for the barrier and the
+  // readiness waits
   const int nb = std::min(cus, kMaxBlocks);
   if (per_cu < 1 || (long)per_cu * cus < nb) return hipErrorInvalidConfiguration;
   // one gate/up row pair and one output octet per block at most
@@ -941,12 +1034,6 @@ static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *n
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {
   const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared);
   if (lds > kFusedLdsMax) return hipErrorInvalidValue;
-  // phase B reads h and h_s through one buffer descriptor based at h
-  if (a.has_shared) {
-    const ptrdiff_t d = (const char *)a.h_s - (const char *)a.h;
-    if (d < (ptrdiff_t)a.T * a.k * a.I * 2 || d + (ptrdiff_t)a.T * a.I_s * 2 >= ((ptrdiff_t)1 << 31))
-      return hipErrorInvalidValue;
-  }
   a.lds_route = route_bytes(a.T, a.k, a.E);
   int nb = 0;
   hipError_t e;

@@ -87,11 +87,11 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
     int Iw;
     if (ent < nr) {
       bank = (const uint8_t *)a.w_gu + (size_t)e * 2 * a.I * G * 16;
-      sbank = (const uint8_t *)a.s_gu + (size_t)e * 2 * a.I * G;
+      sbank = a.x_gu + (size_t)e * 2 * a.I * G;
       Iw = a.I;
     } else {
       bank = (const uint8_t *)a.ws_gu;
-      sbank = (const uint8_t *)a.ss_gu;
+      sbank = a.xs_gu;
       Iw = a.I_s;
     }
     const int row = rg < 2 ? r0 + rg : Iw + r0 + (rg - 2);
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kDnNW * kWave) void gemv_down_kernel(GemvArgs a) {
     const int K = ent < nr ? a.I : a.I_s;
     const int G = K / VPG;
     const uint8_t *bank = ent < nr ? (const uint8_t *)a.w_d + (size_t)e * a.H * G * 16 : (const uint8_t *)a.ws_d;
-    const uint8_t *sbank = ent < nr ? (const uint8_t *)a.s_d + (size_t)e * a.H * G : (const uint8_t *)a.ss_d;
+    const uint8_t *sbank = ent < nr ? a.x_d + (size_t)e * a.H * G : a.xs_d;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int row = o0 + 4 * s + rg;

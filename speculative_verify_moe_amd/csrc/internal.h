@@ -28,10 +28,22 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 // Slots per block of the multi-block alignment.
 constexpr int kAlignChunk = 256;
-// Blocks of the fused decode kernel at most (one per CU) and its barrier words (arrival
-// flags, release word, timeout count).
+// Blocks of the fused decode kernel at most (one per CU).
 constexpr int kMaxBlocks = 1024;
-constexpr int kBarrierWords = kMaxBlocks + 64;
+// The fused kernel's synchronisation words, at offset 0 of every layer workspace (so no other
+// buffer of any plan aliases them, whichever calls share the workspace), 32-bit words:
+//   [0, kMaxBlocks)         arrival flag of each block at the grid barrier (the call's token)
+//   [kBarRelease]           release word of the grid barrier: the last token, with bit 31 set
+//                           when a wait of that barrier gave up
+//   [kBarStatus]            count of waits that gave up (0 in normal use) -- read by the caller
+//   [kBarReady]             gate/up entries every block has finished, published by block 0
+//   [kBarProgress, +NB)     gate/up entries block b has finished and stored (a prefix count)
+// Each group sits on its own 256-byte line.
+constexpr int kBarRelease = kMaxBlocks;
+constexpr int kBarStatus = kMaxBlocks + 64;
+constexpr int kBarReady = kMaxBlocks + 128;
+constexpr int kBarProgress = kMaxBlocks + 192;
+constexpr int kBarrierWords = kBarProgress + kMaxBlocks;
 
 struct AlignOut {
   int32_t *sorted;
@@ -84,6 +96,8 @@ struct GemvArgs {
   const float *s_gu;
   const void *w_d;
   const float *s_d;
+  const uint8_t *x_gu;  // MXFP4: E8M0 block-scale bytes [E][2I][H/32]
+  const uint8_t *x_d;   // MXFP4: [E][H][I/32]
   const int32_t *tl_n;
   const int32_t *tl_e;
   const int32_t *tl_start;
@@ -95,6 +109,8 @@ struct GemvArgs {
   const float *ss_gu;
   const void *ws_d;
   const float *ss_d;
+  const uint8_t *xs_gu;  // MXFP4: the shared expert's block-scale bytes
+  const uint8_t *xs_d;
   const float *gamma;
   // intermediates and output
   uint16_t *h;    // [T*k][I], row = slot
@@ -119,6 +135,7 @@ struct FusedArgs {
   const float *ss_gu;
   const void *ws_d;
   const float *ss_d;
+  const uint8_t *x_gu, *x_d, *xs_gu, *xs_d;  // MXFP4 block-scale bytes (routed, shared)
   float *logits;      // [T][E]
   float *gate_logit;  // [T]
   int32_t *ids;       // [T][k]   (block 0 writes)
@@ -128,7 +145,7 @@ struct FusedArgs {
   uint16_t *h;        // [T*k][I]
   uint16_t *h_s;      // [T][I_s]
   uint16_t *out;      // [T][H]
-  unsigned *bar;      // barrier words: kMaxBlocks arrival flags, release word, timeout count
+  unsigned *bar;      // synchronisation words (kBarrierWords, layout above)
   size_t lds_route;   // set by the launcher
 };
 bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype);

@@ -79,9 +79,10 @@ def test_align_validation(lib):
 
 def _fake_layer(lib, T_shared=True, wtype=0, E=256, k=8, H=2048, I=512):
     P = ctypes.c_void_p
-    sb = ctypes.c_void_p(4096) if wtype == 1 else None
-    routed = lib._Bank(wtype, E, H, I, P(4096), P(4096), sb, sb)
-    shared = lib._Bank(wtype, 1 if T_shared else 0, H, I, P(4096), P(4096), sb, sb)
+    sb = ctypes.c_void_p(4096) if wtype in (1, 2) else None  # fp8 row scales
+    mb = ctypes.c_void_p(4097) if wtype == 3 else None       # MXFP4 block-scale bytes (any alignment)
+    routed = lib._Bank(wtype, E, H, I, P(4096), P(4096), sb, sb, mb, mb)
+    shared = lib._Bank(wtype, 1 if T_shared else 0, H, I, P(4096), P(4096), sb, sb, mb, mb)
     return lib._Layer(H, E, k, 1, P(4096), None, routed, shared, P(4096) if T_shared else None)
 
 
@@ -107,6 +108,20 @@ def test_layer_validation(lib):
     assert f(P(4096), 4096, ctypes.byref(fp8), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_WORKSPACE
     fp8.routed.s_down = None
     assert f(P(4096), 8, ctypes.byref(fp8), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_INVALID_ARG
+    mx = _fake_layer(lib, wtype=3)
+    # MXFP4 scale bytes travel in their own fields, with no alignment asked of them
+    assert f(P(4096), 8, ctypes.byref(mx), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_WORKSPACE
+    assert f(P(4096), 4096, ctypes.byref(mx), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_UNSUPPORTED
+    mx.routed.mx_down = None
+    assert f(P(4096), 8, ctypes.byref(mx), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_INVALID_ARG
+    assert "mx_gate_up and mx_down" in lib.moe_last_error()
+    mx = _fake_layer(lib, wtype=3)
+    mx.routed.s_gate_up = ctypes.c_void_p(4098)  # fp8 row-scale fields are ignored for MXFP4
+    assert f(P(4096), 8, ctypes.byref(mx), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_WORKSPACE
+    fp8 = _fake_layer(lib, wtype=1)
+    fp8.routed.mx_gate_up = None  # and the MXFP4 fields for fp8
+    fp8.routed.s_gate_up = ctypes.c_void_p(4098)
+    assert f(P(4096), 8, ctypes.byref(fp8), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_MISALIGNED
     wt = _fake_layer(lib)
     wt.routed.wtype = 7
     assert f(P(4096), 8, ctypes.byref(wt), P(4096), None, None, None, None, 0, None) == lib.MOE_ERR_INVALID_ARG
@@ -127,6 +142,17 @@ def test_workspace_sizes_and_plans(lib):
     ew = _c(lib, "moe_experts_workspace_size")
     tl = -(-(1 + 256 + 257 + 64) * 4 // 256) * 256           # compact touched-expert list
     assert ew(8, 8, ctypes.byref(L.routed), 16) == 8 * 8 * 512 * 2 + tl
+
+
+def test_status_word_sits_in_the_synchronisation_words(lib):
+    """The status word lies inside the words every plan keeps at offset 0, below the smallest
+    workspace of any call."""
+    off = lib._lib.moe_workspace_status_offset()
+    assert off % 4 == 0 and 0 < off < 16384
+    L = _fake_layer(lib, E=16, k=2, H=256, I=128)
+    wsz = _c(lib, "moe_layer_workspace_size")
+    for T in (1, 8, 64, 65, 4096):
+        assert wsz(T, ctypes.byref(L)) >= off + 4
 
 
 def test_stage_events_hook_bounds(lib):
