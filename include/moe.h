@@ -199,6 +199,20 @@ size_t moe_layer_workspace_size(int32_t T, const moe_layer *L);
 moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                              int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_forward for callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: the same computation with no workspace
+ * argument.  Its scratch is a static 8 MiB array in device memory (one per device, held
+ * until the process ends), so it serves calls whose plan needs at most that much
+ * (moe_layer_workspace_size(T, L) <= 8 MiB: every decode/verify block of the Qwen-like
+ * shapes; a larger call returns MOE_ERR_WORKSPACE and names the size).  It calls no
+ * hipMalloc, hipFree or allocating library routine.  Every call on a device shares that
+ * device's scratch, which keeps the last call's contents: calls that overlap on one device
+ * (different streams, or different threads without ordering) race and must not be made.
+ * On the first call on a device its synchronisation words are cleared by a small kernel on
+ * `stream`.  Arguments, outputs and errors as moe_layer_forward. */
+moe_status moe_layer_forward_noalloc(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out,
+                                     float *logits_out, int32_t *ids_out, float *w_out, void *stream);
+
 /* Byte offset, inside every moe_layer_forward workspace, of a uint32 count of the fused
  * decode kernel's waits that gave up (0 in normal use; see moe_layer_forward).  The count
  * only grows; zeroing the workspace clears it.  Pure host function. */

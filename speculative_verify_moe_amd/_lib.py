@@ -47,6 +47,7 @@ EXPORTS = {
                                            _P, _P, _SZ, _P]),
     "moe_layer_workspace_size": (_SZ, [_I32, ctypes.POINTER(_Layer)]),
     "moe_layer_forward": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_Layer), _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_Layer), _P, _P, _P, _P, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_status_offset": (_SZ, []),
     "moe_describe_plan": (ctypes.c_char_p, [_I32, ctypes.POINTER(_Layer)]),
@@ -310,3 +311,19 @@ def moe_layer_forward(x, layer, out=None, logits_out=None, ids_out=None, w_out=N
                                   _ptr(w_out), _ptr(ws), ws.numel(), _stream()))
     return out
 
+
+def moe_layer_forward_noalloc(x, layer, out=None, logits_out=None, ids_out=None, w_out=None):
+    """The whole layer with the library's static device scratch instead of a workspace (the C
+    entry point allocates nothing; only a missing ``out`` is allocated here, by torch)."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out")
+    for t, dt, name in ((logits_out, torch.float32, "logits_out"), (ids_out, torch.int32, "ids_out"),
+                        (w_out, torch.float32, "w_out")):
+        if t is not None:
+            _dev(t, dt, name)
+    _check(_lib.moe_layer_forward_noalloc(_ptr(x), T, ctypes.byref(layer.struct), _ptr(out), _ptr(logits_out),
+                                          _ptr(ids_out), _ptr(w_out), _stream()))
+    return out

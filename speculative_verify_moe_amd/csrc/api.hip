@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "internal.h"
@@ -253,6 +254,51 @@ void fill_gemv(GemvArgs &g, const uint16_t *x, int T, int H, int k, const moe_ba
   g.s_d = routed->s_down;
   g.x_gu = routed->mx_gate_up;
   g.x_d = routed->mx_down;
+}
+
+// ---------------------------------------------------------------- allocation-free entry point
+// The scratch moe_layer_forward_noalloc uses in place of a caller's workspace: a file-scope
+// device array; every device the library runs on holds its own copy until the process ends.
+// In host code its name stands for a host-side shadow, not a device address: the device
+// address of each device's copy comes from hipGetSymbolAddress (once per device, with that
+// device current), and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+// Clears the first n words of the scratch (the fused kernel's synchronisation words) with a
+// kernel, not a memset, so that the clear may also be captured into a HIP graph.
+__global__ void clear_words_kernel(unsigned *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address; on the device's first use, its synchronisation words
+// are cleared on the caller's stream (the array also starts zeroed when the code object loads).
+moe_status scratch_for_current_device(void **out, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress of the scratch failed: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(clear_words_kernel, dim3(4), dim3(256), 0, s, (unsigned *)p, kBarrierWords);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "clearing the scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -699,6 +745,24 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     return st;
   sg.end();
   return MOE_OK;
+}
+
+moe_status moe_layer_forward_noalloc(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out,
+                                     float *logits_out, int32_t *ids_out, float *w_out, void *stream) {
+  g_err[0] = 0;
+  moe_status st = validate_layer(T, L);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const size_t need = plan_layer(T, L).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "T = %d needs %zu bytes of scratch; the library's static scratch holds %zu (call "
+                "moe_layer_forward with a workspace of moe_layer_workspace_size bytes)",
+                T, need, kScratchBytes);
+  if ((st = check_device()) != MOE_OK) return st;
+  void *ws = nullptr;
+  if ((st = scratch_for_current_device(&ws, (hipStream_t)stream)) != MOE_OK) return st;
+  return moe_layer_forward(x, T, L, out, logits_out, ids_out, w_out, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"
