@@ -329,12 +329,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (g >= H / 4) xt[c] = make_uint2(0, 0);
     }
   }
-  // the shared expert's gate/up rows of this block's row pair, in every wavefront: whichever
-  // wavefront takes entry 0 first in phase A has them (the block's 8 loads share the CU's
-  // caches); the bytes stream during the head
+  // the shared expert's gate/up rows of this block's row pair, in wavefront 0, which takes
+  // entry 0 in phase A: the bytes stream during the head (the other wavefronts' loads are
+  // empty)
   const int pA = blockIdx.x;
   const bool shA = a.has_shared && 2 * pA < a.I_s;
-  gu_load(wa, xa, shA, true, 0, gu_voff(a.I_s, pA), gu_soff(a.I_s, pA));
+  gu_load(wa, xa, shA && wave == 0, true, 0, gu_voff(a.I_s, pA), gu_soff(a.I_s, pA));
 
   // tokens to LDS (for phase A and the router's later tokens), in rows of xg uint4 ending
   // in the zero pad; unguarded (clamped) loads, so they are in flight together
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (lane == 0) {
         s_start[nq] = n_slots;
         s_nt = nq;
-        s_qa = 0;
+        s_qa = a.has_shared ? 1 : 0;  // entry 0, the shared expert, belongs to wavefront 0
         s_qb = 0;
       }
     }
@@ -729,8 +729,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     // every load is issued (past the last entry they read nothing), so the compiler's wait
     // counts are the same on every path and no prefetch is waited for early; entry 0 (the
-    // shared expert) is the first grab of one wavefront, whose rows from phase 0 are in wa
-    int q = grab();
+    // shared expert) is wavefront 0's first, its rows from phase 0 already in wa
+    int q = (sh && wave == 0) ? 0 : grab();
     int q2 = grab();
     if (!(sh && q == 0)) load_a(wa, xa, q);
     load_a(wb, xb, q2);
