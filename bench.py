@@ -419,14 +419,27 @@ def main():
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model/stepping numbers (some
+    hypervisors shorten the model name) and the logical CPUs this process may run on."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if ":" not in ln:
+                    if fields:
+                        break  # the first processor's block is enough
+                    continue
+                key, val = ln.split(":", 1)
+                fields.setdefault(key.strip(), val.strip())
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping") if k in fields)
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 0
+    return f"{name} ({ids}; {usable} logical CPUs usable, {os.cpu_count()} online)"
 
 
 if __name__ == "__main__":

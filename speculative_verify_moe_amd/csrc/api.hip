@@ -520,7 +520,7 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
                         decode_wtype(L->routed.wtype))) {
     snprintf(g_plan, sizeof(g_plan),
              "path=decode-fused T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 moe_decode_fused "
-             "(router, top-k, alignment, gate/up, down, combine; one kernel, two grid barriers)",
+             "(router, top-k, alignment, gate/up, down, combine; one kernel, one grid barrier)",
              T, E, k, p.BM, (long long)p.cap, p.total);
     return g_plan;
   }

@@ -8,14 +8,15 @@
 //
 // One block per CU (8 wavefronts); the grid never exceeds what the device holds resident
 // at once.  Phases:
-//   0  router row n on block n % NB, tokens staged in LDS; every wavefront also loads the
+//   0  router row n on block n % NB, tokens staged in LDS; wavefront 0 also loads the
 //      shared expert's gate/up rows of its block's row pair (they do not depend on the
 //      routing, so they stream while the head of the kernel is latency-bound).
 //                                                                  -- grid barrier
 //   1  every block routes all T tokens itself from the logits (top-k per wavefront, token
 //      masks per expert, entry lists): no exchange, no second launch.
 //   A  wavefronts 0..6: gate/up row pair b (2b, 2b+1 and I+2b, I+2b+1) of the shared expert
-//      (entry 0, its rows already in registers) and of every touched expert; each entry's
+//      (entry 0, taken by wavefront 0, its rows already in registers) and of every touched
+//      expert; each entry's
 //      h values go to an LDS outbox.  Wavefront 7, the stager, stores the outbox to global
 //      memory entry by entry and publishes how many entries the block has finished; one
 //      wavefront of block 0 publishes the minimum over the blocks; the stagers copy the h
