@@ -11,6 +11,7 @@ T=8 verify block (a DFlash block-8 verify pass).
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -43,12 +44,14 @@ WORKLOADS = {
                             "activations (per-row scales), 4096-token prefill chunk"),
 }
 
-FUSED_STAGES = ["moe_decode_fused"]
-DECODE_STAGES = ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"]
-PREFILL_STAGES = ["router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma",
-                  "combine"]
-PREFILL_A8_STAGES = ["router_gemm_mfma", "topk", "align", "quant_tokens", "gemm_gate_up_mfma", "quant_h",
-                     "gemm_down_mfma", "combine"]
+def plan_stages(plan):
+    """The stage names of a plan string, in the order the library attaches stage events:
+    "... stages: 0 name ...; 1 name ...; ..."."""
+    body = plan.split("stages:", 1)[1]
+    names = re.findall(r"(?:^|;)\s*(\d+) ([a-z_0-9]+)", body)
+    assert [int(i) for i, _ in names] == list(range(len(names))), plan
+    return [n for _, n in names]
+
 
 
 def parse():
@@ -179,11 +182,11 @@ def main():
     setup_s = time.time() - t0
     plan = moe.moe_describe_plan(T, layers[0])
     fused = "decode-fused" in plan
-    if prefill:
-        stages = PREFILL_A8_STAGES if "quant_tokens" in plan else PREFILL_STAGES
-    else:
-        stages = FUSED_STAGES if fused else DECODE_STAGES
+    stages = plan_stages(plan)
     nst = len(stages)
+    # stages on the library's second stream (the shared expert at prefill) overlap the others:
+    # then a layer's kernel time is the span from the first stage's start to the last one's end
+    overlapped = "second stream" in plan
 
     # realised routing per replica (touched experts) for the algorithmic byte counts
     touched = []
@@ -301,8 +304,8 @@ def main():
             stage_ms[i, s] = events[i][2 * s].elapsed_time(events[i][2 * s + 1])
     # kernel time per layer: the stages' own durations; the span from the first stage's start to
     # the last one's end also holds the eager pass's launch gaps, which graph replays do not have
-    gpu_ms = stage_ms.sum(axis=1)
     span_ms = np.array([events[i][0].elapsed_time(events[i][2 * nst - 1]) for i in range(K)])
+    gpu_ms = span_ms if overlapped else stage_ms.sum(axis=1)
     nt_steps = np.array([touched[i % L_rep] for i in range(K)])
 
     ms_per_step = elapsed * 1e3 / K
@@ -326,8 +329,9 @@ def main():
                     "kernel": dom_name, "avg_us": round(float(dom_ms.mean()) * 1e3, 2),
                     "alg_bytes_per_launch": int(alg_bytes.mean())}
     else:
-        # gate/up GEMM flops: every routed slot and every token through the shared expert
-        fl = 2 * T * k * 2 * H * I + 2 * T * 2 * H * I_s
+        # gate/up GEMM flops: every routed slot, and every token through the shared expert when
+        # the same launch carries it (not when the shared expert has stages of its own)
+        fl = 2 * T * k * 2 * H * I + (0 if "shared_gate_up_mfma" in stages else 2 * T * 2 * H * I_s)
         achieved = fl / (dom_ms.mean() * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
                     "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4),

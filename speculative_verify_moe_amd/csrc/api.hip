@@ -301,6 +301,49 @@ moe_status scratch_for_current_device(void **out, hipStream_t s) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- the shared expert's stream
+// At prefill the shared expert depends on the tokens only, so its two GEMMs run on a stream of
+// their own while the router, the top-k and the alignment run on the caller's (veloGB10
+// README, "Kernel work": shared-expert work overlapped with the MoE step).  One stream and two
+// events per device, made on first use; a call holds the device's lock from the fork to the
+// join so that concurrent calls from several host threads keep their own dependencies.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+
+// The device's side stream, locked into `lock`, or null (then the shared expert runs in order
+// on the caller's stream).  Nothing is created while the caller's stream is being captured
+// into a graph: creating a stream there could invalidate the capture.
+SideStream *side_stream(hipStream_t caller, std::unique_lock<std::mutex> &lock) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream &ss = g_side[dev];
+  lock = std::unique_lock<std::mutex>(ss.mu);
+  if (ss.s == nullptr) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t st = nullptr;
+    hipEvent_t ef = nullptr, ej = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ef, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ej, hipEventDisableTiming) != hipSuccess) {
+      if (ef != nullptr) (void)hipEventDestroy(ef);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    ss.s = st;
+    ss.fork = ef;
+    ss.join = ej;
+  }
+  return &ss;
+}
+
+moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
+                         int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream, bool allow_side);
+
 }  // namespace
 
 // ======================================================================== exported
@@ -535,6 +578,13 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
              "1 topk; 2 align (align_hist, align_colscan, align_offsets, align_scatter); 3 quant_tokens; "
              "4 gemm_gate_up_mfma (fp8 x fp8); 5 quant_h; 6 gemm_down_mfma (fp8 x fp8); 7 combine",
              T, E, k, p.BM, (long long)p.cap, p.total);
+  } else if (shared) {
+    snprintf(g_plan, sizeof(g_plan),
+             "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 shared_gate_up_mfma "
+             "(second stream, beside stages 2-6); 1 shared_down_mfma (second stream); 2 router_gemm_mfma; "
+             "3 topk; 4 align (align_hist, align_colscan, align_offsets, align_scatter); 5 gemm_gate_up_mfma "
+             "(routed); 6 gemm_down_mfma (routed); 7 combine",
+             T, E, k, p.BM, (long long)p.cap, p.total);
   } else {
     snprintf(g_plan, sizeof(g_plan),
              "path=prefill T=%d E=%d k=%d BM=%d cap=%lld workspace=%zu stages: 0 router_gemm_mfma; "
@@ -547,6 +597,15 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L) {
 
 moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                              int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream) {
+  return layer_forward(x, T, L, out, logits_out, ids_out, w_out, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
+                         int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream, bool allow_side) {
   g_err[0] = 0;
   moe_status st = validate_layer(T, L);
   if (st != MOE_OK) return st;
@@ -669,21 +728,6 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   }
 
   // prefill chunk
-  sg.begin();
-  if ((st = launched(launch_router_gemm(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
-                                        logits, gate, s),
-                     "router_gemm")) != MOE_OK)
-    return st;
-  sg.end();
-  sg.begin();
-  if ((st = launched(launch_topk(logits, T, E, k, L->renormalize != 0, ids, w, shared ? gate : nullptr,
-                                 shared ? gamma : nullptr, s), "topk")) != MOE_OK)
-    return st;
-  sg.end();
-  sg.begin();
-  if ((st = launched(launch_align_large(ids, (int)n, E, p.BM, p.cap, al, (int32_t *)(base + p.off_hist), s),
-                     "align")) != MOE_OK)
-    return st;
   GemmArgs a{};
   a.x = x;
   a.T = T;
@@ -721,6 +765,55 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
     a.hs8 = shared ? (uint8_t *)(base + p.off_hs8) : nullptr;
     a.shs = shared ? (float *)(base + p.off_shs) : nullptr;
   }
+  // the shared expert's gate/up and down as stages of their own, first, on the side stream
+  // from the fork (the tokens are ready) to the join before the combine -- or in order on the
+  // caller's stream when there is no side stream.  Whole 192-token passes keep the shared
+  // expert to about a third of the CUs, so the routing beside it keeps the rest (64-token
+  // passes, which spread it over every CU, and its down projection moved after the routed one
+  // both measured slower).  fp8 activations keep the one-launch order (their shared rows are
+  // quantised with the routed ones).
+  const bool split_shared = shared && !act8;
+  std::unique_lock<std::mutex> side_lock;
+  SideStream *side = split_shared && allow_side ? side_stream(s, side_lock) : nullptr;
+  if (split_shared) {
+    hipStream_t ss = s;
+    if (side != nullptr) {
+      hipError_t e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+      if (e != hipSuccess)
+        return fail(MOE_ERR_DEVICE, "forking the shared expert's stream failed: %s", hipGetErrorString(e));
+      ss = side->s;
+    }
+    GemmArgs as = a;
+    as.seg_mode = SEG_SHARED;
+    sg.begin();
+    if ((st = launched(launch_gemm_gate_up(as, ss), "shared gemm_gate_up")) != MOE_OK) return st;
+    sg.end();
+    sg.begin();
+    if ((st = launched(launch_gemm_down(as, ss), "shared gemm_down")) != MOE_OK) return st;
+    sg.end();
+    if (side != nullptr) {
+      const hipError_t e = hipEventRecord(side->join, side->s);
+      if (e != hipSuccess)
+        return fail(MOE_ERR_DEVICE, "recording the shared expert's join failed: %s", hipGetErrorString(e));
+    }
+    a.seg_mode = SEG_ROUTED;
+  }
+  sg.begin();
+  if ((st = launched(launch_router_gemm(x, T, H, L->router_w, L->router_b, E, shared ? L->shared_gate_w : nullptr,
+                                        logits, gate, s),
+                     "router_gemm")) != MOE_OK)
+    return st;
+  sg.end();
+  sg.begin();
+  if ((st = launched(launch_topk(logits, T, E, k, L->renormalize != 0, ids, w, shared ? gate : nullptr,
+                                 shared ? gamma : nullptr, s), "topk")) != MOE_OK)
+    return st;
+  sg.end();
+  sg.begin();
+  if ((st = launched(launch_align_large(ids, (int)n, E, p.BM, p.cap, al, (int32_t *)(base + p.off_hist), s),
+                     "align")) != MOE_OK)
+    return st;
   sg.end();
   if (act8) {
     sg.begin();
@@ -739,6 +832,10 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   sg.begin();
   if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
   sg.end();
+  if (side != nullptr) {
+    const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "joining the shared expert's stream failed: %s", hipGetErrorString(e));
+  }
   sg.begin();
   if ((st = launched(launch_combine(a.y, shared ? a.y_s : nullptr, w, shared ? gamma : nullptr, T, H, k, out, s),
                      "combine")) != MOE_OK)
@@ -746,6 +843,10 @@ moe_status moe_layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, u
   sg.end();
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 moe_status moe_layer_forward_noalloc(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out,
                                      float *logits_out, int32_t *ids_out, float *w_out, void *stream) {
@@ -762,7 +863,8 @@ moe_status moe_layer_forward_noalloc(const uint16_t *x, int32_t T, const moe_lay
   if ((st = check_device()) != MOE_OK) return st;
   void *ws = nullptr;
   if ((st = scratch_for_current_device(&ws, (hipStream_t)stream)) != MOE_OK) return st;
-  return moe_layer_forward(x, T, L, out, logits_out, ids_out, w_out, ws, kScratchBytes, stream);
+  // no side stream here: its first use would create a stream and events
+  return layer_forward(x, T, L, out, logits_out, ids_out, w_out, ws, kScratchBytes, stream, false);
 }
 
 }  // extern "C"

@@ -476,9 +476,11 @@ hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.H % TKE != 0 || a.I % TKE != 0 || (a.has_shared && a.I_s % TKE != 0)) return hipErrorInvalidValue;
   const int NCH = MODE == MODE_GATE_UP ? (imax + EG_NB / 2 - 1) / (EG_NB / 2) : (a.H + EG_NB - 1) / EG_NB;
-  const int NSEG_S = a.has_shared ? (a.T + EG_MR - 1) / EG_MR : 0;
-  return launch_k(kern, dim3(grid_for((a.E + NSEG_S) * NCH)), dim3(EG_NT), lds, s, a, NCH,
-                  a.E, NSEG_S);
+  const int NSEG_R = a.seg_mode == SEG_SHARED ? 0 : a.E;
+  const int NSEG_S = a.has_shared && a.seg_mode != SEG_ROUTED ? (a.T + EG_MR - 1) / EG_MR : 0;
+  if (NSEG_R + NSEG_S == 0) return hipSuccess;
+  return launch_k(kern, dim3(grid_for((NSEG_R + NSEG_S) * NCH)), dim3(EG_NT), lds, s, a, NCH,
+                  NSEG_R, NSEG_S);
 }
 }  // namespace
 

@@ -152,7 +152,11 @@ bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype);
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len);
 
 // ---------------------------------------------------------------- gemm.hip
+// Which segments an expert-GEMM launch covers: the routed experts' and the shared expert's
+// (one launch), or one kind only (the shared expert then runs on a stream of its own).
+constexpr int SEG_ALL = 0, SEG_ROUTED = 1, SEG_SHARED = 2;
 struct GemmArgs {
+  int seg_mode;  // SEG_ALL, SEG_ROUTED or SEG_SHARED
   const uint16_t *x;
   int T, H, k, E, I, BM;
   int64_t cap;

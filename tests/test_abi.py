@@ -139,6 +139,21 @@ def test_workspace_sizes_and_plans(lib):
     assert b"path=prefill" in plan(4096, ctypes.byref(L))
     assert b"path=decode" in plan(64, ctypes.byref(L))
     assert b"path=prefill" in plan(65, ctypes.byref(L))
+    # prefill with a shared expert: its two GEMMs are stages 0 and 1, on the second stream;
+    # without one, or with fp8 activations, the routed and shared segments share one launch
+    import bench
+    p = plan(4096, ctypes.byref(L)).decode()
+    assert bench.plan_stages(p) == ["shared_gate_up_mfma", "shared_down_mfma", "router_gemm_mfma", "topk", "align",
+                                    "gemm_gate_up_mfma", "gemm_down_mfma", "combine"]
+    assert "second stream" in p
+    nos = _fake_layer(lib, T_shared=False)
+    p = plan(4096, ctypes.byref(nos)).decode()
+    assert bench.plan_stages(p) == ["router_gemm_mfma", "topk", "align", "gemm_gate_up_mfma", "gemm_down_mfma", "combine"]
+    a8 = _fake_layer(lib, wtype=2)
+    p = plan(4096, ctypes.byref(a8)).decode()
+    assert bench.plan_stages(p)[0] == "router_gemm_mfma" and "second stream" not in p
+    assert bench.plan_stages(plan(8, ctypes.byref(L)).decode()) in (
+        ["moe_decode_fused"], ["router_rows", "topk_align_small", "gemv_gate_up", "gemv_down_combine"])
     ew = _c(lib, "moe_experts_workspace_size")
     tl = -(-(1 + 256 + 257 + 64) * 4 // 256) * 256           # compact touched-expert list
     assert ew(8, 8, ctypes.byref(L.routed), 16) == 8 * 8 * 512 * 2 + tl
