@@ -81,7 +81,9 @@ __device__ __forceinline__ void wait_vm() {
 // own fp32 scale.  A stage is 128 codes of K: 128 bytes per row for both operands, the bf16
 // layout byte for byte, and one 16x16x128 fp8 MFMA per tile and stage; the weight-row scale
 // and the activation-row scale multiply the finished sums.
-template <int MODE, int KIND>
+// SHONLY (1: launches of the shared expert's segments alone) changes no code; it gives those
+// launches a kernel name of their own, so that profiles tell them from the routed ones.
+template <int MODE, int KIND, int SHONLY>
 __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH, int NSEG_R, int NSEG_S) {
   extern __shared__ __attribute__((aligned(16))) uint8_t eg_lds[];
   __shared__ float s_rsc[KIND == KIND_A8 ? EG_MR : 1];  // KIND_A8: activation scale of each row
@@ -448,9 +450,9 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
 }
 
 namespace {
-template <int MODE, int KIND>
+template <int MODE, int KIND, int SHONLY>
 hipError_t launch_expert_gemm_t(const GemmArgs &a, hipStream_t s) {
-  auto kern = expert_gemm_kernel<MODE, KIND>;
+  auto kern = expert_gemm_kernel<MODE, KIND, SHONLY>;
   constexpr size_t lds = KIND == KIND_FP8W ? EG_LDS_FP8 : EG_LDS;
   constexpr size_t ESZ = KIND == KIND_BF16 ? 2 : 1;
   constexpr int TKE = KIND == KIND_A8 ? 128 : EG_TK;
@@ -489,13 +491,16 @@ hipError_t launch_expert_gemm(const GemmArgs &a, hipStream_t s) {
   if (a.wtype == 1 || a.wtype == 2) {
     if (a.s_gu == nullptr || a.s_d == nullptr || (a.has_shared && (a.ss_gu == nullptr || a.ss_d == nullptr)))
       return hipErrorInvalidValue;
-    if (a.wtype == 1) return launch_expert_gemm_t<MODE, KIND_FP8W>(a, s);
+    if (a.wtype == 1)
+      return a.seg_mode == SEG_SHARED ? launch_expert_gemm_t<MODE, KIND_FP8W, 1>(a, s)
+                                      : launch_expert_gemm_t<MODE, KIND_FP8W, 0>(a, s);
     if (a.sx == nullptr || (MODE == MODE_GATE_UP ? a.x8 == nullptr : (a.h8 == nullptr || a.sh == nullptr)) ||
         (MODE == MODE_DOWN && a.has_shared && (a.hs8 == nullptr || a.shs == nullptr)))
       return hipErrorInvalidValue;
-    return launch_expert_gemm_t<MODE, KIND_A8>(a, s);
+    return launch_expert_gemm_t<MODE, KIND_A8, 0>(a, s);
   }
-  return launch_expert_gemm_t<MODE, KIND_BF16>(a, s);
+  return a.seg_mode == SEG_SHARED ? launch_expert_gemm_t<MODE, KIND_BF16, 1>(a, s)
+                                  : launch_expert_gemm_t<MODE, KIND_BF16, 0>(a, s);
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s) { return launch_expert_gemm<MODE_GATE_UP>(a, s); }

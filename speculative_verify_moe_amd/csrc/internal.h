@@ -83,7 +83,6 @@ hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t 
 size_t align_hist_ints(int64_t n, int E);
 hipError_t launch_align_large(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, int32_t *hist,
                               hipStream_t s);
-int align_large_kernels();
 
 // ---------------------------------------------------------------- gemv.hip
 struct GemvArgs {

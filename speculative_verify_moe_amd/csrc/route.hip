@@ -314,7 +314,6 @@ size_t align_hist_ints(int64_t n, int E) {
   const int64_t chunks = (n + kAlignChunk - 1) / kAlignChunk;
   return (size_t)(chunks * E);
 }
-int align_large_kernels() { return 4; }
 
 __global__ __launch_bounds__(kAlignChunk) void align_hist_kernel(const int32_t *__restrict__ ids, int n, int E,
                                                                  int32_t *__restrict__ hist) {

@@ -88,16 +88,23 @@ ALIGN_CASES = [
     ("prefill_flash", 4096, 10, 512, 64, 2),
     ("large_ragged", 1337, 3, 200, 16, 1),
     ("E1", 300, 1, 1, 64, 0),
+    # the multi-block alignment just past the one-block size, 1024 experts, and every slot in
+    # one of 16 hot experts (long runs of equal ids across the chunks)
+    ("chunks_1025", 205, 5, 37, 16, 0),
+    ("chunks_16385", 3277, 5, 300, 32, 1),
+    ("chunks_E1024", 4096, 8, 1024, 64, 0),
+    ("chunks_hot", 4096, 8, 256, 64, 0, 16),
 ]
 
 
 @pytest.mark.parametrize("case", ALIGN_CASES, ids=lambda c: c[0])
 def test_align_bit_exact(case):
     from speculative_verify_moe_amd import moe_align, moe_align_capacity
-    name, T, k, E, BM, extra = case
+    name, T, k, E, BM, extra = case[:6]
+    hot = case[6] if len(case) > 6 else E  # the experts the slots are drawn from
     _say(f"[align] {name} T={T} k={k} E={E} BM={BM}")
     rng = np.random.default_rng(T * 7 + E)
-    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids = np.stack([rng.permutation(hot)[:k] for _ in range(T)]).astype(np.int32)
     cap = moe_align_capacity(T, k, E, BM) + extra * BM
     got = moe_align(torch.from_numpy(ids).cuda(), E, BM, cap=cap)
     torch.cuda.synchronize()
