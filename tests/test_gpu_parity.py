@@ -441,6 +441,45 @@ def test_alternating_inputs_on_one_workspace():
 
 
 @pytest.mark.gpu
+def test_concurrent_prefill_calls_from_two_threads():
+    """Two host threads, each on its own stream and workspace, run prefill layers at the same time.
+    Both calls' shared experts go through the device's one second stream (a lock spans each
+    call's fork to join); every output equals the single-threaded result bitwise."""
+    import threading
+    from speculative_verify_moe_amd import moe_layer_forward, moe_layer_workspace_size
+    cfg = configs.CONFIGS["prefill"]
+    T = 200
+    L = G.host_layer(cfg)
+    D = G.device_layer(L)
+    xs = [G.to_dev_bf16(configs.make_tokens(cfg, T, replica=r)) for r in (1, 2)]
+    refs = [G.bf16_bits(moe_layer_forward(x, D)) for x in xs]
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                ws = torch.zeros((moe_layer_workspace_size(T, D),), dtype=torch.uint8, device="cuda")
+                outs = [moe_layer_forward(xs[i], D, ws=ws) for _ in range(8)]
+            s.synchronize()
+            results[i] = [G.bf16_bits(o) for o in outs]
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+    for i in range(2):
+        for j, o in enumerate(results[i]):
+            assert np.array_equal(o, refs[i]), f"thread {i} call {j}"
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("recipe,T", [("qwen36_a3b", 8), ("flash_next_fp8", 6), ("qwen36_a3b", 32), ("prefill", 200)])
 def test_graph_replays_equal_eager(recipe, T):
     """A layer call captured in a HIP graph: every replay (inputs changed in place between
