@@ -228,7 +228,7 @@ const char *moe_describe_plan(int32_t T, const moe_layer *L);
 /* Options of the calling thread (no environment variable is read).
  *   MOE_OPT_DECODE_FUSED: 1 (default) runs decode/verify blocks that fit the fused
  *   kernel (H <= 2048, I and I_s <= 512, tokens and intermediates within LDS) as one
- *   kernel -- router, top-k, alignment, experts and combine with two grid-wide barriers
+ *   kernel -- router, top-k, alignment, experts and combine with one grid-wide barrier
  *   (one block per CU, all resident); 0 runs the same steps as four kernels (router,
  *   top-k + alignment, gate/up, down + combine).  Both give bitwise the same routing and
  *   output.  Other shapes always take the four-kernel path. */
@@ -242,8 +242,20 @@ moe_status moe_set_option(int32_t key, int32_t value);
  * dispatches (hipExtLaunchKernel), events[2i] marking the start of its first kernel and
  * events[2i+1] the end of its last, so their elapsed time is the stage's kernel time.  A
  * stage is one kernel or a fixed group of kernels; moe_describe_plan names the stages in
- * launch order (fused decode: 1 stage, four-kernel decode: 4, prefill: 7). */
+ * launch order (fused decode: 1 stage; four-kernel decode: 4; prefill: 6, or 8 with a
+ * shared expert -- its two GEMMs first, on a second stream -- or with fp8 activations). */
 moe_status moe_set_stage_events(void *const *events, int32_t n_events);
+
+/* Measurement aid, no part of the layer: enqueues one plain streaming read of `bytes`
+ * bytes of device memory at buf (both multiples of 16), by `blocks` workgroups of 256
+ * threads, each thread keeping `depth` (4, 8 or 16) non-temporal 16-byte loads in flight;
+ * the blocks stride over the buffer in chunks of 256 * depth * 16 bytes.  sink (device,
+ * `blocks` uint32) receives one checksum word per block, which keeps every load.  Timed by
+ * the caller (events around the call), it gives the read rate the device attains -- the
+ * context for the HBM fractions of the layer kernels, which stay against the nominal
+ * peak.  The pages define no such call. */
+moe_status moe_measure_stream_read(const void *buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t *sink,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

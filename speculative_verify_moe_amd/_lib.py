@@ -53,6 +53,7 @@ EXPORTS = {
     "moe_describe_plan": (ctypes.c_char_p, [_I32, ctypes.POINTER(_Layer)]),
     "moe_set_stage_events": (ctypes.c_int, [ctypes.POINTER(_P), _I32]),
     "moe_set_option": (ctypes.c_int, [_I32, _I32]),
+    "moe_measure_stream_read": (ctypes.c_int, [_P, _SZ, _I32, _I32, _P, _P]),
 }
 for _name, (_res, _args) in EXPORTS.items():
     _f = getattr(_lib, _name)
@@ -237,6 +238,16 @@ def moe_set_stage_events(events):
         return
     arr, n = events if isinstance(events, tuple) else stage_event_handles(events)
     _check(_lib.moe_set_stage_events(arr, n))
+
+
+def moe_measure_stream_read(buf, blocks, depth, sink=None):
+    """One streaming read of the whole device tensor buf (a measurement aid, no part of the
+    layer) on the current stream; returns the sink tensor (one uint32 checksum per block)."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty((blocks,), dtype=torch.int32, device=buf.device)
+    _check(_lib.moe_measure_stream_read(_ptr(buf), nbytes, blocks, depth, _ptr(sink), _stream()))
+    return sink
 
 
 def moe_route_topk(logits, k, renormalize=True, topk_ids=None, topk_w=None):

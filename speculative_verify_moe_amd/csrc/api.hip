@@ -385,6 +385,19 @@ moe_status moe_set_stage_events(void *const *events, int32_t n_events) {
   return MOE_OK;
 }
 
+moe_status moe_measure_stream_read(const void *buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t *sink,
+                                   void *stream) {
+  g_err[0] = 0;
+  if (buf == nullptr || sink == nullptr) return fail(MOE_ERR_INVALID_ARG, "buf and sink are required");
+  if (bytes == 0 || bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "bytes = %zu: a positive multiple of 16", bytes);
+  if ((uintptr_t)buf % 16 != 0 || !aligned4(sink)) return fail(MOE_ERR_MISALIGNED, "buf must be 16-byte and sink 4-byte aligned");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "blocks = %d: 1 .. 2^20", blocks);
+  if (depth != 4 && depth != 8 && depth != 16) return fail(MOE_ERR_INVALID_ARG, "depth = %d: 4, 8 or 16", depth);
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  return launched(launch_stream_read(buf, bytes / 16, blocks, depth, sink, (hipStream_t)stream), "stream_read");
+}
+
 moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
                           int32_t *topk_ids, float *topk_w, void *stream) {
   g_err[0] = 0;

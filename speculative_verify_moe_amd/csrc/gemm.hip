@@ -879,7 +879,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 hipError_t launch_combine(const uint16_t *y, const uint16_t *y_s, const float *topk_w, const float *gamma, int T,
                           int H, int k, uint16_t *out, hipStream_t s) {
   return launch_k(combine_kernel, dim3(T), dim3(256), 0, s, y, y_s, topk_w, gamma, T, H, k, out);
-  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -441,12 +441,10 @@ static hipError_t launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, bool xl
     auto k = gemv_gate_up_kernel<VPG, CG, true>;
     hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
-  } else {
-    auto k = gemv_gate_up_kernel<VPG, CG, false>;
-    launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
+    return launch_k(k, grid, dim3(kGuNW * kWave), lds, s, a);
   }
-  return hipGetLastError();
+  // (launch_k returns the launch's own status: a later hipGetLastError would read it cleared)
+  return launch_k(gemv_gate_up_kernel<VPG, CG, false>, grid, dim3(kGuNW * kWave), lds, s, a);
 }
 
 hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len) {
@@ -486,14 +484,12 @@ static hipError_t launch_dn(const GemvArgs &a, hipStream_t s, dim3 grid, bool hl
     auto k = gemv_down_kernel<VPG, CG, true>;
     hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
-  } else {
-    auto k = gemv_down_kernel<VPG, CG, false>;
-    hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
-    if (e != hipSuccess) return e;
-    launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
+    return launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
   }
-  return hipGetLastError();
+  auto k = gemv_down_kernel<VPG, CG, false>;
+  hipError_t e = set_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
+  return launch_k(k, grid, dim3(kDnNW * kWave), lds, s, a);
 }
 
 hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len) {
@@ -521,6 +517,41 @@ hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t
     if (cg <= 2) return launch_dn<32, 2>(a, s, grid, hlds, lds);
     if (cg <= 4) return launch_dn<32, 4>(a, s, grid, hlds, lds);
   }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- streaming read (measurement)
+// A plain read of n16 16-byte words: each thread keeps D non-temporal loads in flight, the
+// blocks stride over the buffer in chunks of 256 * D words, and each block folds what it read
+// into one word of sink (so no load is dropped).  Nothing of the layer uses it: it measures
+// the read rate the device attains, as context for the roofline fractions of the layer kernels.
+template <int D>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t *__restrict__ p, size_t n16, uint32_t *sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256 * D;
+  for (size_t base = (size_t)blockIdx.x * 256 * D + threadIdx.x; base < n16; base += stride) {
+    u32x4_t v[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const size_t i = base + (size_t)u * 256;
+      v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  __shared__ uint32_t s_acc;
+  if (threadIdx.x == 0) s_acc = 0;
+  __syncthreads();
+  atomicXor(&s_acc, acc);
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s_acc;
+}
+
+hipError_t launch_stream_read(const void *buf, size_t n16, int blocks, int depth, uint32_t *sink, hipStream_t s) {
+  const u32x4_t *p = static_cast<const u32x4_t *>(buf);
+  if (depth == 4) return launch_k(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  if (depth == 8) return launch_k(stream_read_kernel<8>, dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  if (depth == 16) return launch_k(stream_read_kernel<16>, dim3(blocks), dim3(256), 0, s, p, n16, sink);
   return hipErrorInvalidValue;
 }
 

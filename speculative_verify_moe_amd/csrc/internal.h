@@ -118,6 +118,8 @@ struct GemvArgs {
 };
 hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
 hipError_t launch_gemv_down(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len);
+// a plain streaming read of n16 16-byte words (measurement aid; depth 4, 8 or 16)
+hipError_t launch_stream_read(const void *buf, size_t n16, int blocks, int depth, uint32_t *sink, hipStream_t s);
 
 // ---------------------------------------------------------------- fused.hip
 struct FusedArgs {

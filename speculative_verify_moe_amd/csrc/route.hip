@@ -119,12 +119,11 @@ hipError_t launch_router_rows(const uint16_t *x, int T, int H, const float *w_r,
   dim3 grid((NR + 3) / 4, (T + TP - 1) / TP), block(256);
   const size_t lds = (size_t)(T < TP ? T : TP) * H * 2;
   const int C = (H / 4 + kWave - 1) / kWave;
-  if (C <= 2) launch_k(router_rows_kernel<2>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else if (C <= 4) launch_k(router_rows_kernel<4>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else if (C <= 8) launch_k(router_rows_kernel<8>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else if (C <= 16) launch_k(router_rows_kernel<16>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  else launch_k(router_rows_kernel<32>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
-  return hipGetLastError();
+  if (C <= 2) return launch_k(router_rows_kernel<2>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 4) return launch_k(router_rows_kernel<4>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 8) return launch_k(router_rows_kernel<8>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else if (C <= 16) return launch_k(router_rows_kernel<16>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
+  else return launch_k(router_rows_kernel<32>, grid, block, lds, s, x, T, H, w_r, b_r, E, w_sg, logits, gate_logit);
 }
 
 // ============================================================ top-k (one wavefront per token): topk.h
@@ -143,12 +142,11 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
                        const float *gate_logit, float *gamma, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
   const int epl = (E + kWave - 1) / kWave;
-  if (epl <= 1) launch_k(topk_kernel<1>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
-  else if (epl <= 2) launch_k(topk_kernel<2>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
-  else if (epl <= 4) launch_k(topk_kernel<4>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
-  else if (epl <= 8) launch_k(topk_kernel<8>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
-  else launch_k(topk_kernel<16>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
-  return hipGetLastError();
+  if (epl <= 1) return launch_k(topk_kernel<1>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 2) return launch_k(topk_kernel<2>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 4) return launch_k(topk_kernel<4>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else if (epl <= 8) return launch_k(topk_kernel<8>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
+  else return launch_k(topk_kernel<16>, grid, block, 0, s, logits, T, E, k, renorm, ids, w, gate_logit, gamma);
 }
 
 // ============================================================ alignment, one block (n <= 1024, E <= 1024)
@@ -232,9 +230,8 @@ __global__ __launch_bounds__(1024) void align_small_kernel(const int32_t *__rest
 }
 
 hipError_t launch_align_small(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, hipStream_t s) {
-  launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, BM, (int)cap, al,
-           Touched{nullptr, nullptr, nullptr, nullptr});
-  return hipGetLastError();
+  return launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, BM, (int)cap, al,
+                  Touched{nullptr, nullptr, nullptr, nullptr});
 }
 
 // Decode head: top-k of all T tokens (16 wavefronts) then the alignment, one block.
@@ -262,18 +259,16 @@ hipError_t launch_topk_align_small(const float *logits, const float *gate_logit,
   if (T > 1024 / kWave) {
     hipError_t e = launch_topk(logits, T, E, k, renorm, ids, w, gate_logit, gamma, s);
     if (e != hipSuccess) return e;
-    launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, BM, (int)cap, al, tl);
-    return hipGetLastError();
+    return launch_k(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, T * k, E, BM, (int)cap, al, tl);
   }
   const int epl = (E + kWave - 1) / kWave;
   dim3 grid(1), block(1024);
   const int c = (int)cap;
-  if (epl <= 1) launch_k(topk_align_small_kernel<1>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
-  else if (epl <= 2) launch_k(topk_align_small_kernel<2>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
-  else if (epl <= 4) launch_k(topk_align_small_kernel<4>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
-  else if (epl <= 8) launch_k(topk_align_small_kernel<8>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
-  else launch_k(topk_align_small_kernel<16>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
-  return hipGetLastError();
+  if (epl <= 1) return launch_k(topk_align_small_kernel<1>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 2) return launch_k(topk_align_small_kernel<2>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 4) return launch_k(topk_align_small_kernel<4>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else if (epl <= 8) return launch_k(topk_align_small_kernel<8>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
+  else return launch_k(topk_align_small_kernel<16>, grid, block, 0, s, logits, gate_logit, T, E, k, renorm, BM, c, ids, w, gamma, al, tl);
 }
 
 // Compact touched-expert list from an existing alignment (counts, offsets, sorted ids).
@@ -301,8 +296,7 @@ __global__ __launch_bounds__(1024) void compact_touched_kernel(const int32_t *__
 
 hipError_t launch_compact_touched(const int32_t *counts, const int32_t *offsets, const int32_t *sorted, int E,
                                   Touched tl, hipStream_t s) {
-  launch_k(compact_touched_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, sorted, E, tl);
-  return hipGetLastError();
+  return launch_k(compact_touched_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, sorted, E, tl);
 }
 
 // ============================================================ alignment, many blocks (any n)
@@ -395,11 +389,13 @@ __global__ __launch_bounds__(kAlignChunk) void align_scatter_kernel(const int32_
 hipError_t launch_align_large(const int32_t *ids, int n, int E, int BM, int64_t cap, AlignOut al, int32_t *hist,
                               hipStream_t s) {
   const int chunks = (n + kAlignChunk - 1) / kAlignChunk;
-  launch_k(align_hist_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, hist);
-  launch_k(align_colscan_kernel, dim3(E), dim3(256), 0, s, hist, chunks, E, al.counts);
-  launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, s, al.counts, E, BM, (int)cap, al);
-  launch_k(align_scatter_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, (int)cap, hist, al);
-  return hipGetLastError();
+  // (each launch's own status: a later hipGetLastError would read it cleared)
+  hipError_t e = launch_k(align_hist_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, hist);
+  if (e == hipSuccess) e = launch_k(align_colscan_kernel, dim3(E), dim3(256), 0, s, hist, chunks, E, al.counts);
+  if (e == hipSuccess) e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, s, al.counts, E, BM, (int)cap, al);
+  if (e == hipSuccess)
+    e = launch_k(align_scatter_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, (int)cap, hist, al);
+  return e;
 }
 
 }  // namespace moe

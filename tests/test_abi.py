@@ -175,3 +175,17 @@ def test_stage_events_hook_bounds(lib):
     arr = (ctypes.c_void_p * 65)()
     assert f(arr, 65) == lib.MOE_ERR_INVALID_ARG
     assert f(None, 0) == lib.MOE_OK
+
+
+def test_stream_read_probe_rejects_bad_arguments(lib):
+    """The streaming-read measurement aid validates before it touches a device."""
+    f = _c(lib, "moe_measure_stream_read")
+    buf = ctypes.c_void_p(1 << 20)    # never dereferenced: every call below fails validation
+    sink = ctypes.c_void_p(1 << 21)
+    assert f(None, 1024, 256, 8, sink, None) == lib.MOE_ERR_INVALID_ARG
+    assert f(buf, 0, 256, 8, sink, None) == lib.MOE_ERR_INVALID_ARG
+    assert f(buf, 1000, 256, 8, sink, None) == lib.MOE_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p((1 << 20) + 8), 1024, 256, 8, sink, None) == lib.MOE_ERR_MISALIGNED
+    assert f(buf, 1024, 0, 8, sink, None) == lib.MOE_ERR_INVALID_ARG
+    assert f(buf, 1024, 256, 6, sink, None) == lib.MOE_ERR_INVALID_ARG
+    assert "depth" in lib.moe_last_error()
