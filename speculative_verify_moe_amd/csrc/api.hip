@@ -341,6 +341,20 @@ SideStream *side_stream(hipStream_t caller, std::unique_lock<std::mutex> &lock) 
   return &ss;
 }
 
+// Once the side stream has forked, every return -- also an early one on a failed launch --
+// leaves the caller's stream waiting for the side stream's work, so that no kernel of the call
+// still writes the workspace after the caller's stream has moved past it.
+struct SideJoin {
+  SideStream *side = nullptr;
+  hipStream_t caller = nullptr;
+  ~SideJoin() {
+    if (side != nullptr) {
+      (void)hipEventRecord(side->join, side->s);
+      (void)hipStreamWaitEvent(caller, side->join, 0);
+    }
+  }
+};
+
 moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint16_t *out, float *logits_out,
                          int32_t *ids_out, float *w_out, void *ws, size_t ws_bytes, void *stream, bool allow_side);
 
@@ -788,6 +802,7 @@ moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint1
   const bool split_shared = shared && !act8;
   std::unique_lock<std::mutex> side_lock;
   SideStream *side = split_shared && allow_side ? side_stream(s, side_lock) : nullptr;
+  SideJoin side_join;  // (declared after the lock: it runs before the lock is released)
   if (split_shared) {
     hipStream_t ss = s;
     if (side != nullptr) {
@@ -795,6 +810,8 @@ moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint1
       if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
       if (e != hipSuccess)
         return fail(MOE_ERR_DEVICE, "forking the shared expert's stream failed: %s", hipGetErrorString(e));
+      side_join.side = side;
+      side_join.caller = s;
       ss = side->s;
     }
     GemmArgs as = a;
@@ -846,6 +863,7 @@ moe_status layer_forward(const uint16_t *x, int32_t T, const moe_layer *L, uint1
   if ((st = launched(launch_gemm_down(a, s), "gemm_down")) != MOE_OK) return st;
   sg.end();
   if (side != nullptr) {
+    side_join.side = nullptr;  // joined here, with its status checked
     const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "joining the shared expert's stream failed: %s", hipGetErrorString(e));
   }
