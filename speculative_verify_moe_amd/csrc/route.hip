@@ -364,23 +364,45 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(const int32_t *__re
 __global__ __launch_bounds__(kAlignChunk) void align_scatter_kernel(const int32_t *__restrict__ ids, int n, int E,
                                                                     int cap, const int32_t *__restrict__ hist,
                                                                     AlignOut al) {
-  __shared__ int32_t s_ids[kAlignChunk];
-  const int base = blockIdx.x * kAlignChunk;
-  const int i = base + threadIdx.x;
-  s_ids[threadIdx.x] = i < n ? ids[i] : -1;
-  __syncthreads();
-  if (i < n) {
-    const int e = s_ids[threadIdx.x];
-    int r = 0;
-    for (int q = 0; q < (int)threadIdx.x; ++q) r += (s_ids[q] == e) ? 1 : 0;
-    al.sorted[al.offsets[e] + hist[(size_t)blockIdx.x * E + e] + r] = i;
+  constexpr int NW = kAlignChunk / kWave;
+  // per wavefront of the chunk, how many of its slots chose each expert
+  __shared__ int32_t s_whist[NW][kMaxExperts];
+  // the padded offsets and the counts, staged once: the sentinel fill searches them per
+  // position (a binary search over global memory would be a chain of dependent loads)
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  const int lane = lane_id(), w = wave_id();
+  const int i = blockIdx.x * kAlignChunk + threadIdx.x;
+  const int e = i < n ? ids[i] : -1;
+  for (int j = threadIdx.x; j < NW * E; j += kAlignChunk) s_whist[j / E][j % E] = 0;
+  for (int j = threadIdx.x; j <= E; j += kAlignChunk) {
+    s_off[j] = al.offsets[j];
+    if (j < E) s_cnt[j] = al.counts[j];
   }
-  const int total = al.num_padded[0];
+  __syncthreads();
+  // the slot's rank among the chunk's earlier slots of its expert (the chunk's slots in
+  // order): inside the wavefront, one ballot per distinct expert, led by its first lane
+  int r = 0;
+  uint64_t todo = __ballot(e >= 0);
+  while (todo != 0) {
+    const int leader = __builtin_ctzll(todo);
+    const int v = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(e == v);
+    if (e == v) r = (int)__popcll(m & ((1ull << lane) - 1ull));
+    if (lane == leader) s_whist[w][v] = (int)__popcll(m);
+    todo &= ~m;
+  }
+  __syncthreads();
+  if (e >= 0) {
+    for (int w2 = 0; w2 < w; ++w2) r += s_whist[w2][e];  // ... and in the earlier wavefronts
+    al.sorted[s_off[e] + hist[(size_t)blockIdx.x * E + e] + r] = i;
+  }
+  const int total = s_off[E];  // num_padded
   for (int p = i; p < cap; p += gridDim.x * kAlignChunk) {
     bool pad = true;
     if (p < total) {
-      const int e = segment_of(al.offsets, E, p);
-      pad = (p - al.offsets[e]) >= al.counts[e];
+      const int ex = segment_of(s_off, E, p);
+      pad = (p - s_off[ex]) >= s_cnt[ex];
     }
     if (pad) al.sorted[p] = n;
   }
