@@ -286,25 +286,60 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
       const uint8_t *pb = ldsB + (KIND == KIND_FP8W ? kt & 1 : kt % 3) * EG_BBUF;
       if (KIND == KIND_A8) {
         // lane (fr, fq) holds the 32 codes of K 32 fq .. 32 fq + 31 of its row (logical
-        // chunks 2 fq and 2 fq + 1), for the activation and the weight fragments alike
+        // chunks 2 fq and 2 fq + 1), for the activation and the weight fragments alike.  The
+        // fragment reads are inline asm: the compiler cannot tell them from the direct-to-LDS
+        // loads still in flight into the other buffers and would otherwise wait for every one
+        // of them (vmcnt 0) before the first read, draining the load queue every stage.  Each
+        // block of reads waits for its own results before it ends (an asm output counts as
+        // written when the block ends), and its outputs are early-clobber (no read may land in
+        // a register that a later read of the block takes its address from).
         const int c0 = ((2 * fq) ^ (fr & 7)) * 16, c1 = ((2 * fq + 1) ^ (fr & 7)) * 16;
-        auto frag = [&](const uint8_t *row) {
-          const uint4 lo = *reinterpret_cast<const uint4 *>(row + c0), hi = *reinterpret_cast<const uint4 *>(row + c1);
+        auto addr = [&](const uint8_t *row, int c) { return (uint32_t)(uintptr_t)(row + c); };
+        auto join = [](const u32x4_t &lo, const u32x4_t &hi) {
           return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         };
+        const uint8_t *ra[3], *rb[8];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) ra[j] = pa + ((wm + 4 * j) * 16 + fr) * 128;
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) rb[ni] = pb + (bfr[ni] + fr) * 128;
+        u32x4_t al[3], ah[3], bl[8], bh[8];
+        asm volatile(
+            "ds_read_b128 %0, %14\n\tds_read_b128 %1, %15\n\tds_read_b128 %2, %16\n\t"
+            "ds_read_b128 %3, %17\n\tds_read_b128 %4, %18\n\tds_read_b128 %5, %19\n\t"
+            "ds_read_b128 %6, %20\n\tds_read_b128 %7, %21\n\tds_read_b128 %8, %22\n\t"
+            "ds_read_b128 %9, %23\n\tds_read_b128 %10, %24\n\tds_read_b128 %11, %25\n\t"
+            "ds_read_b128 %12, %26\n\tds_read_b128 %13, %27\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(al[0]), "=&v"(ah[0]), "=&v"(al[1]), "=&v"(ah[1]), "=&v"(al[2]), "=&v"(ah[2]), "=&v"(bl[0]),
+              "=&v"(bh[0]), "=&v"(bl[1]), "=&v"(bh[1]), "=&v"(bl[2]), "=&v"(bh[2]), "=&v"(bl[3]), "=&v"(bh[3])
+            : "v"(addr(ra[0], c0)), "v"(addr(ra[0], c1)), "v"(addr(ra[1], c0)), "v"(addr(ra[1], c1)),
+              "v"(addr(ra[2], c0)), "v"(addr(ra[2], c1)), "v"(addr(rb[0], c0)), "v"(addr(rb[0], c1)),
+              "v"(addr(rb[1], c0)), "v"(addr(rb[1], c1)), "v"(addr(rb[2], c0)), "v"(addr(rb[2], c1)),
+              "v"(addr(rb[3], c0)), "v"(addr(rb[3], c1))
+            : "memory");
+        asm volatile(
+            "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+            "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(bl[4]), "=&v"(bh[4]), "=&v"(bl[5]), "=&v"(bh[5]), "=&v"(bl[6]), "=&v"(bh[6]), "=&v"(bl[7]),
+              "=&v"(bh[7])
+            : "v"(addr(rb[4], c0)), "v"(addr(rb[4], c1)), "v"(addr(rb[5], c0)), "v"(addr(rb[5], c1)),
+              "v"(addr(rb[6], c0)), "v"(addr(rb[6], c1)), "v"(addr(rb[7], c0)), "v"(addr(rb[7], c1))
+            : "memory");
         i32x8_t aq[3];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) aq[j] = frag(pa + ((wm + 4 * j) * 16 + fr) * 128);
+        for (int j = 0; j < 3; ++j) aq[j] = join(al[j], ah[j]);
         // operand formats 0 (e4m3) for both; block scales 127 (2^0): plain products
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-          const i32x8_t bq = frag(pb + (bfr[ni] + fr) * 128);
+        auto mfma_ni = [&](int ni) {
+          const i32x8_t bq = join(bl[ni], bh[ni]);
           acc[0][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[0], bq, acc[0][ni], 0, 0, 0, 127, 0, 127);
           if (mv1)
             acc[1][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[1], bq, acc[1][ni], 0, 0, 0, 127, 0, 127);
           if (mv2)
             acc[2][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2], bq, acc[2][ni], 0, 0, 0, 127, 0, 127);
-        }
+        };
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) mfma_ni(ni);
         return;
       }
 #pragma unroll
@@ -341,7 +376,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
       // flight (vmcnt 0); the stage read here landed at the wait at the top of the stage
       uint4 vv[2];
       asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                   : "=v"(vv[0]), "=v"(vv[1])
+                   : "=&v"(vv[0]), "=&v"(vv[1])
                    : "v"((uint32_t)(uintptr_t)(q + (((2 * hf) ^ ((r >> 2) & 3)) * 16))),
                      "v"((uint32_t)(uintptr_t)(q + (((2 * hf + 1) ^ ((r >> 2) & 3)) * 16)))
                    : "memory");
