@@ -128,7 +128,12 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
   const int wm = wave >> 1, wn = wave & 1;
   // load mapping: a wavefront instruction fills 8 LDS rows (1 KiB); lane L writes row
   // L / 8, physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8)
-  const int lr = lane >> 3, lchunk = (lane & 7) ^ lr;
+  // KIND_A8: a lane's fragment is two logical chunks, 2q and 2q + 1; the logical chunk c sits
+  // at physical chunk tau(c) ^ (r & 7), tau(c) = (c >> 1) | ((c & 1) << 2), so that its two
+  // reads fall on the physical chunks q ^ (r & 7) and (q + 4) ^ (r & 7), the bf16 pattern,
+  // which the LDS serves without bank conflicts (2q ^ (r & 7) conflicted on half the cycles)
+  const int lr = lane >> 3, lphys = (lane & 7) ^ lr;
+  const int lchunk = KIND == KIND_A8 ? ((lphys & 3) << 1) | (lphys >> 2) : lphys;
 
   // ---- B: the expert's weight rows (one scalar descriptor)
   const uint8_t *bank;
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(EG_NT) void expert_gemm_kernel(GemmArgs a, int NCH,
         // block of reads waits for its own results before it ends (an asm output counts as
         // written when the block ends), and its outputs are early-clobber (no read may land in
         // a register that a later read of the block takes its address from).
-        const int c0 = ((2 * fq) ^ (fr & 7)) * 16, c1 = ((2 * fq + 1) ^ (fr & 7)) * 16;
+        const int c0 = (fq ^ (fr & 7)) * 16, c1 = ((fq + 4) ^ (fr & 7)) * 16;
         auto addr = [&](const uint8_t *row, int c) { return (uint32_t)(uintptr_t)(row + c); };
         auto join = [](const u32x4_t &lo, const u32x4_t &hi) {
           return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
