@@ -669,11 +669,11 @@ hipError_t launch_quant_h(const GemmArgs &a, hipStream_t s) {
 // consecutive (token tile, expert tile) pairs, so a token tile's expert tiles share that
 // XCD's L2 copy of its tokens.
 namespace {
-constexpr int RT_M = 128, RT_N = 32, RT_K = 64, RT_W = RT_K + 8;  // LDS row: 72 bf16 (144 bytes)
+constexpr int RT_M = 128, RT_N = 32, RT_K = 64, RT_W = RT_K;  // LDS row: 64 bf16 (128 bytes)
 constexpr int RT_NT = 512;
 constexpr int RT_NS = 4;                                          // register sets
 constexpr int RT_ABUF = RT_M * RT_W, RT_BBUF = 3 * RT_N * RT_W;  // elements per stage
-constexpr size_t RT_LDS = (size_t)2 * (RT_ABUF + RT_BBUF) * 2 + 2 * RT_K * 4;  // 65024 bytes
+constexpr size_t RT_LDS = (size_t)2 * (RT_ABUF + RT_BBUF) * 2 + 2 * RT_K * 4;  // 57856 bytes
 constexpr int RT_GT = 4;                                         // gate tokens per lane at most
 constexpr int RT_GR = RT_NT / 16;                                // gate token groups
 }  // namespace
@@ -708,8 +708,11 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;
 
-  // staging: token rows lrow, lrow + 64 (8 bf16 each); expert row wrow (4 fp32)
-  const int lrow = tid >> 3, lch = tid & 7;
+  // staging: token rows lrow, lrow + 64 (8 bf16 each); expert row wrow (4 fp32).  Each 8
+  // lanes stage one 128-byte row; within 32 lanes the rows run 0, 1, 3, 2, so any 16 lanes
+  // that the LDS serves together (consecutive eights, or eights 16 lanes apart) write one
+  // even and one odd row, i.e. both halves of the banks
+  const int lrow = (tid >> 3) ^ ((tid >> 4) & 1), lch = tid & 7;
   const int wrow = tid >> 4, wq = tid & 15;
   // rows past T or E load the last row (every load is issued, so the wait counts are
   // fixed) and are zeroed when staged
@@ -725,7 +728,7 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
   const float *wp = w_r + (size_t)min(n0 + wrow, E - 1) * H + 4 * wq;
   // gate logit: tokens g0 + gr + RT_GR s of this tile (s < RT_GT), lane part gq
   const bool gate = w_sg != nullptr;
-  const float *sgp = (gate ? w_sg : w_r) + 4 * (tid & 15);  // without a gate: loaded, unused
+  const float *sgp = (gate ? w_sg : w_r) + lane;  // one weight per lane; without a gate: loaded, unused
   const int tpb = (RT_M + NN - 1) / NN;
   const int g0 = nt * tpb, g1 = min(g0 + tpb, RT_M);
   const int gr = tid >> 4, gq = tid & 15;
@@ -737,7 +740,7 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
   struct Stage {
     uint4 xa[2];
     float4 wv;
-    float4 sg;
+    float sg;
   };
   Stage st[RT_NS];
   const int KT = H / RT_K;
@@ -746,44 +749,48 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
 #pragma unroll
     for (int i = 0; i < 2; ++i) S.xa[i] = *reinterpret_cast<const uint4 *>(xr[i] + k0);
     S.wv = *reinterpret_cast<const float4 *>(wp + k0);
-    S.sg = *reinterpret_cast<const float4 *>(sgp + k0);
+    S.sg = sgp[k0];
   };
   auto sstore = [&](const Stage &S, int buf) {
     uint16_t *A = sA + buf * RT_ABUF;
     uint16_t *B = sB + buf * RT_BBUF;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4 *>(&A[(lrow + 64 * i) * RT_W + 8 * lch]) = xok[i] ? S.xa[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&A[(lrow + 64 * i) * RT_W + 8 * (lch ^ (lrow & 7))]) =
+          xok[i] ? S.xa[i] : make_uint4(0, 0, 0, 0);
     uint2 h, m, l;
     const float4 w = wok ? S.wv : make_float4(0.f, 0.f, 0.f, 0.f);
     split3_pk(w.x, w.y, h.x, m.x, l.x);
     split3_pk(w.z, w.w, h.y, m.y, l.y);
-    const int off = wrow * RT_W + 4 * wq;
+    const int off = wrow * RT_W + 8 * ((wq >> 1) ^ (wrow & 7)) + 4 * (wq & 1);
     *reinterpret_cast<uint2 *>(&B[off]) = h;
     *reinterpret_cast<uint2 *>(&B[RT_N * RT_W + off]) = m;
     *reinterpret_cast<uint2 *>(&B[2 * RT_N * RT_W + off]) = l;
-    if (tid < RT_K / 4) *reinterpret_cast<float4 *>(&sG[buf * RT_K + 4 * tid]) = S.sg;
+    if (tid < RT_K) sG[buf * RT_K + tid] = S.sg;
   };
 
   f32x4_t acc[2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  // a fragment row r (every fragment starts at a multiple of 16 rows, so r & 7 == fr & 7)
+  // holds its K chunk q at chunk q ^ (r & 7)
+  const int fr = lane & 15, fq = lane >> 4;
   auto compute = [&](int buf) {
     const uint16_t *A = sA + buf * RT_ABUF;
     const uint16_t *B = sB + buf * RT_BBUF;
 #pragma unroll
     for (int ks = 0; ks < RT_K / 32; ++ks) {
+      const int fc = 8 * ((4 * ks + fq) ^ (fr & 7));
       bf16x8_t af[2], bf[3];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                  &A[(32 * wm + 16 * mi + fr) * RT_W + ks * 32 + fk]));
+        af[mi] = __builtin_bit_cast(bf16x8_t,
+                                    *reinterpret_cast<const uint4 *>(&A[(32 * wm + 16 * mi + fr) * RT_W + fc]));
 #pragma unroll
       for (int part = 0; part < 3; ++part)
         bf[part] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4 *>(&B[(part * RT_N + 16 * wn + fr) * RT_W + ks * 32 + fk]));
+            bf16x8_t, *reinterpret_cast<const uint4 *>(&B[(part * RT_N + 16 * wn + fr) * RT_W + fc]));
 #pragma unroll
       for (int part = 0; part < 3; ++part)
 #pragma unroll
@@ -796,7 +803,8 @@ __global__ __launch_bounds__(RT_NT) void router_mfma_kernel(const uint16_t *__re
       for (int s = 0; s < RT_GT; ++s) {
         const int j = g0 + gr + RT_GR * s;
         if (j < g1) {
-          const uint2 xv = *reinterpret_cast<const uint2 *>(&A[j * RT_W + 4 * gq]);
+          const uint2 xv =
+              *reinterpret_cast<const uint2 *>(&A[j * RT_W + 8 * ((gq >> 1) ^ (j & 7)) + 4 * (gq & 1)]);
           float g = gacc[s];
           g = fmaf(sg.x, bf16_lo(xv.x), g);
           g = fmaf(sg.y, bf16_hi(xv.x), g);
