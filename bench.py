@@ -33,6 +33,7 @@ WORKLOADS = {
     "qwen36_T1": ("qwen36_a3b", 1, "Qwen3.6-35B-A3B-like MoE layer, T=1 decode"),
     "qwen36_T32": ("qwen36_a3b", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32 (two 16-position blocks)"),
     "qwen36_zipf_T32": ("qwen36_a3b_zipf", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32, Zipf(1.1) expert load"),
+    "qwen36_T64": ("qwen36_a3b", 64, "Qwen3.6-35B-A3B-like MoE layer, T=64 (the largest verify block of the decode path)"),
     "flash_fp8_T1": ("flash_next_fp8", 1, "Qwen3.8-Flash-Next-like fp8 MoE layer, T=1 decode"),
     "qwen36_mxfp4_T8": ("qwen36_a3b_mxfp4", 8, "Qwen3.6-35B-A3B-like MoE layer with MXFP4 (4-bit) experts, "
                         "T=8 verify block"),

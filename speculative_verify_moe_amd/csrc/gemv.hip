@@ -115,27 +115,74 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
   // block y takes entries y*NW + w, then every NW*gridDim.y-th (more of a small weight
   // format in flight per row pair)
   const int NWS = kGuNW * gridDim.y;
-  // first entry's rows go out before the staging below
+  // token chunk z of gridDim.z: tokens [t_lo, t_hi), whose rows fit the LDS together.  A
+  // block computes the slots of its chunk's tokens only (each slot once, with the same
+  // arithmetic as without chunks) and walks only the entries that have such slots.
+  const bool chunked = gridDim.z > 1;
+  const int TCH = (a.T + gridDim.z - 1) / gridDim.z;
+  const int t_lo = blockIdx.z * TCH, t_hi = min(a.T, t_lo + TCH);
+  // first entry's rows go out before the staging below (with chunks, the entries are known
+  // only after it)
   int ent = blockIdx.y * kGuNW + wave;
-  if (ent < NE) load(wa, xa, ent, ent < nr ? a.tl_e[ent] : 0);
+  if (!chunked && ent < NE) load(wa, xa, ent, ent < nr ? a.tl_e[ent] : 0);
 
   int32_t *lbase = reinterpret_cast<int32_t *>(smem);
   const ListLds lst = stage_list(a, nr, lbase, NT);
+  // chunked: the entries with slots in the chunk, in order, and each one's slot range
+  int32_t *c_ent = lbase + 2 * nr + 1 + a.T * a.k, *c_q0 = c_ent + NE, *c_q1 = c_q0 + NE;
+  int32_t *c_tmp = c_q1 + NE;  // block scan scratch (kGuNW + 1 ints)
+  const size_t xoff = align16((size_t)(2 * nr + 1 + a.T * a.k + (chunked ? 3 * NE + kGuNW + 1 : 0)) * 4);
   const uint4 *xs;
+  int x_t0 = 0;  // first token row held in xs
   if (XLDS) {
-    uint4 *s_x = reinterpret_cast<uint4 *>(smem + align16((size_t)(2 * nr + 1 + a.T * a.k) * 4));
-    copy_to_lds(s_x, reinterpret_cast<const uint4 *>(a.x), a.T * G8, NT);
+    uint4 *s_x = reinterpret_cast<uint4 *>(smem + xoff);
+    copy_to_lds(s_x, reinterpret_cast<const uint4 *>(a.x) + (size_t)t_lo * G8, (t_hi - t_lo) * G8, NT);
     xs = s_x;
+    x_t0 = t_lo;
   } else {
     xs = reinterpret_cast<const uint4 *>(a.x);
   }
   __syncthreads();
+  int NCE = NE;  // entries this block walks
+  if (chunked) {
+    // an entry's slots are in slot order, i.e. in token order: its chunk slots are one run
+    int run = 0;
+    for (int i0 = 0; i0 < NE; i0 += NT) {
+      const int i = i0 + threadIdx.x;
+      int q0 = 0, q1 = 0;
+      if (i < nr) {
+        const int s1 = lst.start[i + 1];
+        q0 = lst.start[i];
+        while (q0 < s1 && lst.slots[q0] / a.k < t_lo) ++q0;
+        q1 = q0;
+        while (q1 < s1 && lst.slots[q1] / a.k < t_hi) ++q1;
+      } else if (i < NE) {  // the shared expert: every token of the chunk
+        q0 = t_lo;
+        q1 = t_hi;
+      }
+      const int keep = q1 > q0 ? 1 : 0;
+      int cnt;
+      const int idx = run + block_excl_scan<NT>(keep, c_tmp, &cnt);
+      if (keep) {
+        c_ent[idx] = i;
+        c_q0[idx] = q0;
+        c_q1[idx] = q1;
+      }
+      run += cnt;
+    }
+    __syncthreads();
+    NCE = run;
+    if (ent < NCE) load(wa, xa, ent, c_ent[ent] < nr ? lst.e[c_ent[ent]] : 0);
+  }
+  // the walked entry ci: its index in the list (nr: the shared expert) and slot range
+  auto entry_of = [&](int ci) { return chunked ? c_ent[ci] : ci; };
 
-  auto compute = [&](const uint4(&w)[CG], const uint32_t(&ws)[VPG == 32 ? CG : 1], int ent) {
+  auto compute = [&](const uint4(&w)[CG], const uint32_t(&ws)[VPG == 32 ? CG : 1], int ci) {
+    const int ent = entry_of(ci);
     const bool routed = ent < nr;
     const int e = routed ? lst.e[ent] : 0;
-    const int q0 = routed ? lst.start[ent] : 0;
-    const int q1 = routed ? lst.start[ent + 1] : a.T;
+    const int q0 = chunked ? c_q0[ci] : routed ? lst.start[ent] : 0;
+    const int q1 = chunked ? c_q1[ci] : routed ? lst.start[ent + 1] : a.T;
     float bsc[VPG == 32 ? CG : 1];  // MXFP4 block scales of the lane's groups
 #pragma unroll
     for (int c = 0; c < (VPG == 32 ? CG : 1); ++c) bsc[c] = VPG == 32 ? e8m0_scale(ws[c]) : 1.0f;
@@ -151,7 +198,7 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
     for (int q = q0; q < q1; ++q) {
       const int slot = routed ? lst.slots[q] : q;
       const int t = routed ? slot / a.k : q;
-      const uint4 *xr = xs + (size_t)t * G8;
+      const uint4 *xr = xs + (size_t)(t - x_t0) * G8;
       float acc = 0.0f;
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
@@ -185,13 +232,17 @@ __global__ __launch_bounds__(kGuNW * kWave) void gemv_gate_up_kernel(GemvArgs a)
     }
   };
 
-  while (ent < NE) {
+  auto load_ci = [&](uint4(&w)[CG], uint32_t(&xs_)[VPG == 32 ? CG : 1], int ci) {
+    const int en = entry_of(ci);
+    load(w, xs_, en, en < nr ? lst.e[en] : 0);
+  };
+  while (ent < NCE) {
     const int e2 = ent + NWS;
-    if (e2 < NE) load(wb, xb, e2, e2 < nr ? lst.e[e2] : 0);
+    if (e2 < NCE) load_ci(wb, xb, e2);
     compute(wa, xa, ent);
-    if (e2 >= NE) break;
+    if (e2 >= NCE) break;
     const int e3 = e2 + NWS;
-    if (e3 < NE) load(wa, xa, e3, e3 < nr ? lst.e[e3] : 0);
+    if (e3 < NCE) load_ci(wa, xa, e3);
     compute(wb, xb, e2);
     ent = e3;
   }
@@ -450,15 +501,25 @@ static hipError_t launch_gu(const GemvArgs &a, hipStream_t s, dim3 grid, bool xl
 hipError_t launch_gemv_gate_up(const GemvArgs &a, hipStream_t s, char *desc, size_t desc_len) {
   const int rows = a.has_shared && a.I_s > a.I ? a.I_s : a.I;
   dim3 grid(rows / 2);
-  const size_t lb = list_bytes(a);
-  const size_t xbytes = (size_t)a.T * a.H * 2;
+  // token chunks (grid.z): the fewest whose token rows fit the LDS beside the list and the
+  // chunk's entry list; past kMaxChunks, tokens come from global memory in one chunk
+  constexpr int kMaxChunks = 4;
+  const size_t lb1 = list_bytes(a);
+  const size_t lbc = (((size_t)(2 * a.E + 1 + a.T * a.k + 3 * (a.E + 1) + kGuNW + 1) * 4) + 15) & ~(size_t)15;
+  int nz = 1;
+  auto xb_of = [&](int n) { return (size_t)((a.T + n - 1) / n) * a.H * 2; };
+  while (nz < kMaxChunks && (nz == 1 ? lb1 : lbc) + xb_of(nz) > kLdsMax) ++nz;
+  const size_t lb = nz == 1 ? lb1 : lbc;
+  const size_t xbytes = xb_of(nz);
   const bool xlds = lb + xbytes <= kLdsMax;
-  const size_t lds = lb + (xlds ? xbytes : 0);
+  if (!xlds) nz = 1;
+  grid.z = nz;
+  const size_t lds = (nz == 1 ? lb1 : lbc) + (xlds ? xbytes : 0);
   const int vpg = a.wtype == 0 ? 8 : a.wtype == 3 ? 32 : 16;
   if (vpg == 32) grid.y = 2;                  // 4-bit rows are short: two blocks per row pair
   const int groups = a.H / vpg;               // 16-byte groups per weight row
   const int cg = (groups + 15) / 16;
-  if (desc) snprintf(desc, desc_len, "gemv_gate_up<vpg=%d,CG=%d,XLDS=%d> grid=%u block=%d lds=%zu", vpg, cg, (int)xlds, grid.x, kGuNW * kWave, lds);
+  if (desc) snprintf(desc, desc_len, "gemv_gate_up<vpg=%d,CG=%d,XLDS=%d> grid=%ux%ux%u block=%d lds=%zu", vpg, cg, (int)xlds, grid.x, grid.y, grid.z, kGuNW * kWave, lds);
   if (vpg == 8) {
     if (cg <= 4) return launch_gu<8, 4>(a, s, grid, xlds, lds);
     if (cg <= 8) return launch_gu<8, 8>(a, s, grid, xlds, lds);

@@ -146,6 +146,7 @@ LAYER_CASES = [
     ("qwen36_T32", "qwen36_a3b", 32),
     ("qwen36_zipf_T32", "qwen36_a3b_zipf", 32),
     ("qwen36_T64", "qwen36_a3b", 64),
+    ("qwen36_T40", "qwen36_a3b", 40),
     ("flash_fp8_T1", "flash_next_fp8", 1),
     ("flash_fp8_T6", "flash_next_fp8", 6),
     ("prefill_T4096", "prefill", 4096),
@@ -155,6 +156,8 @@ LAYER_CASES = [
     ("qwen36_mxfp4_T1", "qwen36_a3b_mxfp4", 1),
     ("qwen36_mxfp4_T8", "qwen36_a3b_mxfp4", 8),
     ("qwen36_mxfp4_T32", "qwen36_a3b_mxfp4", 32),
+    ("qwen36_mxfp4_T48", "qwen36_a3b_mxfp4", 48),
+    ("flash_fp8_T40", "flash_next_fp8", 40),
     ("prefill_fp8a8_T4096", "prefill_fp8a8", 4096),
     ("prefill_fp8a8_T200", "prefill_fp8a8", 200),
 ]
@@ -317,7 +320,8 @@ BATCH_INVARIANCE_CASES = [
     # recipe, T, four-kernel path forced
     ("qwen36_a3b", 8, False), ("qwen36_a3b_mxfp4", 8, False), ("flash_next_fp8", 6, False),
     ("qwen36_a3b", 16, False), ("qwen36_a3b", 32, False), ("qwen36_a3b", 64, False),
-    ("qwen36_a3b_zipf", 32, False), ("qwen36_a3b_mxfp4", 32, False),
+    ("qwen36_a3b_zipf", 32, False), ("qwen36_a3b_mxfp4", 32, False), ("qwen36_a3b_mxfp4", 48, False),
+    ("flash_next_fp8", 40, False),
     ("qwen36_a3b", 8, True), ("qwen36_a3b", 32, True), ("flash_next_fp8", 6, True), ("qwen36_a3b_mxfp4", 8, True),
 ]
 
