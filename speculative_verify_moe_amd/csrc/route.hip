@@ -21,14 +21,14 @@ namespace moe {
 
 // ============================================================ router (decode)
 // One wavefront per router row n (n < E: expert rows, n == E: the shared gate row) and
-// block row y per chunk of kRouterTB tokens, so that a 32-token block fills the chip
+// block row y per chunk of kRouterTB tokens, so that a 16-token block fills the chip
 // (blockIdx.y splits the tokens; a router row is read once per chunk, from L2 after the
 // first).  The wavefront's fp32 row is loaded into registers first (lane l owns float4
 // groups g = l + 64c), the block stages its tokens into LDS while those loads are in
 // flight (kStage loads per thread in flight together), then each token is one register
 // dot product and one DPP reduction.
 constexpr int kRouterLds = 64 * 1024;
-constexpr int kRouterTB = 8;
+constexpr int kRouterTB = 4;
 
 template <int C>
 __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t *__restrict__ x, int T, int H,
@@ -157,15 +157,35 @@ struct AlignLds {
   int32_t off[kMaxExperts + 1];
   int32_t cstart[kMaxExperts];
   int tmp[1024 / kWave + 1];
+  // per wavefront of slots: how many of them chose each expert (<= 64), 4 to a word
+  uint32_t whist[1024 / kWave][kMaxExperts / 4];
 };
 
 __device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, int BM, int cap, AlignLds &L,
                                             AlignOut al, Touched tl) {
-  constexpr int NT = 1024;
-  const int tid = threadIdx.x;
+  constexpr int NT = 1024, NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int EW = (E + 3) / 4;  // words of one wavefront's counts
+  // a slot's rank among the earlier slots of its expert: for a few slots, a count over the
+  // earlier slots; for many, inside its wavefront one ballot per distinct expert, led by its
+  // first lane (the leader stores the wavefront's count), plus the earlier wavefronts' counts
+  const bool by_ballot = n > 256;
   if (tid < E) L.cnt[tid] = 0;
+  if (by_ballot)
+    for (int j = tid; j < NW * EW; j += NT) L.whist[j / EW][j % EW] = 0u;
   __syncthreads();
   if (tid < n) atomicAdd(&L.cnt[s_ids[tid]], 1);
+  const int se = tid < n ? s_ids[tid] : -1;
+  int r = 0;
+  uint64_t todo = by_ballot ? __ballot(se >= 0) : 0ull;
+  while (todo != 0) {
+    const int leader = __builtin_ctzll(todo);
+    const int v = __builtin_amdgcn_readlane(se, leader);
+    const uint64_t m = __ballot(se == v);
+    if (se == v) r = (int)__popcll(m & ((1ull << lane) - 1ull));
+    if (lane == leader) L.whist[w][v >> 2] |= (uint32_t)__popcll(m) << (8 * (v & 3));
+    todo &= ~m;
+  }
   __syncthreads();
   const int c = tid < E ? L.cnt[tid] : 0;
   const int padded = (c + BM - 1) / BM * BM;
@@ -175,9 +195,10 @@ __device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, 
   if (tid == 0) L.off[E] = total;
   const bool want_tl = tl.n != nullptr;
   if (want_tl) {
-    int n_touched, n_slots;
-    const int idx = block_excl_scan<NT>(c > 0 ? 1 : 0, L.tmp, &n_touched);
-    const int cs = block_excl_scan<NT>(c, L.tmp, &n_slots);
+    // touched flags (high half) and counts (low half, <= n <= 1024) in one scan
+    int both;
+    const int sc = block_excl_scan<NT>((c > 0 ? 1 << 16 : 0) | c, L.tmp, &both);
+    const int idx = sc >> 16, cs = sc & 0xFFFF, n_touched = both >> 16, n_slots = both & 0xFFFF;
     if (tid < E) L.cstart[tid] = cs;
     if (c > 0) {
       tl.e[idx] = tid;
@@ -189,27 +210,25 @@ __device__ __forceinline__ void align_block(const int32_t *s_ids, int n, int E, 
     }
   }
   __syncthreads();
-  // stable scatter: a slot's place is its rank among the earlier slots of its expert
-  if (tid < n) {
-    const int e = s_ids[tid];
-    int r = 0;
-    for (int i = 0; i < tid; ++i) r += (s_ids[i] == e) ? 1 : 0;
-    al.sorted[L.off[e] + r] = tid;
-    if (want_tl) tl.slots[L.cstart[e] + r] = tid;
-  }
-  // padding and tail: every position that no slot takes holds the sentinel n
-  for (int p = tid; p < cap; p += NT) {
-    bool pad = true;
-    if (p < total) {
-      const int e = segment_of(L.off, E, p);
-      pad = (p - L.off[e]) >= L.cnt[e];
+  // the stable order by slot index
+  if (se >= 0) {
+    if (by_ballot) {
+      for (int w2 = 0; w2 < w; ++w2) r += (int)((L.whist[w2][se >> 2] >> (8 * (se & 3))) & 0xFFu);
+    } else {
+      for (int i = 0; i < tid; ++i) r += (s_ids[i] == se) ? 1 : 0;
     }
-    if (pad) al.sorted[p] = n;
+    al.sorted[L.off[se] + r] = tid;
+    if (want_tl) tl.slots[L.cstart[se] + r] = tid;
   }
-  for (int b = tid; b < cap / BM; b += NT) {
-    const int p = b * BM;
-    al.block_expert[b] = p < total ? segment_of(L.off, E, p) : -1;
+  // padding: every position that no slot takes holds the sentinel n (an expert's pad
+  // positions follow its slots; past num_padded the tail up to cap); block_expert: the
+  // expert of each BM-row block of the padded order, -1 past num_padded
+  if (tid < E) {
+    for (int p = L.off[tid] + c; p < L.off[tid + 1]; ++p) al.sorted[p] = n;
+    for (int b = L.off[tid] / BM; b < L.off[tid + 1] / BM; ++b) al.block_expert[b] = tid;
   }
+  for (int p = total + tid; p < cap; p += NT) al.sorted[p] = n;
+  for (int b = total / BM + tid; b < cap / BM; b += NT) al.block_expert[b] = -1;
   if (tid < E) {
     al.counts[tid] = L.cnt[tid];
     al.offsets[tid] = L.off[tid];
