@@ -109,7 +109,8 @@ __device__ __forceinline__ void note_timeout(unsigned *bar, int *s_err) {
 // VPG: weights per 16-byte column group -- 8 bf16, 16 fp8 codes, or 32 MXFP4 codes (which
 // are also one scale block).  CGU / CGD: column groups per lane and weight row in phase A /
 // phase B; CR: float4 router groups per lane.
-template <int VPG, int CGU, int CGD, int CR>
+// RING: the staged h rows of the routed slots wrap around an LDS ring smaller than T*k rows.
+template <int VPG, int CGU, int CGD, int CR, bool RING>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void moe_decode_fused_kernel(FusedArgs a) {
   static_assert(16 * CGU * VPG == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
   static_assert(16 * CGD * VPG == kHW, "lanes must span an h row");
@@ -146,13 +147,18 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ unsigned s_tok;  // this call's barrier token
   // entries whose gate/up rows of this block are in the outbox (or that have none here)
   __shared__ unsigned long long s_done[(kMaxExperts + 1 + 63) / 64];
+  // phase-B entries whose down rows this block has computed (their h rows may be overwritten)
+  __shared__ unsigned long long s_bdone[(kMaxExperts + 1 + 63) / 64];
   uint4 *sx = reinterpret_cast<uint4 *>(smem + a.lds_route);            // [T][xg]
   float *s_y = reinterpret_cast<float *>(sx + (size_t)T * xg);          // [T*k][8]
   float *s_ys = s_y + (size_t)n_slots * kOct;                           // [T][8]
   // h values of this block's row pair, one packed pair per slot position (then T shared)
   uint32_t *s_out = reinterpret_cast<uint32_t *>(s_ys + (size_t)T * kOct);  // [T*k + T]
+  // staged h rows: a ring of HR rows for the routed slot positions (position r in row r % HR;
+  // HR = T*k, no wrap, wherever every position fits), then the shared expert's T rows
+  const int HR = RING ? a.h_ring : n_slots;
   uint4 *hl = reinterpret_cast<uint4 *>(smem + a.lds_route + al16((size_t)T * xg * 16) +
-                                        al16((size_t)(n_slots + T) * (kOct + 1) * 4));  // [T*k + T][hg]
+                                        al16((size_t)(n_slots + T) * (kOct + 1) * 4));  // [HR + T][hg]
   // this call's barrier token follows the release word the previous call left: block 0
   // rewrites that word only after every block has arrived, so every block reads the same
   // value here (the token lives in bits 0..30, never 0, so it differs from a cleared flag)
@@ -375,8 +381,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     s_mlo[e] = 0u;
     s_mhi[e] = 0u;
   }
-  for (int i = tid; i < (n_slots + T) * hg; i += kNT) hl[i] = make_uint4(0, 0, 0, 0);
-  for (int i = tid; i < (kMaxExperts + 1 + 63) / 64; i += kNT) s_done[i] = 0ull;
+  for (int i = tid; i < (HR + T) * hg; i += kNT) hl[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < (kMaxExperts + 1 + 63) / 64; i += kNT) {
+    s_done[i] = 0ull;
+    s_bdone[i] = 0ull;
+  }
   if (tid == 0) {
     s_err = 0;
     s_hready = 0;
@@ -563,22 +572,22 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_make_buffer_rsrc(a.h, 0, NEB > 0 ? n_slots * rbytes : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rhs =
         __builtin_amdgcn_make_buffer_rsrc(a.h_s, 0, (NEB > 0 && sh) ? T * srbytes : 0, 0x00020000);
-    // the first entry at or after q that this block has not finished
-    auto done_upto = [&](int q) {
+    // the first entry at or after q whose bit in mask is clear
+    auto done_upto = [&](const unsigned long long *mask, int q) {
       while (q < total) {
         const unsigned long long m =
-            __hip_atomic_load(&s_done[q >> 6], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >> (q & 63);
+            __hip_atomic_load(&mask[q >> 6], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >> (q & 63);
         const int run = m == ~0ull >> (q & 63) ? 64 - (q & 63) : (int)__builtin_ctzll(~m);
         q += run;
         if (run < 64 - ((q - run) & 63)) break;
       }
       return min(q, total);
     };
-    int pub = 0, staged = 0;
+    int pub = 0, staged = 0, cons = 0;
     unsigned spins = 0;
     while (pub < total || (NEB > 0 && staged < total)) {
       bool moved = false;
-      const int m = done_upto(pub);
+      const int m = done_upto(s_done, pub);
       asm volatile("" ::: "memory");
       if (m > pub) {
         // (1) the outbox of entries [pub, m), then the progress word
@@ -602,19 +611,29 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (g & kBarErr) {  // block 0 gave up waiting for some block: stage what there is
           if (lane == 0) __hip_atomic_store(&s_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        const int upto = (g & kBarErr) ? total : gr;
+        int upto = (g & kBarErr) ? total : gr;
+        if (RING && upto > staged) {
+          // the ring: the rows of entries [staged, upto) may only replace rows of positions
+          // whose entries this block's phase B has computed
+          cons = done_upto(s_bdone, cons);
+          const int cpos = s_start[max(cons - sh, 0)];
+          while (upto > max(staged, sh) && s_start[upto - sh] > cpos + HR) --upto;
+        }
         if (upto > staged) {
           if (sh && staged == 0)
             for (int t = 0; t < T; ++t)
               if (lane * 16 < srbytes)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rhs, (lds_void *)(hl + (size_t)(n_slots + t) * hg), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rhs, (lds_void *)(hl + (size_t)(HR + t) * hg), 16,
                                                          lane * 16, t * srbytes, 0, kSc1);
           if (upto > sh) {
             const int r0 = s_start[max(staged - sh, 0)], r1 = s_start[upto - sh];
-            for (int r = r0; r < r1; ++r)
+            int row = RING ? r0 % HR : r0;  // LDS row of position r
+            for (int r = r0; r < r1; ++r) {
               if (lane * 16 < rbytes)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void *)(hl + (size_t)r * hg), 16, lane * 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void *)(hl + (size_t)row * hg), 16, lane * 16,
                                                          s_slots[r] * rbytes, 0, kSc1);
+              row = RING && row + 1 == HR ? 0 : row + 1;
+            }
           }
           wait_stores();  // the copies have landed in LDS
           staged = upto;
@@ -824,9 +843,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sc1 = sc[kOct * oB + 4 + rg];
       }
       wait_staged(q);
+      int row = shared ? HR + q0 : RING ? q0 % HR : q0;  // LDS row of position qq
       for (int qq = q0; qq < q1; ++qq) {
         const int slot = shared ? qq : s_slots[qq];
-        const uint4 *hr = hl + (size_t)(shared ? n_slots + qq : qq) * hg;
+        const uint4 *hr = hl + (size_t)row * hg;
+        row = RING && !shared && row + 1 == HR ? 0 : row + 1;
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int c = 0; c < CGD; ++c) {
@@ -867,6 +888,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           dst[4 + rg] = round_bf16(acc1 * sc1);
         }
       }
+      // the entry's h rows have been read (their values are used above): the stager may
+      // reuse them (LDS operations of one wavefront complete in order)
+      asm volatile("" ::: "memory");
+      if (RING && lane == 0)
+        __hip_atomic_fetch_or(&s_bdone[q >> 6], 1ull << (q & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
     int q1 = grab_b(), q2b = grab_b(), q3 = grab_b(), q4 = grab_b();
     dn_load(da, sa, q1);
@@ -937,6 +963,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ============================================================ host side
 namespace {
 constexpr size_t kFusedLdsMax = 156 * 1024;
+constexpr int kFusedRingMaxT = 16;  // the largest block that takes the fused kernel with a wrapping ring
 
 size_t route_bytes(int T, int k, int E) {
   const size_t n = (size_t)T * k;
@@ -946,14 +973,26 @@ size_t route_bytes(int T, int k, int E) {
 
 // LDS of one block: the routing region, the tokens, the expert outputs y of the block's rows
 // and the outbox of its h values, and the h rows (all live together: the stager fills h while
-// the tokens are still in use).
-size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared) {
-  const size_t rb = route_bytes(T, k, E);
+// the tokens are still in use).  The h rows of the routed slots form a ring: all T*k of them
+// where they fit, else as many as fit (at least T, one entry's slots).
+namespace {
+size_t fused_fixed_bytes(int T, int H, int E, int k) {
   const size_t n = (size_t)T * k;
-  const size_t xb = al16((size_t)T * (H / 8 + 2) * 16);
-  const size_t yb = al16((n + T) * (kOct + 1) * 4);  // y of the block's rows, then the h outbox
-  const size_t hb = (n + T) * ((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16;
-  return rb + xb + yb + hb;
+  return route_bytes(T, k, E) + al16((size_t)T * (H / 8 + 2) * 16) + al16((n + T) * (kOct + 1) * 4);
+}
+size_t fused_hrow_bytes(int I, int I_s, int has_shared) { return (size_t)((has_shared && I_s > I ? I_s : I) / 8 + 2) * 16; }
+}  // namespace
+
+int fused_h_ring(int T, int H, int E, int k, int I, int I_s, int has_shared) {
+  const size_t fixed = fused_fixed_bytes(T, H, E, k), row = fused_hrow_bytes(I, I_s, has_shared);
+  if (fixed + (size_t)T * row >= kFusedLdsMax) return 0;
+  const size_t rows = (kFusedLdsMax - fixed) / row - T;
+  return (int)std::min((size_t)T * k, rows);
+}
+
+size_t fused_lds_bytes(int T, int H, int E, int k, int I, int I_s, int has_shared) {
+  const int hr = fused_h_ring(T, H, E, k, I, I_s, has_shared);
+  return fused_fixed_bytes(T, H, E, k) + (size_t)(hr + T) * fused_hrow_bytes(I, I_s, has_shared);
 }
 
 namespace {
@@ -982,7 +1021,10 @@ bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype) {
   if (H % grp != 0 || I % grp != 0 || I_s % grp != 0) return false;
   const int nb = std::min(device_cus(), kMaxBlocks);
   if ((I_s > I ? I_s : I) / 2 > nb || H / kOct > nb) return false;
-  return fused_lds_bytes(T, H, E, k, I, I_s, I_s > 0) <= kFusedLdsMax;
+  // a ring smaller than the T*k slots stalls the staging on phase B: past 16 tokens the
+  // four kernels are faster (T = 20 at H = 2048: 143 against 137 us; T = 16: 110 against 118)
+  const int hr = fused_h_ring(T, H, E, k, I, I_s, I_s > 0);
+  return hr >= T && (T <= kFusedRingMaxT || hr == T * k) && fused_lds_bytes(T, H, E, k, I, I_s, I_s > 0) <= kFusedLdsMax;
 }
 
 // Per device: the LDS size the kernel was opened up to, the CU count and how many
@@ -993,9 +1035,9 @@ struct FusedLaunchInfo {
   int cus = 0, per_cu = 0;
 };
 
-template <int VPG, int CGU, int CGD, int CR>
+template <int VPG, int CGU, int CGD, int CR, bool RING>
 static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *nb_out) {
-  auto kern = moe_decode_fused_kernel<VPG, CGU, CGD, CR>;
+  auto kern = moe_decode_fused_kernel<VPG, CGU, CGD, CR, RING>;
   static std::mutex mu;
   static FusedLaunchInfo info[64];
   int dev = 0;
@@ -1034,16 +1076,18 @@ static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *n
 
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len) {
   const size_t lds = fused_lds_bytes(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared);
-  if (lds > kFusedLdsMax) return hipErrorInvalidValue;
+  a.h_ring = fused_h_ring(a.T, a.H, a.E, a.k, a.I, a.I_s, a.has_shared);
+  if (lds > kFusedLdsMax || a.h_ring < a.T) return hipErrorInvalidValue;
   a.lds_route = route_bytes(a.T, a.k, a.E);
   int nb = 0;
   hipError_t e;
-  if (a.wtype == 0) e = launch_fused_t<8, 16, 4, 8>(a, lds, s, &nb);
-  else if (a.wtype == 3) e = launch_fused_t<32, 4, 1, 8>(a, lds, s, &nb);
-  else e = launch_fused_t<16, 8, 2, 8>(a, lds, s, &nb);
+  const bool ring = a.h_ring < a.T * a.k;
+  if (a.wtype == 0) e = ring ? launch_fused_t<8, 16, 4, 8, true>(a, lds, s, &nb) : launch_fused_t<8, 16, 4, 8, false>(a, lds, s, &nb);
+  else if (a.wtype == 3) e = ring ? launch_fused_t<32, 4, 1, 8, true>(a, lds, s, &nb) : launch_fused_t<32, 4, 1, 8, false>(a, lds, s, &nb);
+  else e = ring ? launch_fused_t<16, 8, 2, 8, true>(a, lds, s, &nb) : launch_fused_t<16, 8, 2, 8, false>(a, lds, s, &nb);
   if (desc)
-    snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu",
-             a.wtype == 0 ? "bf16" : a.wtype == 3 ? "mxfp4" : "fp8", nb, kNT, lds);
+    snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu h_ring=%d",
+             a.wtype == 0 ? "bf16" : a.wtype == 3 ? "mxfp4" : "fp8", nb, kNT, lds, a.h_ring);
   return e;
 }
 

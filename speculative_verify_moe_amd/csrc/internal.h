@@ -148,6 +148,7 @@ struct FusedArgs {
   uint16_t *out;      // [T][H]
   unsigned *bar;      // synchronisation words (kBarrierWords, layout above)
   size_t lds_route;   // set by the launcher
+  int h_ring;         // rows of the LDS ring of staged routed h rows (set by the launcher)
 };
 bool fused_decode_fits(int T, int H, int E, int k, int I, int I_s, int wtype);
 hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t desc_len);

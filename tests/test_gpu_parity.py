@@ -143,18 +143,21 @@ LAYER_CASES = [
     ("qwen36_T1", "qwen36_a3b", 1),
     ("qwen36_T8", "qwen36_a3b", 8),
     ("qwen36_T5", "qwen36_a3b", 5),
+    ("qwen36_T16", "qwen36_a3b", 16),
     ("qwen36_T32", "qwen36_a3b", 32),
     ("qwen36_zipf_T32", "qwen36_a3b_zipf", 32),
     ("qwen36_T64", "qwen36_a3b", 64),
     ("qwen36_T40", "qwen36_a3b", 40),
     ("flash_fp8_T1", "flash_next_fp8", 1),
     ("flash_fp8_T6", "flash_next_fp8", 6),
+    ("flash_fp8_T16", "flash_next_fp8", 16),
     ("prefill_T4096", "prefill", 4096),
     ("prefill_T200", "prefill", 200),
     ("prefill_fp8_T4096", "prefill_fp8", 4096),
     ("prefill_fp8_T200", "prefill_fp8", 200),
     ("qwen36_mxfp4_T1", "qwen36_a3b_mxfp4", 1),
     ("qwen36_mxfp4_T8", "qwen36_a3b_mxfp4", 8),
+    ("qwen36_mxfp4_T16", "qwen36_a3b_mxfp4", 16),
     ("qwen36_mxfp4_T32", "qwen36_a3b_mxfp4", 32),
     ("qwen36_mxfp4_T48", "qwen36_a3b_mxfp4", 48),
     ("flash_fp8_T40", "flash_next_fp8", 40),
@@ -321,7 +324,7 @@ BATCH_INVARIANCE_CASES = [
     ("qwen36_a3b", 8, False), ("qwen36_a3b_mxfp4", 8, False), ("flash_next_fp8", 6, False),
     ("qwen36_a3b", 16, False), ("qwen36_a3b", 32, False), ("qwen36_a3b", 64, False),
     ("qwen36_a3b_zipf", 32, False), ("qwen36_a3b_mxfp4", 32, False), ("qwen36_a3b_mxfp4", 48, False),
-    ("flash_next_fp8", 40, False),
+    ("flash_next_fp8", 40, False), ("flash_next_fp8", 16, False), ("qwen36_a3b_zipf", 16, False),
     ("qwen36_a3b", 8, True), ("qwen36_a3b", 32, True), ("flash_next_fp8", 6, True), ("qwen36_a3b_mxfp4", 8, True),
 ]
 
@@ -388,6 +391,9 @@ _FOUR_KERNEL_CASES = [("tiny", {}, 4, True), ("tiny", {}, 64, True), ("qwen36_a3
                       # 16 tokens: top-k and alignment in one block; 17: top-k over the chip first
                       ("tiny", {}, 16, True), ("tiny", {}, 17, True), ("qwen36_a3b", {}, 17, False),
                       ("qwen36_a3b", {}, 1, True), ("qwen36_a3b", {}, 32, False), ("flash_next_fp8", {}, 6, True),
+                      # 12 and 16 tokens: the fused kernel's h rows wrap around its LDS ring
+                      ("qwen36_a3b", {}, 12, True), ("qwen36_a3b", {}, 16, True), ("flash_next_fp8", {}, 16, True),
+                      ("qwen36_a3b_mxfp4", {}, 16, True),
                       ("qwen36_a3b_mxfp4", {}, 8, True), ("qwen36_a3b_mxfp4", {}, 1, True),
                       ("tiny", dict(wtype="mxfp4"), 4, False),
                       ("tiny", dict(wtype="mxfp4", H=512, I=512, I_s=512, bias="normal"), 8, True),
@@ -524,7 +530,8 @@ def test_graph_replays_equal_eager(recipe, T):
 # ---------------------------------------------------------------- the fused kernel's waits
 
 @pytest.mark.parametrize("recipe,T", [("qwen36_a3b", 8), ("qwen36_a3b", 1), ("flash_next_fp8", 6),
-                                      ("qwen36_a3b_mxfp4", 8), ("tiny", 64), ("tiny", 3)])
+                                      ("qwen36_a3b_mxfp4", 8), ("tiny", 64), ("tiny", 3), ("qwen36_a3b", 16),
+                                      ("qwen36_a3b_mxfp4", 16)])
 def test_fused_waits_never_give_up(recipe, T):
     """Normal use of the fused decode kernel: over many calls on one workspace no wait gives up
     (the workspace's status word stays 0) and every output is finite and the same."""
