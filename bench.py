@@ -31,6 +31,7 @@ WORKLOADS = {
     # name: (recipe, T, description)
     "qwen36_T8": ("qwen36_a3b", 8, "Qwen3.6-35B-A3B-like MoE layer, T=8 verify block"),
     "qwen36_T1": ("qwen36_a3b", 1, "Qwen3.6-35B-A3B-like MoE layer, T=1 decode"),
+    "qwen36_T12": ("qwen36_a3b", 12, "Qwen3.6-35B-A3B-like MoE layer, T=12 verify block"),
     "qwen36_T16": ("qwen36_a3b", 16, "Qwen3.6-35B-A3B-like MoE layer, T=16 verify block"),
     "qwen36_T32": ("qwen36_a3b", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32 (two 16-position blocks)"),
     "qwen36_zipf_T32": ("qwen36_a3b_zipf", 32, "Qwen3.6-35B-A3B-like MoE layer, T=32, Zipf(1.1) expert load"),
