@@ -394,6 +394,8 @@ _FOUR_KERNEL_CASES = [("tiny", {}, 4, True), ("tiny", {}, 64, True), ("qwen36_a3
                       # 12 and 16 tokens: the fused kernel's h rows wrap around its LDS ring
                       ("qwen36_a3b", {}, 12, True), ("qwen36_a3b", {}, 16, True), ("flash_next_fp8", {}, 16, True),
                       ("qwen36_a3b_mxfp4", {}, 16, True),
+                      # the ring without a shared expert
+                      ("tiny", dict(H=2048, E=64, k=8, I=512, I_s=0), 16, True),
                       ("qwen36_a3b_mxfp4", {}, 8, True), ("qwen36_a3b_mxfp4", {}, 1, True),
                       ("tiny", dict(wtype="mxfp4"), 4, False),
                       ("tiny", dict(wtype="mxfp4", H=512, I=512, I_s=512, bias="normal"), 8, True),
