@@ -550,21 +550,10 @@ hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s) { return launch_ex
 // ---------------------------------------------------------------- activation rows to fp8
 // One wavefront per row of L bf16 values: s = 2^e for the least e with amax <= 448 * 2^e
 // (1 for an all-zero row), code_i = the e4m3 code nearest a_i * 2^-e (an exact product),
-// ties to an even mantissa, saturating at 448.  A power-of-two scale costs the codes nothing
-// (they are floating point) and makes every quotient exact.
+// ties to an even mantissa.  A power-of-two scale costs the codes nothing (they are floating
+// point) and makes every quotient exact; no quotient exceeds 448, so the hardware conversion
+// (v_cvt_pk_fp8_f32, nearest even) never saturates.
 // Rows whose `sorted` entry is the sentinel (padding of the alignment) are skipped.
-__device__ __forceinline__ uint32_t e4m3_nearest(float v) {
-  // both candidates are formed and one selected, so the code has no branches
-  const float a = fabsf(v);
-  uint32_t u = __float_as_uint(a);
-  u += 0x7FFFFu + ((u >> 20) & 1u);  // 23 mantissa bits to 3, nearest, ties to even
-  const uint32_t nrm = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // exponent bias 127 -> 7
-  const uint32_t sub = (uint32_t)__float2int_rn(a * 512.0f);  // below 2^-6: steps of 2^-9 (8 is 2^-6)
-  uint32_t c = a < 0.015625f ? sub : nrm;
-  c = a < 448.0f ? c : 0x7Eu;  // saturate
-  return a != a ? 0x7Fu : (c | ((__float_as_uint(v) >> 24) & 0x80u));
-}
-
 // NG: 8-value groups per lane (L <= 512 NG); RPW rows per wavefront, all their loads in
 // flight together; each row stays in registers between its amax and its encoding.
 template <int NG, int RPW>
@@ -612,11 +601,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *__restr
     for (int i = 0; i < NG; ++i) {
       if (lane + kWave * i >= G) continue;
       const uint32_t w[4] = {v[rr][i].x, v[rr][i].y, v[rr][i].z, v[rr][i].w};
-      uint32_t c[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        c[q] = e4m3_nearest(ldexpf(bf16_lo(w[q]), -e)) | (e4m3_nearest(ldexpf(bf16_hi(w[q]), -e)) << 8);
-      d[lane + kWave * i] = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+      // v_cvt_pk_fp8_f32: two values to E4M3 codes, nearest even (no value here exceeds 448)
+      int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w[0]), -e), ldexpf(bf16_hi(w[0]), -e), 0, false);
+      c01 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w[1]), -e), ldexpf(bf16_hi(w[1]), -e), c01, true);
+      int c23 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w[2]), -e), ldexpf(bf16_hi(w[2]), -e), 0, false);
+      c23 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w[3]), -e), ldexpf(bf16_hi(w[3]), -e), c23, true);
+      d[lane + kWave * i] = make_uint2((uint32_t)c01, (uint32_t)c23);
     }
     if (lane == 0) scale[row] = ldexpf(1.0f, e);
   }
