@@ -48,13 +48,12 @@ __device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b, float
   return c;
 }
 
-// Two OCP E4M3FN codes (byte `sel*2`, `sel*2+1` of w) -> a packed bf16 pair.  Every
-// E4M3FN value is exact in bf16 (3 mantissa bits, exponents 2^-9..2^8).
+// Two OCP E4M3FN codes (byte `sel*2`, `sel*2+1` of w) -> a packed bf16 pair, in one
+// v_cvt_scalef32_pk_bf16_fp8 (scale 1).  Every E4M3FN value is exact in bf16 (3 mantissa
+// bits, exponents 2^-9..2^8).
 template <bool HI_WORD>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  f2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI_WORD);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI_WORD));
 }
 
 // DPP lane permutations (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1],
