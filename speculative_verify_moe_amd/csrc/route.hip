@@ -321,8 +321,10 @@ hipError_t launch_compact_touched(const int32_t *counts, const int32_t *offsets,
 // ============================================================ alignment, many blocks (any n)
 // 1. per-chunk histograms  hist[c][e]  (chunks of kAlignChunk slots)
 // 2. per-expert exclusive scan over chunks (in place) and the counts
-// 3. padded scan over experts: offsets, num_padded, block_expert
-// 4. scatter: position = offsets[e] + hist[c][e] + rank inside the chunk; sentinel fill
+// 3. scatter: every block scans the padded counts over the experts itself (the same
+//    offsets in every block, with no kernel between); block 0 writes offsets and
+//    num_padded, the blocks share block_expert; position = offsets[e] + hist[c][e] + rank
+//    inside the chunk; sentinel fill
 size_t align_hist_ints(int64_t n, int E) {
   const int64_t chunks = (n + kAlignChunk - 1) / kAlignChunk;
   return (size_t)(chunks * E);
@@ -356,49 +358,52 @@ __global__ __launch_bounds__(256) void align_colscan_kernel(int32_t *__restrict_
   if (threadIdx.x == 0) counts[e] = carry;
 }
 
-__global__ __launch_bounds__(1024) void align_offsets_kernel(const int32_t *__restrict__ counts, int E, int BM,
-                                                             int cap, AlignOut al) {
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int s_tmp[1024 / kWave + 1];
-  const int tid = threadIdx.x;
-  const int padded = tid < E ? (counts[tid] + BM - 1) / BM * BM : 0;
-  int total;
-  const int excl = block_excl_scan<1024>(padded, s_tmp, &total);
-  if (tid < E) {
-    s_off[tid] = excl;
-    al.offsets[tid] = excl;
-  }
-  if (tid == 0) {
-    s_off[E] = total;
-    al.offsets[E] = total;
-    al.num_padded[0] = total;
-  }
-  __syncthreads();
-  for (int b = tid; b < cap / BM; b += 1024) {
-    const int p = b * BM;
-    al.block_expert[b] = p < total ? segment_of(s_off, E, p) : -1;
-  }
-}
-
 __global__ __launch_bounds__(kAlignChunk) void align_scatter_kernel(const int32_t *__restrict__ ids, int n, int E,
-                                                                    int cap, const int32_t *__restrict__ hist,
+                                                                    int BM, int cap, const int32_t *__restrict__ hist,
                                                                     AlignOut al) {
   constexpr int NW = kAlignChunk / kWave;
   // per wavefront of the chunk, how many of its slots chose each expert
   __shared__ int32_t s_whist[NW][kMaxExperts];
-  // the padded offsets and the counts, staged once: the sentinel fill searches them per
+  // the counts and their padded exclusive scan, in LDS: the sentinel fill searches them per
   // position (a binary search over global memory would be a chain of dependent loads)
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int s_tmp[kAlignChunk / kWave + 1];
+  constexpr int PER = (kMaxExperts + kAlignChunk - 1) / kAlignChunk;  // experts per thread in the scan
   const int lane = lane_id(), w = wave_id();
   const int i = blockIdx.x * kAlignChunk + threadIdx.x;
   const int e = i < n ? ids[i] : -1;
   for (int j = threadIdx.x; j < NW * E; j += kAlignChunk) s_whist[j / E][j % E] = 0;
-  for (int j = threadIdx.x; j <= E; j += kAlignChunk) {
-    s_off[j] = al.offsets[j];
-    if (j < E) s_cnt[j] = al.counts[j];
+  {
+    // thread t scans experts PER t .. PER t + PER - 1 (consecutive, so the scan is in expert order)
+    int pc[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ex = PER * threadIdx.x + i;
+      const int c = ex < E ? al.counts[ex] : 0;
+      if (ex < E) s_cnt[ex] = c;
+      pc[i] = (c + BM - 1) / BM * BM;
+      sum += pc[i];
+    }
+    int total;
+    int run = block_excl_scan<kAlignChunk>(sum, s_tmp, &total);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ex = PER * threadIdx.x + i;
+      if (ex < E) s_off[ex] = run;
+      run += pc[i];
+    }
+    if (threadIdx.x == 0) s_off[E] = total;
   }
   __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int j = threadIdx.x; j <= E; j += kAlignChunk) al.offsets[j] = s_off[j];
+    if (threadIdx.x == 0) al.num_padded[0] = s_off[E];
+  }
+  for (int bb = blockIdx.x * kAlignChunk + threadIdx.x; bb < cap / BM; bb += gridDim.x * kAlignChunk) {
+    const int p = bb * BM;
+    al.block_expert[bb] = p < s_off[E] ? segment_of(s_off, E, p) : -1;
+  }
   // the slot's rank among the chunk's earlier slots of its expert (the chunk's slots in
   // order): inside the wavefront, one ballot per distinct expert, led by its first lane
   int r = 0;
@@ -433,9 +438,8 @@ hipError_t launch_align_large(const int32_t *ids, int n, int E, int BM, int64_t 
   // (each launch's own status: a later hipGetLastError would read it cleared)
   hipError_t e = launch_k(align_hist_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, hist);
   if (e == hipSuccess) e = launch_k(align_colscan_kernel, dim3(E), dim3(256), 0, s, hist, chunks, E, al.counts);
-  if (e == hipSuccess) e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, s, al.counts, E, BM, (int)cap, al);
   if (e == hipSuccess)
-    e = launch_k(align_scatter_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, (int)cap, hist, al);
+    e = launch_k(align_scatter_kernel, dim3(chunks), dim3(kAlignChunk), 0, s, ids, n, E, BM, (int)cap, hist, al);
   return e;
 }
 
