@@ -110,7 +110,8 @@ __device__ __forceinline__ void note_timeout(unsigned *bar, int *s_err) {
 // are also one scale block).  CGU / CGD: column groups per lane and weight row in phase A /
 // phase B; CR: float4 router groups per lane.
 // RING: the staged h rows of the routed slots wrap around an LDS ring smaller than T*k rows.
-template <int VPG, int CGU, int CGD, int CR, bool RING>
+// RAMP: each compute wavefront starts phase A with one entry in flight instead of two.
+template <int VPG, int CGU, int CGD, int CR, bool RING, bool RAMP>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) void moe_decode_fused_kernel(FusedArgs a) {
   static_assert(16 * CGU * VPG == kXW && 64 * 4 * CR == kXW, "lanes must span a token row");
   static_assert(16 * CGD * VPG == kHW, "lanes must span an h row");
@@ -750,20 +751,43 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // every load is issued (past the last entry they read nothing), so the compiler's wait
     // counts are the same on every path and no prefetch is waited for early; entry 0 (the
     // shared expert) is wavefront 0's first, its rows from phase 0 already in wa
-    int q = (sh && wave == 0) ? 0 : grab();
-    int q2 = grab();
-    if (!(sh && q == 0)) load_a(wa, xa, q);
-    load_a(wb, xb, q2);
-    while (q < total) {
-      compute_a(wa, xa, q);
-      const int q3 = grab();
+    if constexpr (!RAMP) {
+      int q = (sh && wave == 0) ? 0 : grab();
+      int q2 = grab();
+      if (!(sh && q == 0)) load_a(wa, xa, q);
+      load_a(wb, xb, q2);
+      while (q < total) {
+        compute_a(wa, xa, q);
+        const int q3 = grab();
+        load_a(wa, xa, q3);
+        if (q2 >= total) break;
+        compute_a(wb, xb, q2);
+        const int q4 = grab();
+        load_a(wb, xb, q4);
+        q = q3;
+        q2 = q4;
+      }
+    } else {
+      // the first entry alone in flight: computed before the second is issued, so the
+      // blocks' first h rows (which every phase B waits for) arrive sooner; two after that
+      int q = (sh && wave == 0) ? 0 : grab();
+      if (!(sh && q == 0)) load_a(wa, xa, q);
+      if (q < total) compute_a(wa, xa, q);
+      int q2 = grab();
+      load_a(wb, xb, q2);
+      int q3 = grab();
       load_a(wa, xa, q3);
-      if (q2 >= total) break;
-      compute_a(wb, xb, q2);
-      const int q4 = grab();
-      load_a(wb, xb, q4);
-      q = q3;
-      q2 = q4;
+      while (q2 < total) {
+        compute_a(wb, xb, q2);
+        const int q4 = grab();
+        load_a(wb, xb, q4);
+        if (q3 >= total) break;
+        compute_a(wa, xa, q3);
+        const int q5 = grab();
+        load_a(wa, xa, q5);
+        q2 = q4;
+        q3 = q5;
+      }
     }
 
     // ---------------- phase B: down rows 8o .. 8o+7, o = b, for entry 0 (the shared expert,
@@ -1035,9 +1059,9 @@ struct FusedLaunchInfo {
   int cus = 0, per_cu = 0;
 };
 
-template <int VPG, int CGU, int CGD, int CR, bool RING>
+template <int VPG, int CGU, int CGD, int CR, bool RING, bool RAMP>
 static hipError_t launch_fused_t(FusedArgs &a, size_t lds, hipStream_t s, int *nb_out) {
-  auto kern = moe_decode_fused_kernel<VPG, CGU, CGD, CR, RING>;
+  auto kern = moe_decode_fused_kernel<VPG, CGU, CGD, CR, RING, RAMP>;
   static std::mutex mu;
   static FusedLaunchInfo info[64];
   int dev = 0;
@@ -1082,9 +1106,11 @@ hipError_t launch_fused_decode(FusedArgs a, hipStream_t s, char *desc, size_t de
   int nb = 0;
   hipError_t e;
   const bool ring = a.h_ring < a.T * a.k;
-  if (a.wtype == 0) e = ring ? launch_fused_t<8, 16, 4, 8, true>(a, lds, s, &nb) : launch_fused_t<8, 16, 4, 8, false>(a, lds, s, &nb);
-  else if (a.wtype == 3) e = ring ? launch_fused_t<32, 4, 1, 8, true>(a, lds, s, &nb) : launch_fused_t<32, 4, 1, 8, false>(a, lds, s, &nb);
-  else e = ring ? launch_fused_t<16, 8, 2, 8, true>(a, lds, s, &nb) : launch_fused_t<16, 8, 2, 8, false>(a, lds, s, &nb);
+  // bf16 and MXFP4 start phase A with one entry in flight per wavefront (measured faster at
+  // T = 1 and 16 and no slower elsewhere); fp8 with two (one was slower at T = 6)
+  if (a.wtype == 0) e = ring ? launch_fused_t<8, 16, 4, 8, true, true>(a, lds, s, &nb) : launch_fused_t<8, 16, 4, 8, false, true>(a, lds, s, &nb);
+  else if (a.wtype == 3) e = ring ? launch_fused_t<32, 4, 1, 8, true, true>(a, lds, s, &nb) : launch_fused_t<32, 4, 1, 8, false, true>(a, lds, s, &nb);
+  else e = ring ? launch_fused_t<16, 8, 2, 8, true, false>(a, lds, s, &nb) : launch_fused_t<16, 8, 2, 8, false, false>(a, lds, s, &nb);
   if (desc)
     snprintf(desc, desc_len, "moe_decode_fused<%s> grid=%d block=%d lds=%zu h_ring=%d",
              a.wtype == 0 ? "bf16" : a.wtype == 3 ? "mxfp4" : "fp8", nb, kNT, lds, a.h_ring);
